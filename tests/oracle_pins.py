@@ -1,0 +1,347 @@
+"""Pins for the CPU oracle: each pin checks the oracle against something other
+than itself -- the pages' worked examples, closed forms, invariants, or an
+independent library evaluation (numpy reshapes, torch's float64 attention).
+
+Each pin takes the oracle library handle so the mutant tests can run the same
+pins against deliberately broken builds of the oracle.  A pin raises
+AssertionError on a mismatch.
+"""
+from __future__ import annotations
+
+import math
+import os
+
+import numpy as np
+import torch
+
+import oracle
+from ulysses_head_sharded_amd import synth
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+
+# ---------------------------------------------------------------------------- helpers
+def _read_golden(name):
+    rows = []
+    with open(os.path.join(GOLDEN, name), encoding="utf-8") as f:
+        for line in f:
+            line = line.strip()
+            if line and not line.startswith("#"):
+                rows.append(line)
+    return rows
+
+
+def np_pack(x, s, b, h, d, P):
+    """Pack by numpy reshapes: [s/P,b,(P,hp),d] -> [P,s/P,b,hp,d]."""
+    return x.reshape(s // P, b, P, h // P, d).transpose(2, 0, 1, 3, 4).copy()
+
+
+def np_seq2head(x_all, s, b, h, d, P):
+    """Exchange by numpy reshapes: [j,t,b,(r,hp),d] -> [r,(j,t),b,hp,d]."""
+    v = x_all.reshape(P, s // P, b, P, h // P, d).transpose(3, 0, 1, 2, 4, 5)
+    return v.reshape(P, s, b, h // P, d).copy()
+
+
+def torch_attention(q, k, v, causal):
+    """Independent reference: torch's float64 scaled_dot_product_attention.
+
+    q [s,b,nq,d], k/v [s,b,nkv,d] float64 numpy; KV heads are repeated by
+    contiguous groups.  Returns (o [s,b,nq,d], lse [b,nq,s])."""
+    s, b, nq, d = q.shape
+    nkv = k.shape[2]
+    G = nq // nkv
+    qt = torch.from_numpy(np.ascontiguousarray(q.transpose(1, 2, 0, 3)))  # [b,nq,s,d]
+    kt = torch.from_numpy(np.ascontiguousarray(k.transpose(1, 2, 0, 3))).repeat_interleave(G, 1)
+    vt = torch.from_numpy(np.ascontiguousarray(v.transpose(1, 2, 0, 3))).repeat_interleave(G, 1)
+    o = torch.nn.functional.scaled_dot_product_attention(qt, kt, vt, is_causal=bool(causal))
+    sc = torch.matmul(qt, kt.transpose(-1, -2).contiguous()) / math.sqrt(d)
+    if causal:
+        mask = torch.ones(s, s, dtype=torch.bool).tril()
+        sc = sc.masked_fill(~mask, float("-inf"))
+    lse = torch.logsumexp(sc, dim=-1)
+    return o.numpy().transpose(2, 0, 1, 3), lse.numpy()
+
+
+def widen(a):
+    return synth.bf16_bits_to_f32(a).astype(np.float64) if a.dtype == np.uint16 else \
+        a.astype(np.float64)
+
+
+# ---------------------------------------------------------------------------- layout pins
+def pin_alltoall_worked_example(lib):
+    """The two-rank AllToAll example of the collectives tutorial."""
+    rows = _read_golden("alltoall_2rank.txt")
+    code = {"A0": 0xA0, "A1": 0xA1, "B0": 0xB0, "B1": 0xB1}
+    before = {}
+    after = {}
+    for r in rows:
+        rank, rest = r.split(":")
+        lhs, rhs = rest.split("->")
+        before[int(rank)] = [code[t] for t in lhs.split()]
+        after[int(rank)] = [code[t] for t in rhs.split()]
+    P, s, b, h, d = 2, 2, 1, 2, 1
+    x_all = np.array([before[0], before[1]], dtype=np.uint16).reshape(P, 1, b, h, d)
+    y_all = oracle.seq2head(x_all, s, b, h, d, P, lib=lib)
+    for r in range(P):
+        assert y_all[r].reshape(-1).tolist() == after[r], (r, y_all[r].reshape(-1))
+    # one token per rank: pack alone is the identity, the routing does the work
+    for j in range(P):
+        y = oracle.pack(x_all[j], s, b, h, d, P, lib=lib)
+        assert y.reshape(-1).tolist() == before[j]
+    back = oracle.head2seq(y_all, s, b, h, d, P, lib=lib)
+    assert np.array_equal(back, x_all)
+
+
+def pin_two_card_blocks(lib):
+    """Two-card X_{i,j} example: keep X00, send X01, receive X10."""
+    rows = _read_golden("two_card_blocks.txt")
+    P, s, b, h, d = 2, 4, 1, 4, 3
+    sl, hp = s // P, h // P
+    # element value = 1000*i + 100*j + position inside the block
+    x_all = np.empty((P, sl, b, h, d), dtype=np.int32)
+    for i in range(P):
+        for t in range(sl):
+            for hh in range(h):
+                for e in range(d):
+                    j, k = divmod(hh, hp)
+                    x_all[i, t, 0, hh, e] = 1000 * i + 100 * j + (t * hp + k) * d + e
+
+    def block_label(arr):
+        vals = np.unique(arr // 100)
+        assert vals.size == 1, vals
+        i, j = divmod(int(vals[0]), 10)
+        return f"X{i}{j}"
+
+    y_all = oracle.seq2head(x_all, s, b, h, d, P, lib=lib)
+    for r_line in rows:
+        rank, keeps, sends, receives, after = r_line.split()
+        rank = int(rank)
+        send = oracle.pack(x_all[rank], s, b, h, d, P, lib=lib)
+        assert block_label(send[rank]) == keeps
+        assert block_label(send[1 - rank]) == sends
+        other = oracle.pack(x_all[1 - rank], s, b, h, d, P, lib=lib)
+        assert block_label(other[rank]) == receives
+        seq_blocks = [block_label(y_all[rank][c * sl:(c + 1) * sl]) for c in range(P)]
+        assert ",".join(seq_blocks) == after
+        # inside each block the order of tokens and heads is kept
+        for c in range(P):
+            blk = y_all[rank][c * sl:(c + 1) * sl] % 100
+            assert np.array_equal(blk.reshape(-1), np.arange(sl * hp * d))
+
+
+def pin_conservation_4card(lib):
+    """4 cards, 16 tokens, 8 heads: 32*d_h elements per card before and after."""
+    g = dict(line.split(None, 1) for line in _read_golden("shapes_4card_16tok_8head.txt"))
+    P, s, h = int(g["P"]), int(g["s"]), int(g["h"])
+    per = int(g["elements_per_card_over_d_h"])
+    bsh = tuple(int(v) for v in g["before_shape"].split())
+    ash = tuple(int(v) for v in g["after_shape"].split())
+    for d in (1, 4, 64):
+        b = 1
+        x_all = np.arange(P * (s // P) * b * h * d, dtype=np.int64).reshape(P, s // P, b, h, d)
+        y_all = oracle.seq2head(x_all, s, b, h, d, P, lib=lib)
+        for r in range(P):
+            assert x_all[r].shape[0] * x_all[r].shape[2] == bsh[0] * bsh[1]
+            assert (y_all[r].shape[0], y_all[r].shape[2]) == ash
+            assert x_all[r].size == per * d and y_all[r].size == per * d
+        # nothing duplicated, nothing lost: the exchange is a permutation
+        assert np.array_equal(np.sort(y_all.reshape(-1)), np.arange(x_all.size))
+
+
+def pin_inverse_random_bits(lib):
+    """unpack(pack(x)) = x and head2seq(seq2head(X)) = X on raw bit patterns."""
+    cases = [(16, 1, 8, 64, 4, 4), (12, 2, 6, 5, 3, 2), (8, 2, 4, 3, 2, 8), (32, 1, 16, 7, 8, 2)]
+    for n, (s, b, h, d, P, elt) in enumerate(cases):
+        dt = {2: np.uint16, 4: np.uint32, 8: np.uint64}[elt]
+        nbytes = (s // P) * b * h * d * elt
+        x = synth.random_bits(109 + n, nbytes).view(dt).reshape(s // P, b, h, d)
+        y = oracle.pack(x, s, b, h, d, P, lib=lib)
+        assert np.array_equal(oracle.unpack(y, s, b, h, d, P, lib=lib), x)
+        x_all = synth.random_bits(209 + n, nbytes * P).view(dt).reshape(P, s // P, b, h, d)
+        y_all = oracle.seq2head(x_all, s, b, h, d, P, lib=lib)
+        assert np.array_equal(oracle.head2seq(y_all, s, b, h, d, P, lib=lib), x_all)
+    # float payloads survive untouched (NaN with payload, -0, subnormal, inf)
+    special = np.array([0x7FC01234, 0x80000000, 0x00000001, 0x7F800000, 0xFFBFFFFF,
+                        0x3F800000, 0x7FA00000, 0x807FFFFF], dtype=np.uint32)
+    xs = special.view(np.float32).reshape(2, 1, 4, 1)
+    ys = oracle.pack(xs, 4, 1, 4, 1, 2, lib=lib)
+    assert np.array_equal(ys.view(np.uint32).reshape(-1),
+                          np_pack(special.reshape(2, 1, 4, 1), 4, 1, 4, 1, 2).reshape(-1))
+
+
+def pin_brute_force_tiny(lib):
+    """Every P | s, P | h with s, h <= 12, b <= 2, d <= 3: index-valued inputs
+    against numpy reshapes/transposes."""
+    for s in range(1, 13):
+        for h in range(1, 13):
+            for P in range(1, min(s, h) + 1):
+                if s % P or h % P:
+                    continue
+                for b in (1, 2):
+                    for d in (1, 3):
+                        n = (s // P) * b * h * d
+                        x = np.arange(n, dtype=np.int32).reshape(s // P, b, h, d)
+                        y = oracle.pack(x, s, b, h, d, P, lib=lib)
+                        assert np.array_equal(y, np_pack(x, s, b, h, d, P)), (s, h, P, b, d)
+                        assert np.array_equal(oracle.unpack(y, s, b, h, d, P, lib=lib), x)
+                        if s <= 8 and h <= 8:
+                            x_all = np.arange(n * P, dtype=np.int32).reshape(P, s // P, b, h, d)
+                            y_all = oracle.seq2head(x_all, s, b, h, d, P, lib=lib)
+                            assert np.array_equal(y_all, np_seq2head(x_all, s, b, h, d, P))
+
+
+def pin_pack_then_route_is_seq2head(lib):
+    """Pack on every rank, then route block r of every rank j to rank r in source
+    order: the result is the whole exchange (the receive side is a view)."""
+    for (s, b, h, d, P) in [(16, 1, 8, 4, 4), (12, 2, 6, 2, 3), (8, 2, 8, 1, 8)]:
+        x_all = np.arange(s * b * h * d, dtype=np.int32).reshape(P, s // P, b, h, d)
+        send = np.stack([oracle.pack(x_all[j], s, b, h, d, P, lib=lib) for j in range(P)])
+        recv = np.stack([np.concatenate([send[j, r] for j in range(P)], axis=0)
+                         for r in range(P)])
+        assert np.array_equal(recv, oracle.seq2head(x_all, s, b, h, d, P, lib=lib))
+
+
+# ---------------------------------------------------------------------------- attention pins
+def _rand_share(seed, s, b, nq, nkv, d, dtype):
+    q = synth.tensor(seed + 1, (s, b, nq, d), dtype)
+    k = synth.tensor(seed + 2, (s, b, nkv, d), dtype)
+    v = synth.tensor(seed + 3, (s, b, nkv, d), dtype)
+    return q, k, v
+
+
+def pin_attn_vs_torch(lib):
+    """Random tiny shares, dense and causal, MHA and GQA, fp32 and bf16 inputs,
+    against torch's float64 attention: max error 1e-12."""
+    cases = [  # s, b, h, h_kv, P, d, dtype
+        (1, 1, 2, 2, 1, 4, "f32"), (7, 1, 2, 2, 1, 8, "f32"), (16, 1, 8, 8, 4, 64, "f32"),
+        (33, 2, 4, 2, 2, 8, "bf16"), (24, 1, 8, 2, 2, 16, "bf16"), (40, 2, 6, 3, 3, 4, "f32"),
+        (19, 1, 4, 1, 1, 128, "bf16"),
+    ]
+    for n, (s, b, h, h_kv, P, d, dtype) in enumerate(cases):
+        q, k, v = _rand_share(900 + 10 * n, s, b, h // P, h_kv // P, d, dtype)
+        for causal in (False, True):
+            o, lse = oracle.attn(q, k, v, s, b, h, h_kv, d, P, causal, lib=lib)
+            o_t, lse_t = torch_attention(widen(q), widen(k), widen(v), causal)
+            assert np.max(np.abs(o - o_t)) < 1e-12, (n, causal, np.max(np.abs(o - o_t)))
+            assert np.max(np.abs(lse - lse_t)) < 1e-12, (n, causal)
+
+
+def pin_attn_large_scores(lib):
+    """Scores of size ~100 (Q scaled by 60): the max subtraction keeps exp finite."""
+    s, b, nq, d = 24, 1, 2, 8
+    q, k, v = _rand_share(950, s, b, nq, nq, d, "f32")
+    q = (q * 60.0).astype(np.float32)
+    for causal in (False, True):
+        o, lse = oracle.attn(q, k, v, s, b, nq, nq, d, 1, causal, lib=lib)
+        o_t, lse_t = torch_attention(widen(q), widen(k), widen(v), causal)
+        assert np.all(np.isfinite(o)) and np.all(np.isfinite(lse))
+        assert np.max(np.abs(o - o_t)) < 1e-10 and np.max(np.abs(lse - lse_t)) < 1e-10
+
+
+def pin_attn_closed_forms(lib):
+    """Q = 0 gives uniform weights; V = c gives O = c; causal row 0 gives V_0
+    exactly; s = 1 gives O = V."""
+    s, b, nq, nkv, d = 13, 2, 4, 2, 8
+    _, k, v = _rand_share(960, s, b, nq, nkv, d, "f32")
+    q0 = np.zeros((s, b, nq, d), dtype=np.float32)
+    vd = v.astype(np.float64)
+    G = nq // nkv
+    o, lse = oracle.attn(q0, k, v, s, b, nq, nkv, d, 1, True, lib=lib)
+    csum = np.cumsum(vd, axis=0) / np.arange(1, s + 1)[:, None, None, None]
+    for i in range(nq):
+        assert np.max(np.abs(o[:, :, i] - csum[:, :, i // G])) < 1e-12
+        assert np.max(np.abs(lse[:, i] - np.log(np.arange(1, s + 1))[None, :])) < 1e-12
+    o, lse = oracle.attn(q0, k, v, s, b, nq, nkv, d, 1, False, lib=lib)
+    mean = vd.mean(axis=0)
+    for i in range(nq):
+        assert np.max(np.abs(o[:, :, i] - mean[None, :, i // G])) < 1e-12
+        assert np.max(np.abs(lse[:, i] - math.log(s))) < 1e-12
+    # V = c
+    q, k, _ = _rand_share(970, s, b, nq, nkv, d, "f32")
+    vc = np.full((s, b, nkv, d), 0.375, dtype=np.float32)
+    for causal in (False, True):
+        o, _ = oracle.attn(q, k, vc, s, b, nq, nkv, d, 1, causal, lib=lib)
+        assert np.max(np.abs(o - 0.375)) < 1e-12
+    # causal row 0 sees only key 0: weight exactly 1
+    o, lse = oracle.attn(q, k, v, s, b, nq, nkv, d, 1, True, lib=lib)
+    for i in range(nq):
+        assert np.array_equal(o[0, :, i], vd[0, :, i // G])
+        sc0 = (q[0, :, i].astype(np.float64) * k[0, :, i // G].astype(np.float64)).sum(-1)
+        assert np.max(np.abs(lse[:, i, 0] - sc0 / math.sqrt(d))) < 1e-12
+    # s = 1
+    q1, k1, v1 = _rand_share(980, 1, b, nq, nkv, d, "bf16")
+    for causal in (False, True):
+        o, _ = oracle.attn(q1, k1, v1, 1, b, nq, nkv, d, 1, causal, lib=lib)
+        for i in range(nq):
+            assert np.array_equal(o[0, :, i], widen(v1)[0, :, i // G])
+
+
+def pin_attn_rows_sum_to_one(lib):
+    """sum_j exp(S_j - LSE) = 1 with S from numpy, and V = 1 gives O = 1."""
+    s, b, nq, d = 21, 1, 3, 16
+    q, k, v = _rand_share(990, s, b, nq, nq, d, "bf16")
+    qd, kd = widen(q), widen(k)
+    for causal in (False, True):
+        _, lse = oracle.attn(q, k, v, s, b, nq, nq, d, 1, causal, lib=lib)
+        for i in range(nq):
+            S = (qd[:, 0, i, :] @ kd[:, 0, i, :].T) / math.sqrt(d)
+            if causal:
+                S = np.where(np.tri(s, dtype=bool), S, -np.inf)
+            tot = np.exp(S - lse[0, i][:, None]).sum(axis=1)
+            assert np.max(np.abs(tot - 1.0)) < 1e-12
+        ones = np.full(v.shape, 0x3F80, dtype=np.uint16)  # bf16 1.0
+        o, _ = oracle.attn(q, k, ones, s, b, nq, nq, d, 1, causal, lib=lib)
+        assert np.max(np.abs(o - 1.0)) < 1e-12
+
+
+def pin_attn_equivariance(lib):
+    """Dense: permuting K and V rows together leaves O unchanged; permuting Q
+    rows permutes O rows."""
+    s, b, nq, nkv, d = 17, 2, 4, 2, 8
+    q, k, v = _rand_share(1000, s, b, nq, nkv, d, "f32")
+    perm = np.argsort(synth.uniform01(1007, s))
+    o, _ = oracle.attn(q, k, v, s, b, nq, nkv, d, 1, False, lib=lib)
+    o2, _ = oracle.attn(q, k[perm], v[perm], s, b, nq, nkv, d, 1, False, lib=lib)
+    assert np.max(np.abs(o - o2)) < 1e-12
+    o3, _ = oracle.attn(q[perm], k, v, s, b, nq, nkv, d, 1, False, lib=lib)
+    assert np.max(np.abs(o3 - o[perm])) < 1e-12
+
+
+def pin_head_independence(lib):
+    """Unsharded attention over all heads of the global tensors, sliced to rank
+    r's heads, equals rank r's attention on its exchanged share (bit-exact)."""
+    s, b, h, h_kv, d, P = 16, 2, 8, 4, 8, 2
+    qg = synth.tensor(1101, (s, b, h, d), "bf16")
+    kg = synth.tensor(1102, (s, b, h_kv, d), "bf16")
+    vg = synth.tensor(1103, (s, b, h_kv, d), "bf16")
+    for causal in (False, True):
+        o_full, lse_full = oracle.attn(qg, kg, vg, s, b, h, h_kv, d, 1, causal, lib=lib)
+        shards = lambda g, hh: g.reshape(P, s // P, b, hh, d)  # noqa: E731 - seq split
+        qs = oracle.seq2head(shards(qg, h), s, b, h, d, P, lib=lib)
+        ks = oracle.seq2head(shards(kg, h_kv), s, b, h_kv, d, P, lib=lib)
+        vs = oracle.seq2head(shards(vg, h_kv), s, b, h_kv, d, P, lib=lib)
+        hp = h // P
+        for r in range(P):
+            o_r, lse_r = oracle.attn(qs[r], ks[r], vs[r], s, b, h, h_kv, d, P, causal, lib=lib)
+            assert np.array_equal(o_r, o_full[:, :, r * hp:(r + 1) * hp])
+            assert np.array_equal(lse_r, lse_full[:, r * hp:(r + 1) * hp])
+
+
+def pin_rows_match_full(lib):
+    """attn_rows on a row sample equals the full evaluation at those rows."""
+    s, b, nq, nkv, d = 50, 2, 4, 1, 16
+    q, k, v = _rand_share(1200, s, b, nq, nkv, d, "bf16")
+    rows = synth.row_sample(1207, s, b, nq, n_random=8, edge=3, tile_bounds=(16,))
+    for causal in (False, True):
+        o, lse = oracle.attn(q, k, v, s, b, nq, nkv, d, 1, causal, lib=lib)
+        orows, lrows = oracle.attn_rows(q, k, v, rows, s, b, nq, nkv, d, 1, causal, lib=lib)
+        assert np.array_equal(orows, o[rows[:, 2], rows[:, 0], rows[:, 1]])
+        assert np.array_equal(lrows, lse[rows[:, 0], rows[:, 1], rows[:, 2]])
+
+
+LAYOUT_PINS = [pin_alltoall_worked_example, pin_two_card_blocks, pin_conservation_4card,
+               pin_inverse_random_bits, pin_brute_force_tiny, pin_pack_then_route_is_seq2head]
+ATTN_PINS = [pin_attn_vs_torch, pin_attn_large_scores, pin_attn_closed_forms,
+             pin_attn_rows_sum_to_one, pin_attn_equivariance, pin_head_independence,
+             pin_rows_match_full]
+ALL_PINS = LAYOUT_PINS + ATTN_PINS

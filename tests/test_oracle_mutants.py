@@ -1,0 +1,62 @@
+"""Plant plausible mistakes in copies of the oracle (on the CPU) and check that
+its pins catch every one.  Shows the pins constrain the oracle rather than
+restate it."""
+import os
+import subprocess
+
+import pytest
+
+import oracle
+import oracle_pins
+
+SRC = os.path.join(os.path.dirname(oracle.__file__), "ulys_oracle.c")
+
+# (name, text in the oracle, replacement)
+MUTANTS = [
+    ("drop_scale", "scores[j] = acc * scale;", "scores[j] = acc;"),
+    ("causal_excludes_diagonal", "J->causal ? t + 1 : J->s", "J->causal ? t : J->s"),
+    ("gqa_round_robin", "const int64_t g = i / (nq / nkv);", "const int64_t g = i % nkv;"),
+    ("no_max_shift_in_lse", "*lse_out = m + log(l);", "*lse_out = log(l);"),
+    ("drop_normalisation", "o_row[e] /= l;", "o_row[e] /= 1.0;"),
+    ("k_row_uses_query_head", "J->k + ((j * b + be) * nkv + g) * d",
+     "J->k + ((j * b + be) * nkv + (i % nkv)) * d"),
+    ("pack_heads_strided", "int64_t xi = ((t * b + be) * h + (r * hp + k)) * d + e;\n"
+     "            memcpy(dst + yi * elt",
+     "int64_t xi = ((t * b + be) * h + (k * P + r)) * d + e;\n"
+     "            memcpy(dst + yi * elt"),
+    ("seq2head_rank_major_tokens", "int64_t tg = j * sl + t; /* position",
+     "int64_t tg = t * P + j; /* position"),
+    ("unpack_swaps_groups", "int64_t xi = ((t * b + be) * h + (r * hp + k)) * d + e;\n"
+     "            int64_t yi = (((r * sl + t) * b + be) * hp + k) * d + e;\n"
+     "            memcpy(dst + xi",
+     "int64_t xi = ((t * b + be) * h + ((P - 1 - r) * hp + k)) * d + e;\n"
+     "            int64_t yi = (((r * sl + t) * b + be) * hp + k) * d + e;\n"
+     "            memcpy(dst + xi"),
+    ("bf16_widen_wrong_shift", "<< 16;", "<< 15;"),
+]
+
+
+@pytest.mark.parametrize("name,old,new", MUTANTS, ids=[m[0] for m in MUTANTS])
+def test_mutant_is_caught(name, old, new, tmp_path):
+    src = open(SRC, encoding="utf-8").read()
+    assert src.count(old) == 1, f"mutation site for {name} not unique"
+    mutated = tmp_path / f"oracle_{name}.c"
+    mutated.write_text(src.replace(old, new), encoding="utf-8")
+    so = tmp_path / f"liboracle_{name}.so"
+    oracle.build(str(mutated), str(so))
+    lib = oracle.load(str(so))
+    caught = []
+    for pin in oracle_pins.ALL_PINS:
+        try:
+            pin(lib)
+        except (AssertionError, ValueError):
+            caught.append(pin.__name__)
+    assert caught, f"no pin catches mutant {name}"
+
+
+def test_unmutated_copy_passes(tmp_path):
+    so = tmp_path / "liboracle_copy.so"
+    oracle.build(SRC, str(so))
+    lib = oracle.load(str(so))
+    for pin in oracle_pins.ALL_PINS:
+        pin(lib)
