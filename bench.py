@@ -1,0 +1,234 @@
+"""Benchmark of the Ulysses per-rank hot path on one MI355X.
+
+A step is one pass of the whole path over one rank's share of a layer:
+pack Q, K, V (seq->head send side), head-sharded attention over the whole
+sequence, unpack O (head->seq receive side).  The all-to-all itself is not
+part of a one-GPU step: the rank's own send buffer stands in for its receive
+buffer (same shape, [s, b, h/P, d]), so the attention consumes the pack's
+output and the unpack consumes the attention's output.
+
+Prints ONE JSON line.  ``value`` is attention FLOPs per step over the whole
+step time (TFLOP/s); per-kernel durations come from HIP events recorded on
+the stream the kernels run on, inside the timed region.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "attn TFLOP/s (% bf16 MFMA peak) + pack/unpack GB/s (% HBM peak), 1 GPU"
+PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
+PEAK_F32_TFLOPS = 157.3    # MI355X fp32 vector
+PEAK_HBM_GBPS = 8000.0     # MI355X HBM3E
+PROFILE_DIR = os.path.join(ROOT, "profiles")
+
+
+def parse_args():
+    ap = argparse.ArgumentParser(description=__doc__)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="gpt1.2b-32k")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0,
+                    help="wall-time budget of the oracle's cpu_baseline sample")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    return ap.parse_args()
+
+
+def source_digest(path: str) -> str:
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()
+
+
+def counter_traffic(kernel_src: str, workload: str):
+    """HBM bytes per launch from committed rocprofv3 counter summaries, or None
+    when none exist or the kernel source changed since they were taken."""
+    path = os.path.join(PROFILE_DIR, f"attn_bf16_{workload}_counters.txt")
+    if not os.path.exists(path):
+        return None
+    fields = {}
+    with open(path, encoding="utf-8") as f:
+        for line in f:
+            if ":" in line and not line.startswith("#"):
+                key, val = line.split(":", 1)
+                fields[key.strip()] = val.strip()
+    if fields.get("source_sha256") != source_digest(kernel_src):
+        return None
+    try:
+        return float(fields["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def cpu_baseline(w, q, k, v, budget_s: float):
+    """The oracle, as it stands, on a bounded sample of the same share: random
+    query rows in batches until the wall-time budget is spent."""
+    import numpy as np
+
+    import oracle
+    from ulysses_head_sharded_amd import synth
+
+    threads = oracle.default_threads()
+    u = synth.uniform01(100 * w.c + 7, 1 << 16)
+    flops, rows_done, t_used, idx = 0.0, 0, 0.0, 0
+    batch = max(threads, 16)
+    while t_used < budget_s and idx + batch <= u.size:
+        sel = u[idx:idx + batch]
+        idx += batch
+        t = np.minimum((sel * w.s).astype(np.int64), w.s - 1)
+        rows = np.stack([np.zeros_like(t), (np.arange(t.size) % w.hp), t], axis=1)
+        keys = (t + 1) if w.causal else np.full_like(t, w.s)
+        t0 = time.perf_counter()
+        oracle.attn_rows(q, k, v, rows, w.s, w.b, w.h, w.h_kv, w.d, w.P, w.causal,
+                         nthreads=threads)
+        t_used += time.perf_counter() - t0
+        flops += float(4 * w.d * keys.sum())
+        rows_done += t.size
+    return {
+        "value": flops / t_used / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+        "sample": f"{rows_done} uniformly drawn query rows of the {w.name} share "
+                  f"(fp64 oracle, {t_used:.1f} s wall, algorithmic flops of the sample)",
+    }
+
+
+def main():
+    args = parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one rank's share on ONE GPU; --gpus {args.gpus} is not "
+              "supported (the all-to-all across GPUs is not part of this build)",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    from ulysses_head_sharded_amd import binding, synth
+    from ulysses_head_sharded_amd.workloads import WORKLOADS
+
+    binding.load()
+    w = WORKLOADS[args.workload]
+    dev = torch.device("cuda:0")
+    tdt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+    sl, hp, hkvp = w.s // w.P, w.hp, w.hkvp
+
+    def upload(a):
+        if a.dtype == np.uint16:
+            return torch.from_numpy(a.view(np.int16)).to(dev).view(torch.bfloat16)
+        return torch.from_numpy(a).to(dev)
+
+    # rank-local shards [s/P, b, heads, d] of Q, K, V (seeded, synthetic)
+    xq_h = synth.tensor(100 * w.c + 1, (sl, w.b, w.h, w.d), w.dtype)
+    xk_h = synth.tensor(100 * w.c + 2, (sl, w.b, w.h_kv, w.d), w.dtype)
+    xv_h = synth.tensor(100 * w.c + 3, (sl, w.b, w.h_kv, w.d), w.dtype)
+    xq, xk, xv = upload(xq_h), upload(xk_h), upload(xv_h)
+    yq = torch.empty((w.P, sl, w.b, hp, w.d), dtype=tdt, device=dev)
+    yk = torch.empty((w.P, sl, w.b, hkvp, w.d), dtype=tdt, device=dev)
+    yv = torch.empty((w.P, sl, w.b, hkvp, w.d), dtype=tdt, device=dev)
+    o = torch.empty((w.s, w.b, hp, w.d), dtype=tdt, device=dev)
+    xo = torch.empty((sl, w.b, w.h, w.d), dtype=tdt, device=dev)
+    code = binding.ULYS_BF16 if w.dtype == "bf16" else binding.ULYS_F32
+    stream = torch.cuda.current_stream()
+    sh = stream.cuda_stream
+
+    def call(rc, what):
+        if rc != 0:
+            raise RuntimeError(f"{what}: {binding.ulys_status_string(rc)}")
+
+    ev = {n: [] for n in ("pack0", "pack1", "attn0", "attn1", "unpack1")}
+
+    def step(record: bool):
+        if record:
+            e = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+            e[0].record(stream)
+        call(binding.ulys_pack_seq2head(xq.data_ptr(), yq.data_ptr(), w.s, w.b, w.h, w.d, w.P,
+                                        code, sh), "pack q")
+        call(binding.ulys_pack_seq2head(xk.data_ptr(), yk.data_ptr(), w.s, w.b, w.h_kv, w.d,
+                                        w.P, code, sh), "pack k")
+        call(binding.ulys_pack_seq2head(xv.data_ptr(), yv.data_ptr(), w.s, w.b, w.h_kv, w.d,
+                                        w.P, code, sh), "pack v")
+        if record:
+            e[1].record(stream)
+        # the send buffers stand in for the receive buffers: [P, s/P, b, hp, d] == [s, b, hp, d]
+        call(binding.ulys_attn_fwd(yq.data_ptr(), yk.data_ptr(), yv.data_ptr(), o.data_ptr(),
+                                   None, w.s, w.b, w.h, w.h_kv, w.d, w.P, int(w.causal), code,
+                                   sh), "attn")
+        if record:
+            e[2].record(stream)
+        call(binding.ulys_unpack_head2seq(o.data_ptr(), xo.data_ptr(), w.s, w.b, w.h, w.d, w.P,
+                                          code, sh), "unpack o")
+        if record:
+            e[3].record(stream)
+            ev["pack0"].append(e[0])
+            ev["pack1"].append(e[1])
+            ev["attn1"].append(e[2])
+            ev["unpack1"].append(e[3])
+
+    for _ in range(args.warmup):
+        step(False)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step(True)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_step = (t1 - t0) * 1e3 / args.steps
+
+    pack_ms = float(np.mean([a.elapsed_time(b) for a, b in zip(ev["pack0"], ev["pack1"])]))
+    attn_ms = float(np.mean([a.elapsed_time(b) for a, b in zip(ev["pack1"], ev["attn1"])]))
+    unpack_ms = float(np.mean([a.elapsed_time(b) for a, b in zip(ev["attn1"], ev["unpack1"])]))
+
+    flops = w.attn_flops()
+    attn_tflops = flops / (attn_ms * 1e-3) / 1e12
+    peak = PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_F32_TFLOPS
+    pack_bytes = 2 * (w.shard_bytes() + 2 * w.shard_bytes(kv=True))
+    unpack_bytes = 2 * w.shard_bytes()
+    pack_gbps = pack_bytes / (pack_ms * 1e-3) / 1e9
+    unpack_gbps = unpack_bytes / (unpack_ms * 1e-3) / 1e9
+    layout_gbps = (pack_bytes + unpack_bytes) / ((pack_ms + unpack_ms) * 1e-3) / 1e9
+    kernel_src = os.path.join(ROOT, "ulysses_head_sharded_amd", "csrc",
+                              "attn_bf16.hip" if w.dtype == "bf16" else "attn_f32.hip")
+
+    rec = {
+        "metric": METRIC,
+        "value": round(flops / (ms_step * 1e-3) / 1e12, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic (seeded N(0,1), SplitMix64 + Box-Muller)",
+        "config": {"workload": w.name, "P": w.P, "s": w.s, "b": w.b, "h": w.h, "h_kv": w.h_kv,
+                   "d_h": w.d, "causal": w.causal, "share": f"[{w.s},{w.b},{hp},{w.d}]"},
+        "attn": {"ms": round(attn_ms, 4), "tflops": round(attn_tflops, 2),
+                 "frac_peak": round(attn_tflops / peak, 4), "flops": flops},
+        "layout": {"pack_qkv_us": round(pack_ms * 1e3, 2), "unpack_o_us": round(unpack_ms * 1e3, 2),
+                   "pack_gbps": round(pack_gbps, 1), "unpack_gbps": round(unpack_gbps, 1),
+                   "gbps": round(layout_gbps, 1),
+                   "frac_hbm_peak": round(layout_gbps / PEAK_HBM_GBPS, 4),
+                   "bytes": pack_bytes + unpack_bytes},
+        "roofline": {"bound": "mfma", "achieved": round(attn_tflops, 2), "peak": peak,
+                     "unit": "TFLOP/s", "frac": round(attn_tflops / peak, 4),
+                     "traffic": counter_traffic(kernel_src, w.name)},
+    }
+    if not args.no_cpu_baseline:
+        # the oracle gets its own seeded share-shaped inputs (same distribution)
+        q_h = synth.tensor(100 * w.c + 1, (w.s, w.b, hp, w.d), w.dtype)
+        k_h = synth.tensor(100 * w.c + 2, (w.s, w.b, hkvp, w.d), w.dtype)
+        v_h = synth.tensor(100 * w.c + 3, (w.s, w.b, hkvp, w.d), w.dtype)
+        rec["cpu_baseline"] = cpu_baseline(w, q_h, k_h, v_h, args.cpu_seconds)
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

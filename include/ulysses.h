@@ -1,0 +1,125 @@
+/*
+ * ulysses.h -- C ABI of the MI355X (gfx950) per-rank hot path of
+ * DeepSpeed-Ulysses sequence parallelism: the local halves of the two
+ * all-to-alls and the head-sharded attention between them.
+ *
+ * Pages cited (title, then section):
+ *   [ATLAS] "02 · DeepSpeed-Ulysses" (llm-infra-atlas, parallel/04_cp),
+ *           §1 attention is parallel over heads, §2 the all-to-all as a
+ *           transpose, §3 the head-count constraint.
+ *   [DSU]   "DeepSpeed-Ulysses 深度解析：用 All-to-All 序列并行撑起百万 Token
+ *           超长序列训练", core design steps 1-5 and the DistributedAttention
+ *           signature (scatter_idx, gather_idx, sp_stream, num_kv_heads).
+ *   [SPCP]  "长上下文训练中的 SP 与 CP：从 Megatron 到分布式 Attention",
+ *           the Ulysses section (P must divide the KV head count under GQA)
+ *           and the Ring section (online softmax, scale 1/sqrt(d_h)).
+ *
+ * General conventions
+ *   - Every tensor pointer is a DEVICE pointer to a contiguous row-major
+ *     array (last axis fastest) and must be 16-byte aligned.  The caller owns
+ *     every buffer; the library allocates nothing and keeps no state between
+ *     calls, so all entry points are thread-safe.
+ *   - s, h and h_kv are GLOBAL sizes (whole sequence, all heads); P is the
+ *     number of ranks of the sequence-parallel group.  Shapes below use
+ *     sl = s/P, hp = h/P, hkvp = h_kv/P.
+ *   - stream is a hipStream_t passed as void* (NULL = the null stream).  Each
+ *     entry only enqueues kernels on it and never synchronizes.
+ *   - Arguments are validated on the host first; on any error the entry
+ *     point returns a negative ULYS_ERR_* code and launches nothing.  A
+ *     launch failure returns ULYS_ERR_HIP.  No entry prints, throws or sets
+ *     errno.
+ *   - Outputs are written out of place: the byte ranges of inputs and
+ *     outputs must not overlap (ULYS_ERR_ALIAS).
+ */
+#ifndef ULYSSES_H_
+#define ULYSSES_H_
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Element types. */
+typedef enum { ULYS_F32 = 0, ULYS_BF16 = 1 } ulys_dtype;
+
+/* Status codes. */
+enum {
+  ULYS_OK = 0,
+  ULYS_ERR_NULL = -1,         /* a required pointer is NULL                      */
+  ULYS_ERR_DIM = -2,          /* a size is <= 0 or too large                      */
+  ULYS_ERR_DIVISIBILITY = -3, /* P does not divide s, h or h_kv, or h_kv !| h     */
+  ULYS_ERR_UNSUPPORTED = -4,  /* dtype or head size not supported by the kernel   */
+  ULYS_ERR_ALIGNMENT = -5,    /* a pointer is not 16-byte aligned                 */
+  ULYS_ERR_ALIAS = -6,        /* an output overlaps an input or another output    */
+  ULYS_ERR_HIP = -7           /* the HIP runtime reported a launch error          */
+};
+
+/*
+ * Seq->head all-to-all, send side (pack), one rank.
+ * [ATLAS] §2: the local [sl, heads, d] is split along the head axis into P
+ * equal groups and group r is sent to rank r; [DSU] step 3 (the exchange of
+ * Q, K and V before attention, scatter_idx=2).  For K and V pass h = h_kv.
+ *
+ *   x : input  [sl, b, h, d_h]        the rank's sequence shard
+ *   y : output [P, sl, b, hp, d_h]    send buffer; block r is for rank r,
+ *                                     y[r] = x[:, :, r*hp:(r+1)*hp, :]
+ * The receive side needs no kernel: rank r's P received blocks, stored in
+ * source-rank order, are exactly its [s, b, hp, d_h] share (the sequence
+ * axis is outermost).  The move is bit-exact for every bit pattern.
+ * Errors: NULL pointers, sizes <= 0, P !| s or P !| h, dtype not F32/BF16,
+ * misaligned or overlapping buffers.
+ */
+int ulys_pack_seq2head(const void* x, void* y, int64_t s, int64_t b, int64_t h,
+                       int64_t d_h, int32_t P, int32_t dtype, void* stream);
+
+/*
+ * Head->seq all-to-all, receive side (unpack), one rank.
+ * [ATLAS] §2: the second all-to-all inverts the first: the P blocks received
+ * (block r holds head group r of this rank's sequence segment) are
+ * concatenated along the head axis; [DSU] step 5 (gather_idx=2 for the
+ * output).  It is the exact inverse of ulys_pack_seq2head.
+ *
+ *   y : input  [P, sl, b, hp, d_h]    received blocks, block r = head group r
+ *   x : output [sl, b, h, d_h]        x[:, :, r*hp:(r+1)*hp, :] = y[r]
+ * Errors: as ulys_pack_seq2head.
+ */
+int ulys_unpack_head2seq(const void* y, void* x, int64_t s, int64_t b, int64_t h,
+                         int64_t d_h, int32_t P, int32_t dtype, void* stream);
+
+/*
+ * Head-sharded attention on one rank's share (forward).
+ * [ATLAS] §1 and [DSU] step 4: with the whole sequence for hp heads, each
+ * head computes softmax(Q K^T / sqrt(d_h)) V independently; the scale is
+ * fixed at 1/sqrt(d_h) ([SPCP], Ring section).  causal != 0 lets query t see
+ * keys j <= t (global positions; the received blocks are in sequence order).
+ * GQA: query head i of the share reads KV head i / (h/h_kv), i.e. contiguous
+ * groups ([DSU] num_kv_heads; [SPCP] requires P | h_kv).
+ *
+ *   q   : [s, b, hp, d_h]      o : [s, b, hp, d_h]   (same dtype as q)
+ *   k,v : [s, b, hkvp, d_h]
+ *   lse : [b, hp, s] fp32 natural-log sum of exp of the scaled scores,
+ *         or NULL to skip it.
+ * O is accumulated in fp32 and rounded once (nearest-even) to the dtype.
+ * Supported: ULYS_BF16 with d_h in {64, 128} (MFMA kernel); ULYS_F32 with
+ * d_h in {64, 128} (fp32 kernel).  s may be any positive multiple of P.
+ * Errors: as above, plus h_kv !| h, P !| h_kv, unsupported d_h/dtype, and
+ * o or lse overlapping q, k, v or each other.
+ */
+int ulys_attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+                  int64_t s, int64_t b, int64_t h, int64_t h_kv, int64_t d_h, int32_t P,
+                  int32_t causal, int32_t dtype, void* stream);
+
+/* Static, human-readable text for a status code (never NULL). */
+const char* ulys_status_string(int status);
+
+/* ABI version of this header: (major << 16) | minor. */
+int ulys_abi_version(void);
+
+#define ULYS_ABI_VERSION ((1 << 16) | 0)
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ULYSSES_H_ */

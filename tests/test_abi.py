@@ -1,0 +1,111 @@
+"""The C-ABI library: it loads, exports every symbol the header declares, and
+rejects bad arguments on the host before any HIP call (no GPU needed: every
+call here returns from validation without launching)."""
+import os
+import re
+
+import pytest
+
+from ulysses_head_sharded_amd import binding as B
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "ulysses.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(B.LIB_PATH):
+        from ulysses_head_sharded_amd import build
+        build.build()
+    return B.load()
+
+
+def declared_symbols():
+    text = open(HEADER, encoding="utf-8").read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(ulys_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_header_declares_the_abi():
+    assert declared_symbols() == sorted(B.EXPORTED)
+
+
+def test_every_declared_symbol_is_exported(lib):
+    for name in declared_symbols():
+        assert hasattr(lib, name), name
+
+
+def test_version(lib):
+    assert B.ulys_abi_version() == (1 << 16)
+
+
+def test_status_strings(lib):
+    codes = [B.ULYS_OK, B.ULYS_ERR_NULL, B.ULYS_ERR_DIM, B.ULYS_ERR_DIVISIBILITY,
+             B.ULYS_ERR_UNSUPPORTED, B.ULYS_ERR_ALIGNMENT, B.ULYS_ERR_ALIAS, B.ULYS_ERR_HIP]
+    texts = [B.ulys_status_string(c) for c in codes]
+    assert len(set(texts)) == len(texts)
+    assert B.ulys_status_string(12345) == "unknown status"
+
+
+# fake, never-dereferenced device addresses: validation rejects every call below
+X, Y = 0x7F0000000000, 0x7F0100000000
+
+
+@pytest.mark.parametrize("fn", [B.ulys_pack_seq2head, B.ulys_unpack_head2seq])
+@pytest.mark.parametrize("args,expect", [
+    ((None, Y, 16, 1, 8, 64, 4, B.ULYS_BF16), B.ULYS_ERR_NULL),
+    ((X, None, 16, 1, 8, 64, 4, B.ULYS_BF16), B.ULYS_ERR_NULL),
+    ((X, Y, 0, 1, 8, 64, 4, B.ULYS_BF16), B.ULYS_ERR_DIM),
+    ((X, Y, 16, -1, 8, 64, 4, B.ULYS_BF16), B.ULYS_ERR_DIM),
+    ((X, Y, 16, 1, 8, 64, 0, B.ULYS_BF16), B.ULYS_ERR_DIM),
+    ((X, Y, 18, 1, 8, 64, 4, B.ULYS_BF16), B.ULYS_ERR_DIVISIBILITY),
+    ((X, Y, 16, 1, 6, 64, 4, B.ULYS_BF16), B.ULYS_ERR_DIVISIBILITY),
+    ((X, Y, 16, 1, 8, 64, 4, 7), B.ULYS_ERR_UNSUPPORTED),
+    ((X + 8, Y, 16, 1, 8, 64, 4, B.ULYS_F32), B.ULYS_ERR_ALIGNMENT),
+    ((X, Y + 2, 16, 1, 8, 64, 4, B.ULYS_F32), B.ULYS_ERR_ALIGNMENT),
+    ((X, X + 4096, 16, 1, 8, 64, 4, B.ULYS_F32), B.ULYS_ERR_ALIAS),   # 8 KiB each
+    ((X + 4096, X, 16, 1, 8, 64, 4, B.ULYS_F32), B.ULYS_ERR_ALIAS),
+    ((X, Y, 1 << 41, 1, 8, 64, 1, B.ULYS_F32), B.ULYS_ERR_DIM),
+])
+def test_layout_rejects(lib, fn, args, expect):
+    assert fn(*args) == expect
+
+
+Q, K, V, O, L = (0x7F0000000000 + i * (1 << 32) for i in range(5))
+
+
+@pytest.mark.parametrize("args,expect", [
+    ((None, K, V, O, L, 64, 1, 8, 8, 128, 4, 1, B.ULYS_BF16), B.ULYS_ERR_NULL),
+    ((Q, K, V, None, L, 64, 1, 8, 8, 128, 4, 1, B.ULYS_BF16), B.ULYS_ERR_NULL),
+    ((Q, K, V, O, L, 0, 1, 8, 8, 128, 4, 1, B.ULYS_BF16), B.ULYS_ERR_DIM),
+    ((Q, K, V, O, L, 64, 1, 8, 0, 128, 4, 1, B.ULYS_BF16), B.ULYS_ERR_DIM),
+    ((Q, K, V, O, L, 66, 1, 8, 8, 128, 4, 1, B.ULYS_BF16), B.ULYS_ERR_DIVISIBILITY),
+    ((Q, K, V, O, L, 64, 1, 8, 2, 128, 4, 1, B.ULYS_BF16), B.ULYS_ERR_DIVISIBILITY),  # P !| h_kv
+    ((Q, K, V, O, L, 64, 1, 12, 8, 128, 4, 1, B.ULYS_BF16), B.ULYS_ERR_DIVISIBILITY),
+    ((Q, K, V, O, L, 64, 1, 8, 8, 96, 4, 1, B.ULYS_BF16), B.ULYS_ERR_UNSUPPORTED),
+    ((Q, K, V, O, L, 64, 1, 8, 8, 128, 4, 1, 3), B.ULYS_ERR_UNSUPPORTED),
+    ((Q, K + 4, V, O, L, 64, 1, 8, 8, 128, 4, 1, B.ULYS_BF16), B.ULYS_ERR_ALIGNMENT),
+    ((Q, K, V, O, L + 4, 64, 1, 8, 8, 128, 4, 1, B.ULYS_BF16), B.ULYS_ERR_ALIGNMENT),
+    ((Q, K, V, Q + 256, L, 64, 1, 8, 8, 128, 4, 1, B.ULYS_BF16), B.ULYS_ERR_ALIAS),
+    ((Q, K, V, V, None, 64, 1, 8, 8, 128, 4, 1, B.ULYS_BF16), B.ULYS_ERR_ALIAS),
+    ((Q, K, V, O, O + 64, 64, 1, 8, 8, 128, 4, 1, B.ULYS_BF16), B.ULYS_ERR_ALIAS),
+    ((Q, K, V, O, K, 64, 1, 8, 8, 128, 4, 1, B.ULYS_BF16), B.ULYS_ERR_ALIAS),
+])
+def test_attn_rejects(lib, args, expect):
+    assert B.ulys_attn_fwd(*args) == expect
+
+
+def test_tensor_helper_raises_status(lib):
+    err = B.UlyssesError(B.ULYS_ERR_DIVISIBILITY, "ulys_pack_seq2head")
+    assert "divide" in str(err) and err.status == B.ULYS_ERR_DIVISIBILITY
+
+
+def test_product_path_does_not_reach_the_oracle():
+    """The package sources never import or load the CPU oracle."""
+    pkg = os.path.join(ROOT, "ulysses_head_sharded_amd")
+    for dirpath, _, files in os.walk(pkg):
+        for f in files:
+            if f.endswith((".py", ".cpp", ".hip", ".h")):
+                text = open(os.path.join(dirpath, f), encoding="utf-8").read()
+                assert "import oracle" not in text and "ulys_oracle" not in text, f
+                assert "from oracle" not in text, f

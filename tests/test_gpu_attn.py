@@ -1,0 +1,167 @@
+"""GPU parity of the head-sharded attention against the fp64 CPU oracle.
+
+Tolerances: max |O_gpu - O_ref| <= 2e-2 for bf16 inputs, <= 1e-4 for fp32
+inputs (the oracle runs in fp64 on the same rounded inputs).  LSE is checked to
+1e-3 (bf16) / 1e-5 (fp32) absolute."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from gpu_util import Guarded, as_f64, dev, from_dev, share_inputs, to_dev
+from ulysses_head_sharded_amd import binding, synth
+from ulysses_head_sharded_amd.workloads import WORKLOADS
+
+pytestmark = pytest.mark.gpu
+
+TOL = {"bf16": 2e-2, "f32": 1e-4}
+LSE_TOL = {"bf16": 1e-3, "f32": 1e-5}
+TORCH_DT = {"bf16": torch.bfloat16, "f32": torch.float32}
+
+
+def gpu_attn(q, k, v, s, b, h, h_kv, d, P, causal, dtype, want_lse=True):
+    dev()
+    hp = h // P
+    qd, kd, vd = to_dev(q), to_dev(k), to_dev(v)
+    o = Guarded((s, b, hp, d), TORCH_DT[dtype])
+    lse = Guarded((b, hp, s), torch.float32) if want_lse else None
+    rc = binding.ulys_attn_fwd(qd.data_ptr(), kd.data_ptr(), vd.data_ptr(), o.tensor.data_ptr(),
+                               lse.tensor.data_ptr() if lse else None, s, b, h, h_kv, d, P,
+                               int(causal), binding.ULYS_BF16 if dtype == "bf16" else
+                               binding.ULYS_F32, torch.cuda.current_stream().cuda_stream)
+    assert rc == 0, binding.ulys_status_string(rc)
+    torch.cuda.synchronize()
+    assert o.guards_intact()
+    if lse:
+        assert lse.guards_intact()
+    return from_dev(o.tensor), (from_dev(lse.tensor) if lse else None)
+
+
+# s spans several 64-key tiles with ragged tails; (h, h_kv, P) covers MHA,
+# GQA 4:1 and 8:1 (two head subgroups per KV head) and MQA
+SMALL = []
+for dtype, d in [("bf16", 128), ("bf16", 64), ("f32", 64), ("f32", 128)]:
+    for (s, b) in [(1, 1), (5, 2), (64, 1), (65, 1), (200, 2), (321, 1), (1000, 1)]:
+        for (h, h_kv, P) in [(2, 2, 1), (8, 2, 2), (16, 2, 1), (8, 8, 4), (4, 1, 1)]:
+            if dtype == "f32" and s > 321:
+                continue
+            for causal in (False, True):
+                SMALL.append((dtype, d, s, b, h, h_kv, P, causal))
+
+
+@pytest.mark.parametrize("dtype,d,s,b,h,h_kv,P,causal", SMALL)
+def test_small_full_parity(dtype, d, s, b, h, h_kv, P, causal):
+    print(f"case {dtype} d={d} s={s} b={b} h={h} h_kv={h_kv} P={P} causal={causal}",
+          flush=True)
+    q, k, v = share_inputs(7, s, b, h // P, h_kv // P, d, dtype)
+    o, lse = gpu_attn(q, k, v, s, b, h, h_kv, d, P, causal, dtype)
+    o_ref, lse_ref = oracle.attn(q, k, v, s, b, h, h_kv, d, P, causal)
+    err = np.max(np.abs(as_f64(o) - o_ref))
+    assert err <= TOL[dtype], err
+    assert np.max(np.abs(lse.astype(np.float64) - lse_ref)) <= LSE_TOL[dtype]
+
+
+def test_tiny_workload_parity():
+    w = WORKLOADS["tiny"]
+    q, k, v = share_inputs(w.c, w.s, w.b, w.hp, w.hkvp, w.d, w.dtype)
+    o, lse = gpu_attn(q, k, v, w.s, w.b, w.h, w.h_kv, w.d, w.P, w.causal, w.dtype)
+    o_ref, lse_ref = oracle.attn(q, k, v, w.s, w.b, w.h, w.h_kv, w.d, w.P, w.causal)
+    assert np.max(np.abs(as_f64(o) - o_ref)) <= TOL[w.dtype]
+    assert np.max(np.abs(lse - lse_ref)) <= LSE_TOL[w.dtype]
+
+
+# full-size workloads: sampled rows (the oracle computes them one by one)
+FULL = {
+    "gpt1.2b-32k": dict(n_random=256, edge=32),
+    "mha-128k": dict(n_random=48, edge=16),
+    "gqa-64k": dict(n_random=64, edge=16),
+    "mtok-1m": dict(n_random=12, edge=6),
+    "dit-256k": dict(n_random=6, edge=4),
+}
+
+
+@pytest.mark.parametrize("name", list(FULL))
+def test_full_size_sampled_parity(name):
+    w = WORKLOADS[name]
+    print(f"case {name}: s={w.s} b={w.b} hp={w.hp} hkvp={w.hkvp} causal={w.causal}", flush=True)
+    q, k, v = share_inputs(w.c, w.s, w.b, w.hp, w.hkvp, w.d, w.dtype)
+    o, lse = gpu_attn(q, k, v, w.s, w.b, w.h, w.h_kv, w.d, w.P, w.causal, w.dtype)
+    rows = synth.row_sample(100 * w.c + 7, w.s, w.b, w.hp, tile_bounds=(64, 128),
+                            **FULL[name])
+    o_ref, lse_ref = oracle.attn_rows(q, k, v, rows, w.s, w.b, w.h, w.h_kv, w.d, w.P,
+                                      w.causal)
+    got = as_f64(o[rows[:, 2], rows[:, 0], rows[:, 1]])
+    err = np.max(np.abs(got - o_ref))
+    print(f"  {rows.shape[0]} rows, max err {err:.3e}", flush=True)
+    assert err <= TOL[w.dtype]
+    lse_got = lse[rows[:, 0], rows[:, 1], rows[:, 2]].astype(np.float64)
+    assert np.max(np.abs(lse_got - lse_ref)) <= LSE_TOL[w.dtype]
+    # properties over every row: finite, and |O| bounded by max |V| (convex combination)
+    of = as_f64(o)
+    assert np.all(np.isfinite(of)) and np.all(np.isfinite(lse))
+    assert np.max(np.abs(of)) <= np.max(np.abs(as_f64(v))) + TOL[w.dtype]
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_value_ones_gives_ones(causal):
+    s, b, h, h_kv, d, P = 777, 1, 4, 2, 128, 1
+    q, k, _ = share_inputs(11, s, b, h, h_kv, d, "bf16")
+    ones = np.full((s, b, h_kv, d), 0x3F80, dtype=np.uint16)
+    o, _ = gpu_attn(q, k, ones, s, b, h, h_kv, d, P, causal, "bf16", want_lse=False)
+    assert np.max(np.abs(as_f64(o) - 1.0)) <= TOL["bf16"]
+
+
+def test_causal_row0_is_v0_and_q_zero_is_mean():
+    s, b, h, d = 300, 2, 2, 128
+    q, k, v = share_inputs(12, s, b, h, h, d, "bf16")
+    o, _ = gpu_attn(q, k, v, s, b, h, h, d, 1, True, "bf16")
+    assert np.array_equal(o[0], v[0])  # weight exactly 1 on key 0, exact bf16 round trip
+    qz = np.zeros_like(q)
+    o, lse = gpu_attn(qz, k, v, s, b, h, h, d, 1, True, "bf16")
+    mean = np.cumsum(as_f64(v), axis=0) / np.arange(1, s + 1)[:, None, None, None]
+    assert np.max(np.abs(as_f64(o) - mean)) <= TOL["bf16"]
+    assert np.max(np.abs(lse - np.log(np.arange(1, s + 1))[None, None, :])) <= 1e-4
+
+
+def test_large_scores_stay_finite():
+    s, b, h, d = 500, 1, 2, 128
+    q, k, v = share_inputs(13, s, b, h, h, d, "f32")
+    q8 = synth.f32_to_bf16_bits(q * 8.0)
+    kb, vb = synth.f32_to_bf16_bits(k), synth.f32_to_bf16_bits(v)
+    for causal in (False, True):
+        o, lse = gpu_attn(q8, kb, vb, s, b, h, h, d, 1, causal, "bf16")
+        o_ref, lse_ref = oracle.attn(q8, kb, vb, s, b, h, h, d, 1, causal)
+        assert np.all(np.isfinite(as_f64(o)))
+        assert np.max(np.abs(as_f64(o) - o_ref)) <= TOL["bf16"]
+
+
+def test_deterministic():
+    s, b, h, h_kv, d = 2048, 2, 8, 2, 128
+    q, k, v = share_inputs(14, s, b, h, h_kv, d, "bf16")
+    o1, l1 = gpu_attn(q, k, v, s, b, h, h_kv, d, 1, True, "bf16")
+    o2, l2 = gpu_attn(q, k, v, s, b, h, h_kv, d, 1, True, "bf16")
+    assert np.array_equal(o1, o2) and np.array_equal(l1, l2)
+
+
+def test_head_independence_chain():
+    """Emulated exchange of all P ranks, then per-rank attention, then the
+    reverse exchange, equals unsharded attention over all heads (GQA, causal)."""
+    P, s, b, h, h_kv, d = 4, 512, 2, 8, 4, 128
+    qg = synth.tensor(1501, (s, b, h, d), "bf16")
+    kg = synth.tensor(1502, (s, b, h_kv, d), "bf16")
+    vg = synth.tensor(1503, (s, b, h_kv, d), "bf16")
+    sl = s // P
+
+    def exchange(glob, heads):
+        sends = [binding.pack_seq2head(to_dev(glob.reshape(P, sl, b, heads, d)[j]), P)
+                 for j in range(P)]
+        return [torch.cat([sends[j][r] for j in range(P)], dim=0) for r in range(P)]
+
+    qs, ks, vs = exchange(qg, h), exchange(kg, h_kv), exchange(vg, h_kv)
+    outs = [binding.attn_fwd(qs[r], ks[r], vs[r], P=P, causal=True)[0] for r in range(P)]
+    back = [binding.unpack_head2seq(torch.stack([outs[r][j * sl:(j + 1) * sl]
+                                                 for r in range(P)])) for j in range(P)]
+    torch.cuda.synchronize()
+    got = np.concatenate([from_dev(x) for x in back], axis=0)
+    o_ref, _ = oracle.attn(qg, kg, vg, s, b, h, h_kv, d, 1, True)
+    assert np.max(np.abs(as_f64(got) - o_ref)) <= TOL["bf16"]

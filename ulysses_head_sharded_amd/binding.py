@@ -1,0 +1,149 @@
+"""Thin Python binding of libulysses.so (ctypes; argument marshalling only).
+
+The ``ulys_*`` functions mirror the C ABI of ``include/ulysses.h`` one to one
+(plain integers for pointers and sizes).  The tensor helpers below them only
+allocate outputs with torch, read ``data_ptr()`` and the current stream, and
+raise on a non-zero status: every step of the path runs in the HIP kernels.
+There is no fallback: if the library is missing, loading raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "libulysses.so")
+
+ULYS_F32, ULYS_BF16 = 0, 1
+ULYS_OK = 0
+ULYS_ERR_NULL, ULYS_ERR_DIM, ULYS_ERR_DIVISIBILITY = -1, -2, -3
+ULYS_ERR_UNSUPPORTED, ULYS_ERR_ALIGNMENT, ULYS_ERR_ALIAS, ULYS_ERR_HIP = -4, -5, -6, -7
+
+# every symbol include/ulysses.h declares
+EXPORTED = ("ulys_pack_seq2head", "ulys_unpack_head2seq", "ulys_attn_fwd",
+            "ulys_status_string", "ulys_abi_version")
+
+_lib = None
+
+
+class UlyssesError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        super().__init__(f"{what}: {ulys_status_string(status)} (status {status})")
+        self.status = status
+
+
+def load(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Load the HIP library; raises if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise ImportError(f"{path} is missing: build it with __graft_entry__.build() "
+                          "(hipcc --offload-arch=gfx950); there is no fallback path")
+    lib = ctypes.CDLL(path)
+    i64, i32, vp = ctypes.c_int64, ctypes.c_int32, ctypes.c_void_p
+    lay = [vp, vp, i64, i64, i64, i64, i32, i32, vp]
+    lib.ulys_pack_seq2head.argtypes = lay
+    lib.ulys_pack_seq2head.restype = ctypes.c_int
+    lib.ulys_unpack_head2seq.argtypes = lay
+    lib.ulys_unpack_head2seq.restype = ctypes.c_int
+    lib.ulys_attn_fwd.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i32, i32, i32, vp]
+    lib.ulys_attn_fwd.restype = ctypes.c_int
+    lib.ulys_status_string.argtypes = [ctypes.c_int]
+    lib.ulys_status_string.restype = ctypes.c_char_p
+    lib.ulys_abi_version.argtypes = []
+    lib.ulys_abi_version.restype = ctypes.c_int
+    _lib = lib
+    return lib
+
+
+# ------------------------------------------------------------------ raw C-ABI mirrors
+def ulys_pack_seq2head(x, y, s, b, h, d_h, P, dtype, stream=None) -> int:
+    return load().ulys_pack_seq2head(x, y, s, b, h, d_h, P, dtype, stream)
+
+
+def ulys_unpack_head2seq(y, x, s, b, h, d_h, P, dtype, stream=None) -> int:
+    return load().ulys_unpack_head2seq(y, x, s, b, h, d_h, P, dtype, stream)
+
+
+def ulys_attn_fwd(q, k, v, o, lse, s, b, h, h_kv, d_h, P, causal, dtype, stream=None) -> int:
+    return load().ulys_attn_fwd(q, k, v, o, lse, s, b, h, h_kv, d_h, P, causal, dtype, stream)
+
+
+def ulys_status_string(status: int) -> str:
+    return load().ulys_status_string(status).decode()
+
+
+def ulys_abi_version() -> int:
+    return load().ulys_abi_version()
+
+
+# ------------------------------------------------------------------ tensor helpers
+def _torch():
+    import torch
+    return torch
+
+
+def dtype_code(t) -> int:
+    torch = _torch()
+    if t.dtype == torch.float32:
+        return ULYS_F32
+    if t.dtype == torch.bfloat16:
+        return ULYS_BF16
+    raise TypeError(f"unsupported dtype {t.dtype}; use float32 or bfloat16")
+
+
+def _stream(stream):
+    if stream is not None:
+        return stream
+    return _torch().cuda.current_stream().cuda_stream
+
+
+def _check(rc: int, what: str) -> None:
+    if rc != ULYS_OK:
+        raise UlyssesError(rc, what)
+
+
+def pack_seq2head(x, P: int, out=None, stream=None):
+    """x [s/P, b, h, d] (CUDA tensor) -> send buffer [P, s/P, b, h/P, d]."""
+    sl, b, h, d = x.shape
+    if h % P:
+        raise ValueError(f"P={P} must divide h={h}")
+    if out is None:
+        out = _torch().empty((P, sl, b, h // P, d), dtype=x.dtype, device=x.device)
+    _check(ulys_pack_seq2head(x.data_ptr(), out.data_ptr(), sl * P, b, h, d, P,
+                              dtype_code(x), _stream(stream)), "ulys_pack_seq2head")
+    return out
+
+
+def unpack_head2seq(y, out=None, stream=None):
+    """y [P, s/P, b, h/P, d] (received blocks) -> [s/P, b, h, d]."""
+    P, sl, b, hp, d = y.shape
+    if out is None:
+        out = _torch().empty((sl, b, hp * P, d), dtype=y.dtype, device=y.device)
+    _check(ulys_unpack_head2seq(y.data_ptr(), out.data_ptr(), sl * P, b, hp * P, d, P,
+                                dtype_code(y), _stream(stream)), "ulys_unpack_head2seq")
+    return out
+
+
+def attn_fwd(q, k, v, P: int = 1, causal: bool = False, out=None, lse=False, stream=None):
+    """One rank's share: q [s, b, h/P, d], k/v [s, b, h_kv/P, d] -> o [s, b, h/P, d].
+
+    ``lse`` may be False (skip), True (allocate [b, h/P, s] float32) or a tensor.
+    Returns (o, lse or None)."""
+    torch = _torch()
+    s, b, hp, d = q.shape
+    hkvp = k.shape[2]
+    if out is None:
+        out = torch.empty_like(q)
+    lse_t = None
+    if lse is True:
+        lse_t = torch.empty((b, hp, s), dtype=torch.float32, device=q.device)
+    elif lse is not False and lse is not None:
+        lse_t = lse
+    rc = ulys_attn_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                       lse_t.data_ptr() if lse_t is not None else None,
+                       s, b, hp * P, hkvp * P, d, P, int(bool(causal)), dtype_code(q),
+                       _stream(stream))
+    _check(rc, "ulys_attn_fwd")
+    return out, lse_t

@@ -1,0 +1,148 @@
+// abi.cpp -- the extern "C" entry points declared in include/ulysses.h.
+//
+// Each entry validates everything on the host (sizes, divisibility, dtype,
+// alignment, aliasing) and returns before touching the HIP runtime when an
+// argument is bad; only then does it enqueue its kernel on the caller's
+// stream.  Nothing here allocates, synchronizes or keeps state.
+#include <stdint.h>
+#include <string.h>
+
+#include "internal.h"
+#include "ulysses.h"
+
+namespace {
+
+constexpr int64_t kMaxDim = int64_t(1) << 40;    // per-argument sanity bound
+constexpr int64_t kMaxBytes = int64_t(1) << 46;  // 64 TiB: any real buffer is smaller
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+bool overlaps(const void* a, int64_t na, const void* b, int64_t nb) {
+  const uintptr_t x = reinterpret_cast<uintptr_t>(a), y = reinterpret_cast<uintptr_t>(b);
+  return x < y + (uintptr_t)nb && y < x + (uintptr_t)na;
+}
+
+int elt_size(int32_t dtype) {
+  if (dtype == ULYS_F32) return 4;
+  if (dtype == ULYS_BF16) return 2;
+  return 0;
+}
+
+// Product of positive sizes with an overflow guard; -1 when too large.
+int64_t checked_product(std::initializer_list<int64_t> xs) {
+  int64_t r = 1;
+  for (int64_t x : xs) {
+    if (x <= 0 || x > kMaxDim) return -1;
+    if (r > kMaxBytes / x) return -1;
+    r *= x;
+  }
+  return r;
+}
+
+// Shared validation of the two layout entry points.
+int check_layout(const void* in, const void* out, int64_t s, int64_t b, int64_t h, int64_t d_h,
+                 int32_t P, int32_t dtype, int64_t* bytes) {
+  if (!in || !out) return ULYS_ERR_NULL;
+  if (s <= 0 || b <= 0 || h <= 0 || d_h <= 0 || P <= 0) return ULYS_ERR_DIM;
+  if (s > kMaxDim || b > kMaxDim || h > kMaxDim || d_h > kMaxDim) return ULYS_ERR_DIM;
+  if (s % P != 0 || h % P != 0) return ULYS_ERR_DIVISIBILITY;
+  const int elt = elt_size(dtype);
+  if (elt == 0) return ULYS_ERR_UNSUPPORTED;
+  const int64_t n = checked_product({s / P, b, h, d_h, (int64_t)elt});
+  if (n < 0) return ULYS_ERR_DIM;
+  if (!aligned16(in) || !aligned16(out)) return ULYS_ERR_ALIGNMENT;
+  if (overlaps(in, n, out, n)) return ULYS_ERR_ALIAS;
+  *bytes = n;
+  return ULYS_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int ulys_pack_seq2head(const void* x, void* y, int64_t s, int64_t b, int64_t h, int64_t d_h,
+                       int32_t P, int32_t dtype, void* stream) {
+  int64_t bytes = 0;
+  const int rc = check_layout(x, y, s, b, h, d_h, P, dtype, &bytes);
+  if (rc != ULYS_OK) return rc;
+  const int64_t run = (h / P) * d_h * elt_size(dtype);
+  // x is [sl*b][P] runs, y is [P][sl*b] runs
+  const hipError_t e = ulys::launch_transpose_runs(x, y, (uint64_t)((s / P) * b), (uint64_t)P,
+                                                   (uint64_t)run, (hipStream_t)stream);
+  return e == hipSuccess ? ULYS_OK : ULYS_ERR_HIP;
+}
+
+int ulys_unpack_head2seq(const void* y, void* x, int64_t s, int64_t b, int64_t h, int64_t d_h,
+                         int32_t P, int32_t dtype, void* stream) {
+  int64_t bytes = 0;
+  const int rc = check_layout(y, x, s, b, h, d_h, P, dtype, &bytes);
+  if (rc != ULYS_OK) return rc;
+  const int64_t run = (h / P) * d_h * elt_size(dtype);
+  // y is [P][sl*b] runs, x is [sl*b][P] runs
+  const hipError_t e = ulys::launch_transpose_runs(y, x, (uint64_t)P, (uint64_t)((s / P) * b),
+                                                   (uint64_t)run, (hipStream_t)stream);
+  return e == hipSuccess ? ULYS_OK : ULYS_ERR_HIP;
+}
+
+int ulys_attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int64_t s,
+                  int64_t b, int64_t h, int64_t h_kv, int64_t d_h, int32_t P, int32_t causal,
+                  int32_t dtype, void* stream) {
+  if (!q || !k || !v || !o) return ULYS_ERR_NULL;
+  if (s <= 0 || b <= 0 || h <= 0 || h_kv <= 0 || d_h <= 0 || P <= 0) return ULYS_ERR_DIM;
+  if (s > kMaxDim || b > kMaxDim || h > kMaxDim || h_kv > kMaxDim || d_h > kMaxDim)
+    return ULYS_ERR_DIM;
+  if (s % P != 0 || h % P != 0 || h_kv % P != 0 || h % h_kv != 0) return ULYS_ERR_DIVISIBILITY;
+  const int elt = elt_size(dtype);
+  if (elt == 0) return ULYS_ERR_UNSUPPORTED;
+  if (d_h != 64 && d_h != 128) return ULYS_ERR_UNSUPPORTED;
+  const int64_t hp = h / P, hkvp = h_kv / P;
+  const int64_t nq = checked_product({s, b, hp, d_h, (int64_t)elt});
+  const int64_t nkv = checked_product({s, b, hkvp, d_h, (int64_t)elt});
+  const int64_t nl = checked_product({b, hp, s, (int64_t)sizeof(float)});
+  if (nq < 0 || nkv < 0 || nl < 0) return ULYS_ERR_DIM;
+  // the kernels index tokens and work items with 32-bit integers
+  if (s > 0x7FFFFFFF || b * hp > 0x7FFFFFFF || b * hp * s > (int64_t(1) << 40))
+    return ULYS_ERR_DIM;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o)) return ULYS_ERR_ALIGNMENT;
+  if (lse && !aligned16(lse)) return ULYS_ERR_ALIGNMENT;
+  if (overlaps(o, nq, q, nq) || overlaps(o, nq, k, nkv) || overlaps(o, nq, v, nkv))
+    return ULYS_ERR_ALIAS;
+  if (lse && (overlaps(lse, nl, q, nq) || overlaps(lse, nl, k, nkv) ||
+              overlaps(lse, nl, v, nkv) || overlaps(lse, nl, o, nq)))
+    return ULYS_ERR_ALIAS;
+
+  ulys::AttnArgs a;
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.o = o;
+  a.lse = lse;
+  a.s = s;
+  a.b = b;
+  a.hp = hp;
+  a.hkvp = hkvp;
+  a.d = d_h;
+  a.causal = causal != 0;
+  const hipError_t e = (dtype == ULYS_BF16) ? ulys::launch_attn_bf16(a, (hipStream_t)stream)
+                                            : ulys::launch_attn_f32(a, (hipStream_t)stream);
+  return e == hipSuccess ? ULYS_OK : ULYS_ERR_HIP;
+}
+
+const char* ulys_status_string(int status) {
+  switch (status) {
+    case ULYS_OK: return "ok";
+    case ULYS_ERR_NULL: return "a required pointer is NULL";
+    case ULYS_ERR_DIM: return "a size is non-positive or too large";
+    case ULYS_ERR_DIVISIBILITY:
+      return "P must divide s, h and h_kv, and h_kv must divide h";
+    case ULYS_ERR_UNSUPPORTED: return "unsupported dtype or head size";
+    case ULYS_ERR_ALIGNMENT: return "a pointer is not 16-byte aligned";
+    case ULYS_ERR_ALIAS: return "an output overlaps an input or another output";
+    case ULYS_ERR_HIP: return "the HIP runtime reported a launch error";
+    default: return "unknown status";
+  }
+}
+
+int ulys_abi_version(void) { return ULYS_ABI_VERSION; }
+
+}  // extern "C"

@@ -1,0 +1,56 @@
+// internal.h -- declarations shared by the host-side ABI and the kernel files
+// of the HIP library.  Not installed; the public surface is include/ulysses.h.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace ulys {
+
+// Division of 32-bit unsigned numerators by a runtime-invariant divisor with a
+// multiply-high and a shift (Granlund & Montgomery, "Division by invariant
+// integers using multiplication", PLDI 1994, round-up variant).
+struct FastDiv {
+  uint32_t div;    // the divisor d >= 1
+  uint32_t mul;    // m = floor(2^32 * (2^l - d) / d) + 1
+  uint32_t shift;  // l = ceil(log2 d)
+};
+
+inline FastDiv make_fastdiv(uint32_t d) {
+  FastDiv f;
+  f.div = d;
+  uint32_t l = 0;
+  while ((1ull << l) < d) ++l;
+  f.shift = l;
+  f.mul = (uint32_t)(((1ull << 32) * ((1ull << l) - d)) / d + 1);
+  return f;
+}
+
+__device__ __forceinline__ uint32_t fast_div(uint32_t n, FastDiv f) {
+  uint32_t t = __umulhi(n, f.mul);
+  return (uint32_t)(((uint64_t)t + n) >> f.shift);
+}
+
+// Layout kernels: out[bb][a] = in[a][bb] over an [A][B] grid of runs of
+// run_bytes bytes each (a run is hp*d_h contiguous elements).
+hipError_t launch_transpose_runs(const void* in, void* out, uint64_t A, uint64_t B,
+                                 uint64_t run_bytes, hipStream_t stream);
+
+struct AttnArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  void* o;
+  float* lse;       // may be null
+  int64_t s;        // sequence length of the share
+  int64_t b;        // batch
+  int64_t hp;       // query heads of the share
+  int64_t hkvp;     // KV heads of the share
+  int64_t d;        // head size
+  int causal;
+};
+
+hipError_t launch_attn_bf16(const AttnArgs& a, hipStream_t stream);
+hipError_t launch_attn_f32(const AttnArgs& a, hipStream_t stream);
+
+}  // namespace ulys
