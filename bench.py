@@ -39,7 +39,23 @@ def parse_args():
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="wall-time budget of the oracle's cpu_baseline sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain device-to-device copy of known size (for scaling "
+                         "rocprofv3 FETCH_SIZE/WRITE_SIZE to bytes) and exit")
     return ap.parse_args()
+
+
+def copy_calibration():
+    """Three plain copies of a 1 GiB buffer; the copy kernel reads and writes
+    exactly 1 GiB per dispatch, the yardstick for the HBM byte counters."""
+    import torch
+    n = 1 << 30
+    src = torch.empty(n, dtype=torch.uint8, device="cuda:0").fill_(7)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes_per_dispatch": n}), flush=True)
 
 
 def source_digest(path: str) -> str:
@@ -100,6 +116,9 @@ def cpu_baseline(w, q, k, v, budget_s: float):
 
 def main():
     args = parse_args()
+    if args.copy_calibration:
+        copy_calibration()
+        return
     if args.gpus != 1:
         print(f"bench.py measures one rank's share on ONE GPU; --gpus {args.gpus} is not "
               "supported (the all-to-all across GPUs is not part of this build)",
@@ -141,7 +160,7 @@ def main():
         if rc != 0:
             raise RuntimeError(f"{what}: {binding.ulys_status_string(rc)}")
 
-    ev = {n: [] for n in ("pack0", "pack1", "attn0", "attn1", "unpack1")}
+    ev = {n: [] for n in ("pack0", "pack1", "attn1", "unpack1")}
 
     def step(record: bool):
         if record:

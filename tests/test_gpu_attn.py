@@ -45,6 +45,8 @@ for dtype, d in [("bf16", 128), ("bf16", 64), ("f32", 64), ("f32", 128)]:
         for (h, h_kv, P) in [(2, 2, 1), (8, 2, 2), (16, 2, 1), (8, 8, 4), (4, 1, 1)]:
             if dtype == "f32" and s > 321:
                 continue
+            if s % P:
+                continue  # the ABI rejects P !| s (covered by the CPU error-path tests)
             for causal in (False, True):
                 SMALL.append((dtype, d, s, b, h, h_kv, P, causal))
 

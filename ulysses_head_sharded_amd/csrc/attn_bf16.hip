@@ -232,7 +232,17 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(Params p) {
       mx = fmaxf(mx, __shfl_xor(mx, 32));
       const float m_new = fmaxf(m_run, mx);
       const float base = (m_new == -INFINITY) ? 0.f : m_new * p.c;
-      const float alpha = __builtin_amdgcn_exp2f(m_run * p.c - base);
+      // rescale the running sum and accumulator only when some row's max grew;
+      // rows whose max is unchanged keep a factor of exactly 1
+      if (__ballot(m_new > m_run) != 0) {
+        const float alpha = (m_new > m_run) ? __builtin_amdgcn_exp2f(m_run * p.c - base) : 1.f;
+        l_run *= alpha;
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
+      }
+      m_run = m_new;
       float ps = 0.f;
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
@@ -242,12 +252,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(Params p) {
           sacc[kb][r] = e;
           ps += e;
         }
-      l_run = l_run * alpha + ps;
-      m_run = m_new;
-#pragma unroll
-      for (int db = 0; db < D / 32; ++db)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
+      l_run += ps;
 
       // P^T operands: 16-key step ks uses registers 8 (ks%2) .. +7 of block ks/2
       bf16x8 pb[kBN / 16];
