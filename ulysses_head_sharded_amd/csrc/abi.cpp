@@ -103,6 +103,11 @@ int ulys_attn_fwd(const void* q, const void* k, const void* v, void* o, float* l
   // the kernels index tokens and work items with 32-bit integers
   if (s > 0x7FFFFFFF || b * hp > 0x7FFFFFFF || b * hp * s > (int64_t(1) << 40))
     return ULYS_ERR_DIM;
+  // the bf16 kernel addresses each tensor with 32-bit byte offsets (plus one
+  // tile of keys past the end, which its buffer loads read as zero)
+  if (dtype == ULYS_BF16 && (nq + 2 * 64 * b * hp * d_h * 2 >= (int64_t(1) << 31) ||
+                             nkv + 2 * 64 * b * hkvp * d_h * 2 >= (int64_t(1) << 31)))
+    return ULYS_ERR_DIM;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o)) return ULYS_ERR_ALIGNMENT;
   if (lse && !aligned16(lse)) return ULYS_ERR_ALIGNMENT;
   if (overlaps(o, nq, q, nq) || overlaps(o, nq, k, nkv) || overlaps(o, nq, v, nkv))

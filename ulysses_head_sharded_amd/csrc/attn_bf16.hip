@@ -46,19 +46,22 @@ constexpr int kWaves = 4;
 constexpr int kThreads = 64 * kWaves;
 constexpr int kBN = 64;  // keys per tile
 constexpr int kQW = 32;  // queries per wave
+// dword 3 of a raw buffer resource (no swizzle, 32-bit data format) on gfx9
+constexpr int kRsrcWord3 = 0x00020000;
 
 template <int D>
 struct Cfg {
   static constexpr int KP = D + 8;    // K row pitch in bf16 elements (odd multiple of 16 B)
-  static constexpr int VP = kBN + 8;  // V^T row pitch in bf16 elements (odd multiple of 16 B)
+  static constexpr int VP = D + 16;   // V row pitch in bf16 elements (4 rows x 32 B disjoint banks)
   static constexpr int K_ELEMS = kBN * KP;
-  static constexpr int V_ELEMS = D * VP;
-  static constexpr int BUF_ELEMS = K_ELEMS + V_ELEMS;
-  static constexpr int KCH = D / 8;                         // 16-byte chunks per row
-  static constexpr int K_LOADS = kBN * KCH / kThreads;      // 16-byte K loads per thread
-  static constexpr int V_KPT = kBN * D / (kThreads * 8);    // V keys per thread (x 8 d)
-  static_assert(K_LOADS * kThreads == kBN * KCH, "K tile split");
-  static_assert(V_KPT == 2 || V_KPT == 4, "V tile split");
+  static constexpr int V_ELEMS = kBN * VP;
+  // LDS: V0 V1 K0 K1, so every read offset fits the 16-bit immediate field
+  static constexpr int V_BASE = 0;
+  static constexpr int K_BASE = 2 * V_ELEMS;
+  static constexpr int LDS_ELEMS = 2 * (K_ELEMS + V_ELEMS);
+  static constexpr int KCH = D / 8;                          // 16-byte chunks per row
+  static constexpr int LOADS = kBN * KCH / kThreads;         // 16-byte loads per thread per tensor
+  static_assert(LOADS * kThreads == kBN * KCH, "tile split");
 };
 
 struct Params {
@@ -73,34 +76,68 @@ struct Params {
   int QB;      // queries per head per workgroup = 32 * 4 / QH
   int n_qblk;  // ceil(s / QB)
   int nsub;    // G / QH
-  int64_t q_tok, kv_tok;  // elements between consecutive tokens
-  float c;                // log2(e) / sqrt(d_h)
+  int slots;   // workgroups resident at once (CUs x workgroups per CU), 0 = no pairing
+  int q_tok_bytes, kv_tok_bytes;  // bytes between consecutive tokens
+  int q_bytes, kv_bytes;  // tensor sizes in bytes (bounds of the buffer resources)
+  float c;     // log2(e) / sqrt(d_h)
 };
 
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 x) { return __builtin_bit_cast(bf16x8, x); }
 
-// Column of key kk (0..63) inside a V^T row: inside each 16-key step the
-// 4-key chunks are stored in the order 0, 2, 1, 3, which puts the keys a lane
-// pair (l, l+32) holds in P^T next to each other.
-__device__ __forceinline__ int vt_col(int kk) {
-  const int c = (kk >> 2) & 3;
-  const int pc = ((c & 1) << 1) | (c >> 1);
-  return (kk & ~15) | (pc << 2) | (kk & 3);
+// Raw buffer resource over a whole tensor: loads past num_bytes return 0 and
+// stores past it are dropped, which handles the ragged tail without branches.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* base, int num_bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, num_bytes,
+                                           kRsrcWord3);
+}
+
+// The value of x in the partner lane (l ^ 32) combined with max / sum.
+__device__ __forceinline__ float xmax32(float x) {
+  const uint32_t u = __builtin_bit_cast(uint32_t, x);
+  const auto sw = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  return fmaxf(__builtin_bit_cast(float, (uint32_t)sw[0]),
+               __builtin_bit_cast(float, (uint32_t)sw[1]));
+}
+__device__ __forceinline__ float xsum32(float x) {
+  const uint32_t u = __builtin_bit_cast(uint32_t, x);
+  const auto sw = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  return __builtin_bit_cast(float, (uint32_t)sw[0]) + __builtin_bit_cast(float, (uint32_t)sw[1]);
+}
+
+// Transposing LDS read (ds_read_b64_tr_b16).  Within each group of 16 lanes,
+// output lane 4a+e receives element e of the 8-byte reads of source lanes a,
+// a+4, a+8, a+12.  When source lane s reads 4 elements at row r0 + s/4,
+// column c0 + 4 (s%4) of a row-major tile, output lane L therefore holds
+// rows r0 .. r0+3 of column c0 + L: four consecutive keys of one feature,
+// i.e. one half of an MFMA operand taken straight from row-major V.
+__device__ __forceinline__ u32x2 lds_read_tr(const uint16_t* p) {
+  typedef short i16x4 __attribute__((ext_vector_type(4)));
+  const i16x4 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) i16x4*)(p));
+  return __builtin_bit_cast(u32x2, r);
 }
 
 template <int D, bool CAUSAL>
 __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(Params p) {
   using C = Cfg<D>;
-  __shared__ __attribute__((aligned(16))) uint16_t lds[2 * C::BUF_ELEMS];
+  __shared__ __attribute__((aligned(16))) uint16_t lds[C::LDS_ELEMS];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int l32 = lane & 31, hh = lane >> 5;
 
-  // ---- work item: longest causal q-block first, then batch, KV head, head subgroup
+  // ---- work item.  Items are ranked longest causal q-block first (then batch,
+  // KV head, head subgroup).  The first `slots` workgroups are resident at once;
+  // the dispatcher gives workgroups p and p + slots/2 the same CU, so the second
+  // half of that first wave takes the ranks in reverse, pairing the longest item
+  // with the shortest on each CU.  Later workgroups start as slots free up and
+  // take the remaining ranks longest-first.
+  int rank = blockIdx.x;
+  if (CAUSAL && p.slots > 0 && rank < p.slots && rank >= p.slots / 2)
+    rank = p.slots + p.slots / 2 - 1 - rank;
   const int per_q = p.b * p.hkvp * p.nsub;
-  const int qi = blockIdx.x / per_q;
-  int rest = blockIdx.x - qi * per_q;
+  const int qi = rank / per_q;
+  int rest = rank - qi * per_q;
   const int qblk = CAUSAL ? (p.n_qblk - 1 - qi) : qi;
   const int sub = rest % p.nsub;
   rest /= p.nsub;
@@ -111,17 +148,24 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(Params p) {
   const int q0 = qblk * p.QB + (wave % wph) * kQW;  // first query of this wave
   const int my_q = q0 + l32;
 
-  const uint16_t* qbase = p.q + (int64_t)(be * p.hp + head) * D;
-  const uint16_t* kbase = p.k + (int64_t)(be * p.hkvp + kvg) * D;
-  const uint16_t* vbase = p.v + (int64_t)(be * p.hkvp + kvg) * D;
+  const __amdgpu_buffer_rsrc_t rq = rsrc(p.q, p.q_bytes);
+  const __amdgpu_buffer_rsrc_t rk = rsrc(p.k, p.kv_bytes);
+  const __amdgpu_buffer_rsrc_t rv = rsrc(p.v, p.kv_bytes);
+  const int q_head_off = (be * p.hp + head) * D * 2;     // bytes
+  const int kv_head_off = (be * p.hkvp + kvg) * D * 2;   // bytes
 
   // ---- Q^T fragments (B operand): lane holds query my_q, d = 16*dk + 8*hh .. +7
   bf16x8 qf[D / 16];
+  {
+    const int qoff = my_q * p.q_tok_bytes + q_head_off + hh * 16;
 #pragma unroll
-  for (int dk = 0; dk < D / 16; ++dk) {
-    u32x4 x = {0u, 0u, 0u, 0u};
-    if (my_q < p.s) x = *(const u32x4*)(qbase + (int64_t)my_q * p.q_tok + dk * 16 + hh * 8);
-    qf[dk] = as_bf16x8(x);
+    for (int dk = 0; dk < D / 16; ++dk)
+      qf[dk] = as_bf16x8(__builtin_amdgcn_raw_buffer_load_b128(rq, qoff + dk * 32, 0, 0));
+    // consume Q here so its loads are complete before the key loop: otherwise
+    // the loop inherits them as outstanding and every tile waits on the vector
+    // memory counter, i.e. on the next tile's K/V loads
+#pragma unroll
+    for (int dk = 0; dk < D / 16; ++dk) asm volatile("" ::"v"(qf[dk]));
   }
 
   const int q_hi = min(p.s, (qblk + 1) * p.QB);
@@ -129,57 +173,36 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(Params p) {
   const int wave_last_q = min(q0 + kQW, p.s) - 1;
   const int wave_tiles = (q0 >= p.s) ? 0 : (CAUSAL ? wave_last_q / kBN + 1 : n_tiles);
 
-  // ---- global -> register staging of one K/V tile
-  u32x4 kreg[C::K_LOADS];
-  u32x4 vreg[C::V_KPT];
-  const int v_dc = tid % C::KCH;           // d chunk of this thread's V block
-  const int v_kg = tid / C::KCH;           // key group of this thread's V block
+  // ---- global -> register staging of one K/V tile (rows past s read as 0).
+  // Thread tid moves 16-byte chunk ch = tid + i*256 of each tile: row ch / KCH,
+  // chunk ch % KCH, so 16 consecutive lanes cover one contiguous key row.
+  u32x4 kreg[C::LOADS];
+  u32x4 vreg[C::LOADS];
   auto load_tile = [&](int t) {
     const int k0 = t * kBN;
 #pragma unroll
-    for (int i = 0; i < C::K_LOADS; ++i) {
+    for (int i = 0; i < C::LOADS; ++i) {
       const int ch = tid + i * kThreads;
       const int row = ch / C::KCH, col = ch % C::KCH;
-      const int key = k0 + row;
-      u32x4 x = {0u, 0u, 0u, 0u};
-      if (key < p.s) x = *(const u32x4*)(kbase + (int64_t)key * p.kv_tok + col * 8);
-      kreg[i] = x;
-    }
-#pragma unroll
-    for (int j = 0; j < C::V_KPT; ++j) {
-      const int key = k0 + v_kg * C::V_KPT + j;
-      u32x4 x = {0u, 0u, 0u, 0u};
-      if (key < p.s) x = *(const u32x4*)(vbase + (int64_t)key * p.kv_tok + v_dc * 8);
-      vreg[j] = x;
+      const int off = (k0 + row) * p.kv_tok_bytes + kv_head_off + col * 16;
+      kreg[i] = __builtin_amdgcn_raw_buffer_load_b128(rk, off, 0, 0);
+      vreg[i] = __builtin_amdgcn_raw_buffer_load_b128(rv, off, 0, 0);
     }
   };
   auto store_tile = [&](int buf) {
-    uint16_t* kl = lds + buf * C::BUF_ELEMS;
-    uint16_t* vl = kl + C::K_ELEMS;
+    uint16_t* kl = lds + C::K_BASE + buf * C::K_ELEMS;
+    uint16_t* vl = lds + C::V_BASE + buf * C::V_ELEMS;
 #pragma unroll
-    for (int i = 0; i < C::K_LOADS; ++i) {
+    for (int i = 0; i < C::LOADS; ++i) {
       const int ch = tid + i * kThreads;
       const int row = ch / C::KCH, col = ch % C::KCH;
       *(u32x4*)(kl + row * C::KP + col * 8) = kreg[i];
-    }
-    // transpose the V_KPT x 8 block in registers: row d gets V_KPT consecutive keys
-    const int col = vt_col(v_kg * C::V_KPT);
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      uint32_t w[C::V_KPT / 2];
-#pragma unroll
-      for (int jj = 0; jj < C::V_KPT / 2; ++jj) {
-        const uint32_t a = vreg[2 * jj][e >> 1], bq = vreg[2 * jj + 1][e >> 1];
-        w[jj] = (e & 1) ? ((a >> 16) | (bq & 0xFFFF0000u)) : ((a & 0xFFFFu) | (bq << 16));
-      }
-      uint16_t* dst = vl + (v_dc * 8 + e) * C::VP + col;
-      if constexpr (C::V_KPT == 4) {
-        *(u32x2*)dst = u32x2{w[0], w[1]};
-      } else {
-        *(uint32_t*)dst = w[0];
-      }
+      *(u32x4*)(vl + row * C::VP + col * 8) = vreg[i];
     }
   };
+  // lane part of the transposing V reads: row 4*hh + (l%16)/4 of a 16-key step
+  // (the keys this lane's P^T registers hold), feature 16*((l/16)%2) + 4*(l%4)
+  const int v_lane = (4 * hh + ((lane & 15) >> 2)) * C::VP + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
 
   f32x16 oacc[D / 32];
 #pragma unroll
@@ -198,8 +221,8 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(Params p) {
     if (t + 1 < n_tiles) load_tile(t + 1);
 
     if (t < wave_tiles) {
-      const uint16_t* kl = lds + cur * C::BUF_ELEMS;
-      const uint16_t* vl = kl + C::K_ELEMS;
+      const uint16_t* kl = lds + C::K_BASE + cur * C::K_ELEMS;
+      const uint16_t* vl = lds + C::V_BASE + cur * C::V_ELEMS + v_lane;
       const int k0 = t * kBN;
 
       // S^T block kb: keys k0 + 32 kb + (8 (r/4) + 4 hh + r%4), query my_q
@@ -216,20 +239,21 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(Params p) {
       }
 
       const bool need_mask = (k0 + kBN > p.s) || (CAUSAL && k0 + kBN - 1 > q0);
+      if (need_mask) {
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int key = k0 + kb * 32 + 8 * (r >> 2) + 4 * hh + (r & 3);
+            if (key >= p.s || (CAUSAL && key > my_q)) sacc[kb][r] = -INFINITY;
+          }
+      }
       float mx = -INFINITY;
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          float x = sacc[kb][r];
-          if (need_mask) {
-            const int key = k0 + kb * 32 + 8 * (r >> 2) + 4 * hh + (r & 3);
-            if (key >= p.s || (CAUSAL && key > my_q)) x = -INFINITY;
-          }
-          sacc[kb][r] = x;
-          mx = fmaxf(mx, x);
-        }
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
+        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[kb][r]);
+      mx = xmax32(mx);
       const float m_new = fmaxf(m_run, mx);
       const float base = (m_new == -INFINITY) ? 0.f : m_new * p.c;
       // rescale the running sum and accumulator only when some row's max grew;
@@ -261,11 +285,15 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(Params p) {
 #pragma unroll
         for (int e = 0; e < 8; ++e) pb[ks][e] = (__bf16)sacc[ks >> 1][(ks & 1) * 8 + e];
 
+      // O^T += V^T P^T.  Key step ks: this lane's P^T registers hold keys
+      // 16 ks + 8 j + 4 hh + (0..3) in slots 4 j .. 4 j + 3 (j = 0, 1)
 #pragma unroll
       for (int db = 0; db < D / 32; ++db)
 #pragma unroll
         for (int ks = 0; ks < kBN / 16; ++ks) {
-          const bf16x8 a = *(const bf16x8*)(vl + (db * 32 + l32) * C::VP + ks * 16 + hh * 8);
+          const u32x2 lo = lds_read_tr(vl + (ks * 16) * C::VP + db * 32);
+          const u32x2 hi = lds_read_tr(vl + (ks * 16 + 8) * C::VP + db * 32);
+          const bf16x8 a = as_bf16x8(u32x4{lo[0], lo[1], hi[0], hi[1]});
           oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[ks], oacc[db], 0, 0, 0);
         }
     }
@@ -274,29 +302,30 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(Params p) {
     __syncthreads();
   }
 
-  // ---- epilogue: O = A / l, rounded once to bf16; lse in natural log
-  const float l_tot = l_run + __shfl_xor(l_run, 32);
-  if (my_q < p.s) {
-    const float inv = 1.f / l_tot;
-    uint16_t* obase = p.o + (int64_t)my_q * p.q_tok + (int64_t)(be * p.hp + head) * D;
+  // ---- epilogue: O = A / l, rounded once to bf16; lse in natural log.  Rows
+  // past s fall outside the buffer resource and are dropped by the stores.
+  const float l_tot = xsum32(l_run);
+  const float inv = 1.f / l_tot;
+  const __amdgpu_buffer_rsrc_t ro = rsrc(p.o, p.q_bytes);
+  const int ooff = my_q * p.q_tok_bytes + q_head_off + hh * 8;
 #pragma unroll
-    for (int db = 0; db < D / 32; ++db)
+  for (int db = 0; db < D / 32; ++db)
 #pragma unroll
-      for (int g4 = 0; g4 < 4; ++g4) {
-        const __bf16 x0 = (__bf16)(oacc[db][4 * g4 + 0] * inv);
-        const __bf16 x1 = (__bf16)(oacc[db][4 * g4 + 1] * inv);
-        const __bf16 x2 = (__bf16)(oacc[db][4 * g4 + 2] * inv);
-        const __bf16 x3 = (__bf16)(oacc[db][4 * g4 + 3] * inv);
-        const uint32_t w0 = (uint32_t)__builtin_bit_cast(uint16_t, x0) |
-                            ((uint32_t)__builtin_bit_cast(uint16_t, x1) << 16);
-        const uint32_t w1 = (uint32_t)__builtin_bit_cast(uint16_t, x2) |
-                            ((uint32_t)__builtin_bit_cast(uint16_t, x3) << 16);
-        *(u32x2*)(obase + db * 32 + 8 * g4 + 4 * hh) = u32x2{w0, w1};
-      }
-    if (p.lse && hh == 0)
-      p.lse[(int64_t)(be * p.hp + head) * p.s + my_q] =
-          (m_run * p.c + __builtin_amdgcn_logf(l_tot)) * 0.69314718055994531f;
-  }
+    for (int g4 = 0; g4 < 4; ++g4) {
+      const __bf16 x0 = (__bf16)(oacc[db][4 * g4 + 0] * inv);
+      const __bf16 x1 = (__bf16)(oacc[db][4 * g4 + 1] * inv);
+      const __bf16 x2 = (__bf16)(oacc[db][4 * g4 + 2] * inv);
+      const __bf16 x3 = (__bf16)(oacc[db][4 * g4 + 3] * inv);
+      const uint32_t w0 = (uint32_t)__builtin_bit_cast(uint16_t, x0) |
+                          ((uint32_t)__builtin_bit_cast(uint16_t, x1) << 16);
+      const uint32_t w1 = (uint32_t)__builtin_bit_cast(uint16_t, x2) |
+                          ((uint32_t)__builtin_bit_cast(uint16_t, x3) << 16);
+      __builtin_amdgcn_raw_buffer_store_b64(u32x2{w0, w1}, ro, ooff + (db * 32 + 8 * g4) * 2, 0,
+                                            0);
+    }
+  if (p.lse && hh == 0 && my_q < p.s)
+    p.lse[(int64_t)(be * p.hp + head) * p.s + my_q] =
+        (m_run * p.c + __builtin_amdgcn_logf(l_tot)) * 0.69314718055994531f;
 }
 
 template <int D>
@@ -316,12 +345,23 @@ hipError_t launch_d(const AttnArgs& a, hipStream_t stream) {
   p.QB = kQW * (kWaves / p.QH);
   p.n_qblk = (p.s + p.QB - 1) / p.QB;
   p.nsub = p.G / p.QH;
-  p.q_tok = a.b * a.hp * D;
-  p.kv_tok = a.b * a.hkvp * D;
+  p.q_tok_bytes = (int)(a.b * a.hp * D * 2);
+  p.kv_tok_bytes = (int)(a.b * a.hkvp * D * 2);
+  p.q_bytes = (int)(a.s * a.b * a.hp * D * 2);
+  p.kv_bytes = (int)(a.s * a.b * a.hkvp * D * 2);
   p.c = (float)(1.4426950408889634 / sqrt((double)D));
   const int64_t items = (int64_t)p.n_qblk * p.b * p.hkvp * p.nsub;
   if (items <= 0) return hipSuccess;
   if (items > 0x7FFFFFFF) return hipErrorInvalidValue;
+  // pairing applies when the whole first resident wave is present
+  int dev = 0, cus = 0;
+  p.slots = 0;
+  if (hipGetDevice(&dev) == hipSuccess &&
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess) {
+    const int per_cu = (D == 128) ? 2 : 3;  // LDS- and VGPR-limited residency of this kernel
+    const int64_t slots = (int64_t)cus * per_cu;
+    if (items >= slots && (slots % 2) == 0) p.slots = (int)slots;
+  }
   if (a.causal)
     hipLaunchKernelGGL((attn_bf16_kernel<D, true>), dim3((unsigned)items), dim3(kThreads), 0,
                        stream, p);
