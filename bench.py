@@ -52,7 +52,10 @@ def copy_calibration():
     n = 1 << 30
     src = torch.empty(n, dtype=torch.uint8, device="cuda:0").fill_(7)
     dst = torch.empty_like(src)
+    evict = torch.empty_like(src)
     for _ in range(3):
+        evict.fill_(1)  # 1 GiB of other writes push src out of L2 and the 256 MiB MALL
+        torch.cuda.synchronize()
         dst.copy_(src)
     torch.cuda.synchronize()
     print(json.dumps({"copy_calibration_bytes_per_dispatch": n}), flush=True)

@@ -19,17 +19,19 @@
 //    sum are lane-local; only one exchange with the partner lane (l ^ 32) is
 //    needed per tile for the max, and one at the end for the sum.
 //  * The probabilities stay in registers and become the B operand of
-//    O^T += V^T P^T with the same instruction; V^T (the A operand) is read
-//    from LDS, where V is stored transposed ([d][key]) with the keys of each
-//    16-key step permuted so every lane reads 16 contiguous bytes that match
-//    the keys its P^T registers hold.
-//  * K and V^T tiles of 64 keys are double-buffered in LDS; the next tile's
-//    global loads are in flight during the current tile's MFMAs.  Rows are
-//    padded so the 16-byte LDS reads of 8 consecutive rows hit distinct banks.
-//  * exp2 with log2(e)/sqrt(d_h) folded into one FMA per score; causal tiles
-//    above a wave's diagonal are skipped, the diagonal tile is masked.
-//  * Work items are ordered longest-first (causal) so short items fill the
-//    tail of the grid.
+//    O^T += V^T P^T with the same instruction.  V stays row-major in LDS; its
+//    A operand comes from ds_read_b64_tr_b16, which transposes 4x4 blocks of
+//    16-bit values across lanes as it reads.
+//  * K and V tiles of 64 keys are double-buffered in LDS (two workgroups per
+//    CU); the next tile's global loads are in flight during the current
+//    tile's MFMAs.  Loads go through raw buffer resources, so rows past the
+//    sequence read as zero and the ragged tail needs no branch.  Rows are
+//    padded so every LDS access pattern used hits distinct banks.
+//  * exp2 with log2(e)/sqrt(d_h) folded into one FMA per score; the online
+//    rescale runs only when some row's max grew; causal tiles above a wave's
+//    diagonal are skipped and only diagonal / tail tiles are masked.
+//  * Work items are ordered longest-first (causal); in the first resident
+//    wave the longest and shortest items share a CU.
 #include <math.h>
 
 #include "internal.h"
