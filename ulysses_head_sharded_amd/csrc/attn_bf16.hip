@@ -23,10 +23,12 @@
 //    A operand comes from ds_read_b64_tr_b16, which transposes 4x4 blocks of
 //    16-bit values across lanes as it reads.
 //  * K and V tiles of 64 keys are double-buffered in LDS (two workgroups per
-//    CU); the next tile's global loads are in flight during the current
+//    CU) and filled by direct global->LDS buffer loads (no staging
+//    registers); the next tile's loads are in flight during the current
 //    tile's MFMAs.  Loads go through raw buffer resources, so rows past the
-//    sequence read as zero and the ragged tail needs no branch.  Rows are
-//    padded so every LDS access pattern used hits distinct banks.
+//    sequence read as zero and the ragged tail needs no branch.  Tile rows
+//    are unpadded with XOR-swizzled 16-byte chunks chosen so the MFMA K reads
+//    and the transposing V reads both hit distinct banks.
 //  * exp2 with log2(e)/sqrt(d_h) folded into one FMA per score; the online
 //    rescale runs only when some row's max grew; causal tiles above a wave's
 //    diagonal are skipped and only diagonal / tail tiles are masked.
@@ -53,17 +55,17 @@ constexpr int kRsrcWord3 = 0x00020000;
 
 template <int D>
 struct Cfg {
-  static constexpr int KP = D + 8;    // K row pitch in bf16 elements (odd multiple of 16 B)
-  static constexpr int VP = D + 16;   // V row pitch in bf16 elements (4 rows x 32 B disjoint banks)
-  static constexpr int K_ELEMS = kBN * KP;
-  static constexpr int V_ELEMS = kBN * VP;
+  static constexpr int ROW_BYTES = D * 2;             // one key row of K or V
+  static constexpr int CHUNKS = ROW_BYTES / 16;       // 16-byte chunks per row
+  static constexpr int TILE_BYTES = kBN * ROW_BYTES;  // one K or V tile, unpadded
   // LDS: V0 V1 K0 K1, so every read offset fits the 16-bit immediate field
   static constexpr int V_BASE = 0;
-  static constexpr int K_BASE = 2 * V_ELEMS;
-  static constexpr int LDS_ELEMS = 2 * (K_ELEMS + V_ELEMS);
-  static constexpr int KCH = D / 8;                          // 16-byte chunks per row
-  static constexpr int LOADS = kBN * KCH / kThreads;         // 16-byte loads per thread per tensor
-  static_assert(LOADS * kThreads == kBN * KCH, "tile split");
+  static constexpr int K_BASE = 2 * TILE_BYTES;
+  static constexpr int LDS_BYTES = 4 * TILE_BYTES;
+  // direct global->LDS loads: one wave instruction fills 1 KiB = ROWS_PER_LOAD rows
+  static constexpr int ROWS_PER_LOAD = 1024 / ROW_BYTES;
+  static constexpr int LOADS = kBN / (ROWS_PER_LOAD * kWaves);  // per wave per tensor
+  static_assert(LOADS * ROWS_PER_LOAD * kWaves == kBN, "tile split");
 };
 
 struct Params {
@@ -119,10 +121,26 @@ __device__ __forceinline__ u32x2 lds_read_tr(const uint16_t* p) {
   return __builtin_bit_cast(u32x2, r);
 }
 
+// One direct global->LDS load: every lane's 16 bytes at byte offset voff of
+// the resource land at lds_dst + 16 * lane (out-of-range lanes write zeros).
+__device__ __forceinline__ void load_lds16(__amdgpu_buffer_rsrc_t r, uint8_t* lds_dst, int voff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds_dst,
+                                           16, voff, 0, 0, 0);
+}
+
+// LDS tiles are unpadded, with the 16-byte chunks of row r XOR-swizzled:
+//  * K: chunk c is stored at c ^ (r & 7).  The QK MFMA reads 8 consecutive rows
+//    at one logical chunk, which then land in 8 different bank groups.
+//  * V: chunk c is stored at c ^ 2 (r & 3).  A transposing read takes 4
+//    consecutive rows x 32 bytes per 16 lanes, which then land in 4 different
+//    32-byte bank groups.
+__device__ __forceinline__ int k_swz(int r) { return r & 7; }
+__device__ __forceinline__ int v_swz(int r) { return 2 * (r & 3); }
+
 template <int D, bool CAUSAL>
 __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(Params p) {
   using C = Cfg<D>;
-  __shared__ __attribute__((aligned(16))) uint16_t lds[C::LDS_ELEMS];
+  __shared__ __attribute__((aligned(16))) uint8_t lds[C::LDS_BYTES];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
@@ -175,37 +193,18 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(Params p) {
   const int wave_last_q = min(q0 + kQW, p.s) - 1;
   const int wave_tiles = (q0 >= p.s) ? 0 : (CAUSAL ? wave_last_q / kBN + 1 : n_tiles);
 
-  // ---- global -> register staging of one K/V tile (rows past s read as 0).
-  // Thread tid moves 16-byte chunk ch = tid + i*256 of each tile: row ch / KCH,
-  // chunk ch % KCH, so 16 consecutive lanes cover one contiguous key row.
-  u32x4 kreg[C::LOADS];
-  u32x4 vreg[C::LOADS];
-  auto load_tile = [&](int t) {
-    const int k0 = t * kBN;
+  // ---- global -> LDS loads of one K/V tile (rows past s read as 0).  Wave w,
+  // load i fills LDS rows R0 = (w*LOADS + i)*ROWS_PER_LOAD .. +ROWS_PER_LOAD-1;
+  // lane j lands at byte 16 j of that KiB: row R0 + j / CHUNKS, stored chunk
+  // j % CHUNKS, so it fetches the logical chunk that the swizzle puts there.
+  int k_src[C::LOADS], v_src[C::LOADS];  // per-lane global byte offsets at key 0
 #pragma unroll
-    for (int i = 0; i < C::LOADS; ++i) {
-      const int ch = tid + i * kThreads;
-      const int row = ch / C::KCH, col = ch % C::KCH;
-      const int off = (k0 + row) * p.kv_tok_bytes + kv_head_off + col * 16;
-      kreg[i] = __builtin_amdgcn_raw_buffer_load_b128(rk, off, 0, 0);
-      vreg[i] = __builtin_amdgcn_raw_buffer_load_b128(rv, off, 0, 0);
-    }
-  };
-  auto store_tile = [&](int buf) {
-    uint16_t* kl = lds + C::K_BASE + buf * C::K_ELEMS;
-    uint16_t* vl = lds + C::V_BASE + buf * C::V_ELEMS;
-#pragma unroll
-    for (int i = 0; i < C::LOADS; ++i) {
-      const int ch = tid + i * kThreads;
-      const int row = ch / C::KCH, col = ch % C::KCH;
-      *(u32x4*)(kl + row * C::KP + col * 8) = kreg[i];
-      *(u32x4*)(vl + row * C::VP + col * 8) = vreg[i];
-    }
-  };
-  // lane part of the transposing V reads: row 4*hh + (l%16)/4 of a 16-key step
-  // (the keys this lane's P^T registers hold), feature 16*((l/16)%2) + 4*(l%4)
-  const int v_lane = (4 * hh + ((lane & 15) >> 2)) * C::VP + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
-
+  for (int i = 0; i < C::LOADS; ++i) {
+    const int row = (wave * C::LOADS + i) * C::ROWS_PER_LOAD + lane / C::CHUNKS;
+    const int pc = lane % C::CHUNKS;
+    k_src[i] = row * p.kv_tok_bytes + kv_head_off + ((pc ^ k_swz(row)) << 4);
+    v_src[i] = row * p.kv_tok_bytes + kv_head_off + ((pc ^ v_swz(row)) << 4);
+  }
   f32x16 oacc[D / 32];
 #pragma unroll
   for (int db = 0; db < D / 32; ++db)
@@ -214,31 +213,68 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(Params p) {
   float m_run = -INFINITY;  // running max of raw scores (q.k)
   float l_run = 0.f;        // this lane's share of the running sum
 
-  load_tile(0);
-  store_tile(0);
+  auto load_tile = [&](int t, int buf) {
+    const int koff = t * kBN * p.kv_tok_bytes;
+#pragma unroll
+    for (int i = 0; i < C::LOADS; ++i) {
+      const int dst = (wave * C::LOADS + i) * 1024;
+      load_lds16(rk, lds + C::K_BASE + buf * C::TILE_BYTES + dst, k_src[i] + koff);
+      load_lds16(rv, lds + C::V_BASE + buf * C::TILE_BYTES + dst, v_src[i] + koff);
+    }
+  };
+  // lane parts of the LDS read addresses (bytes).  K: row kb*32 + l32, chunk
+  // (2 dk + hh) ^ (l32 & 7); the bit of the chunk above 7 passes the swizzle.
+  int k_rd[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) k_rd[j] = l32 * C::ROW_BYTES + (((2 * j + hh) ^ (l32 & 7)) << 4);
+  // V (transposing reads): row 4 hh + (l%16)/4 of a 16-key step (the keys this
+  // lane's P^T registers hold), byte column 64 db + 32 ((l/16)%2) + 8 (l%4)
+  const int vr = 4 * hh + ((lane & 15) >> 2);
+  int v_rd[2];
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int c = 4 * j + 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1);
+    v_rd[j] = vr * C::ROW_BYTES + ((c ^ v_swz(vr)) << 4) + 8 * (lane & 1);
+  }
+
+  load_tile(0, 0);
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
 
   for (int t = 0; t < n_tiles; ++t) {
     const int cur = t & 1;
-    if (t + 1 < n_tiles) load_tile(t + 1);
+    if (t + 1 < n_tiles) load_tile(t + 1, cur ^ 1);
 
     if (t < wave_tiles) {
-      const uint16_t* kl = lds + C::K_BASE + cur * C::K_ELEMS;
-      const uint16_t* vl = lds + C::V_BASE + cur * C::V_ELEMS + v_lane;
+      const uint8_t* kl = lds + C::K_BASE + cur * C::TILE_BYTES;
+      const uint8_t* vl = lds + C::V_BASE + cur * C::TILE_BYTES;
       const int k0 = t * kBN;
 
-      // S^T block kb: keys k0 + 32 kb + (8 (r/4) + 4 hh + r%4), query my_q
+      // S^T block kb: keys k0 + 32 kb + (8 (r/4) + 4 hh + r%4), query my_q.
+      // The two blocks' MFMA chains are interleaved.
       f32x16 sacc[2];
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
+      for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) sacc[kb][r] = 0.f;
 #pragma unroll
-        for (int dk = 0; dk < D / 16; ++dk) {
-          const bf16x8 a = *(const bf16x8*)(kl + (kb * 32 + l32) * C::KP + dk * 16 + hh * 8);
+      for (int dk = 0; dk < D / 16; ++dk)
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+          const bf16x8 a = *(const bf16x8*)(kl + kb * 32 * C::ROW_BYTES + (dk >> 2) * 128 +
+                                            k_rd[dk & 3]);
           sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[dk], sacc[kb], 0, 0, 0);
         }
+      // keep four K operand reads in flight ahead of the MFMAs that use them:
+      // four LDS reads, then alternate one MFMA / one LDS read, then the last
+      // four MFMAs (measured best of 4, 8 and 16 reads ahead)
+      __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+      for (int i = 0; i < 2 * D / 16 - 4; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
       }
+      __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
 
       const bool need_mask = (k0 + kBN > p.s) || (CAUSAL && k0 + kBN - 1 > q0);
       if (need_mask) {
@@ -288,19 +324,22 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(Params p) {
         for (int e = 0; e < 8; ++e) pb[ks][e] = (__bf16)sacc[ks >> 1][(ks & 1) * 8 + e];
 
       // O^T += V^T P^T.  Key step ks: this lane's P^T registers hold keys
-      // 16 ks + 8 j + 4 hh + (0..3) in slots 4 j .. 4 j + 3 (j = 0, 1)
+      // 16 ks + 8 j + 4 hh + (0..3) in slots 4 j .. 4 j + 3 (j = 0, 1).  The
+      // feature blocks' MFMA chains are interleaved.
 #pragma unroll
-      for (int db = 0; db < D / 32; ++db)
+      for (int ks = 0; ks < kBN / 16; ++ks)
 #pragma unroll
-        for (int ks = 0; ks < kBN / 16; ++ks) {
-          const u32x2 lo = lds_read_tr(vl + (ks * 16) * C::VP + db * 32);
-          const u32x2 hi = lds_read_tr(vl + (ks * 16 + 8) * C::VP + db * 32);
+        for (int db = 0; db < D / 32; ++db) {
+          const uint8_t* vb = vl + (ks * 16) * C::ROW_BYTES + (db >> 1) * 128 + v_rd[db & 1];
+          const u32x2 lo = lds_read_tr(reinterpret_cast<const uint16_t*>(vb));
+          const u32x2 hi = lds_read_tr(reinterpret_cast<const uint16_t*>(vb + 8 * C::ROW_BYTES));
           const bf16x8 a = as_bf16x8(u32x4{lo[0], lo[1], hi[0], hi[1]});
           oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[ks], oacc[db], 0, 0, 0);
         }
     }
 
-    if (t + 1 < n_tiles) store_tile(cur ^ 1);
+    // the next tile's direct loads must have landed before anyone reads it
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
   }
 
