@@ -158,6 +158,12 @@ def main():
     code = binding.ULYS_BF16 if w.dtype == "bf16" else binding.ULYS_F32
     stream = torch.cuda.current_stream()
     sh = stream.cuda_stream
+    # workspace for the attention's causal load balancing, allocated once
+    ws_bytes = binding.ulys_attn_fwd_workspace_size(w.s, w.b, w.h, w.h_kv, w.d, w.P,
+                                                    int(w.causal), code)
+    if ws_bytes < 0:
+        raise RuntimeError(f"workspace size: {binding.ulys_status_string(int(ws_bytes))}")
+    ws = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=dev)
 
     def call(rc, what):
         if rc != 0:
@@ -178,9 +184,9 @@ def main():
         if record:
             e[1].record(stream)
         # the send buffers stand in for the receive buffers: [P, s/P, b, hp, d] == [s, b, hp, d]
-        call(binding.ulys_attn_fwd(yq.data_ptr(), yk.data_ptr(), yv.data_ptr(), o.data_ptr(),
-                                   None, w.s, w.b, w.h, w.h_kv, w.d, w.P, int(w.causal), code,
-                                   sh), "attn")
+        call(binding.ulys_attn_fwd_ws(yq.data_ptr(), yk.data_ptr(), yv.data_ptr(), o.data_ptr(),
+                                      None, w.s, w.b, w.h, w.h_kv, w.d, w.P, int(w.causal), code,
+                                      ws.data_ptr(), ws_bytes, sh), "attn")
         if record:
             e[2].record(stream)
         call(binding.ulys_unpack_head2seq(o.data_ptr(), xo.data_ptr(), w.s, w.b, w.h, w.d, w.P,
@@ -233,7 +239,8 @@ def main():
         "config": {"workload": w.name, "P": w.P, "s": w.s, "b": w.b, "h": w.h, "h_kv": w.h_kv,
                    "d_h": w.d, "causal": w.causal, "share": f"[{w.s},{w.b},{hp},{w.d}]"},
         "attn": {"ms": round(attn_ms, 4), "tflops": round(attn_tflops, 2),
-                 "frac_peak": round(attn_tflops / peak, 4), "flops": flops},
+                 "frac_peak": round(attn_tflops / peak, 4), "flops": flops,
+                 "workspace_bytes": int(ws_bytes)},
         "layout": {"pack_qkv_us": round(pack_ms * 1e3, 2), "unpack_o_us": round(unpack_ms * 1e3, 2),
                    "pack_gbps": round(pack_gbps, 1), "unpack_gbps": round(unpack_gbps, 1),
                    "gbps": round(layout_gbps, 1),

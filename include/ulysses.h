@@ -110,13 +110,47 @@ int ulys_attn_fwd(const void* q, const void* k, const void* v, void* o, float* l
                   int64_t s, int64_t b, int64_t h, int64_t h_kv, int64_t d_h, int32_t P,
                   int32_t causal, int32_t dtype, void* stream);
 
+/*
+ * ulys_attn_fwd with a caller-owned workspace, used to balance causal work.
+ * When a causal share has too few 128-query blocks to fill the GPU's resident
+ * workgroups twice (e.g. s = 32768 with 2 heads), one block's keys would set
+ * the run time; with a workspace of ulys_attn_fwd_workspace_size() bytes the
+ * keys of every block are split into two halves computed by separate
+ * workgroups, each leaving its partial (m, l, O) state in the workspace, and a
+ * second kernel merges the halves with the online-softmax rescaling
+ * ([SPCP] Ring section: partial results over disjoint key ranges combine by
+ * rescaling with the running max).  The result equals ulys_attn_fwd's up to
+ * fp32 rounding order.
+ *
+ *   workspace       : device pointer, 16-byte aligned, or NULL (then this call
+ *                     is ulys_attn_fwd); must not overlap q, k, v, o or lse.
+ *                     Contents on entry are ignored; on return undefined.
+ *   workspace_bytes : its size; a smaller workspace than required disables the
+ *                     split (still correct).
+ * Errors: as ulys_attn_fwd, plus ULYS_ERR_DIM for workspace_bytes < 0,
+ * ULYS_ERR_ALIGNMENT / ULYS_ERR_ALIAS for the workspace.  Calls that share one
+ * workspace must be ordered (same stream).
+ */
+int ulys_attn_fwd_ws(const void* q, const void* k, const void* v, void* o, float* lse,
+                     int64_t s, int64_t b, int64_t h, int64_t h_kv, int64_t d_h, int32_t P,
+                     int32_t causal, int32_t dtype, void* workspace, int64_t workspace_bytes,
+                     void* stream);
+
+/*
+ * Workspace bytes ulys_attn_fwd_ws uses for these arguments on the current
+ * device (0 when it would not split).  Negative ULYS_ERR_* for arguments
+ * ulys_attn_fwd would reject on size, divisibility or dtype grounds.
+ */
+int64_t ulys_attn_fwd_workspace_size(int64_t s, int64_t b, int64_t h, int64_t h_kv, int64_t d_h,
+                                     int32_t P, int32_t causal, int32_t dtype);
+
 /* Static, human-readable text for a status code (never NULL). */
 const char* ulys_status_string(int status);
 
 /* ABI version of this header: (major << 16) | minor. */
 int ulys_abi_version(void);
 
-#define ULYS_ABI_VERSION ((1 << 16) | 0)
+#define ULYS_ABI_VERSION ((1 << 16) | 1)
 
 #ifdef __cplusplus
 }

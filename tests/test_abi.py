@@ -36,7 +36,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_version(lib):
-    assert B.ulys_abi_version() == (1 << 16)
+    assert B.ulys_abi_version() == (1 << 16) | 1
 
 
 def test_status_strings(lib):
@@ -109,3 +109,32 @@ def test_product_path_does_not_reach_the_oracle():
                 text = open(os.path.join(dirpath, f), encoding="utf-8").read()
                 assert "import oracle" not in text and "ulys_oracle" not in text, f
                 assert "from oracle" not in text, f
+
+
+W = 0x7F0000000000 + 5 * (1 << 32)
+
+
+@pytest.mark.parametrize("ws,nbytes,expect", [
+    (W + 8, 1 << 20, B.ULYS_ERR_ALIGNMENT),
+    (W, -1, B.ULYS_ERR_DIM),
+    (Q + 4096, 1 << 20, B.ULYS_ERR_ALIAS),      # overlaps q
+    (O - 64, 1 << 20, B.ULYS_ERR_ALIAS),        # overlaps o
+    (L, 64, B.ULYS_ERR_ALIAS),                  # overlaps lse
+])
+def test_attn_ws_rejects(lib, ws, nbytes, expect):
+    args = (Q, K, V, O, L, 64, 1, 8, 8, 128, 4, 1, B.ULYS_BF16, ws, nbytes)
+    assert B.ulys_attn_fwd_ws(*args) == expect
+
+
+@pytest.mark.parametrize("args,expect", [
+    ((0, 1, 8, 8, 128, 4, 1, B.ULYS_BF16), B.ULYS_ERR_DIM),
+    ((66, 1, 8, 8, 128, 4, 1, B.ULYS_BF16), B.ULYS_ERR_DIVISIBILITY),
+    ((64, 1, 8, 8, 96, 4, 1, B.ULYS_BF16), B.ULYS_ERR_UNSUPPORTED),
+    ((64, 1, 8, 8, 128, 4, 1, 9), B.ULYS_ERR_UNSUPPORTED),
+])
+def test_workspace_size_rejects(lib, args, expect):
+    assert B.ulys_attn_fwd_workspace_size(*args) == expect
+
+
+def test_workspace_size_fp32_is_zero(lib):
+    assert B.ulys_attn_fwd_workspace_size(16, 1, 8, 8, 64, 4, 0, B.ULYS_F32) == 0

@@ -19,21 +19,36 @@ LSE_TOL = {"bf16": 1e-3, "f32": 1e-5}
 TORCH_DT = {"bf16": torch.bfloat16, "f32": torch.float32}
 
 
-def gpu_attn(q, k, v, s, b, h, h_kv, d, P, causal, dtype, want_lse=True):
+def gpu_attn(q, k, v, s, b, h, h_kv, d, P, causal, dtype, want_lse=True, ws=False):
+    """Attention through the C ABI: ulys_attn_fwd, or with ws=True
+    ulys_attn_fwd_ws with the workspace it asks for (guarded too)."""
     dev()
     hp = h // P
     qd, kd, vd = to_dev(q), to_dev(k), to_dev(v)
     o = Guarded((s, b, hp, d), TORCH_DT[dtype])
     lse = Guarded((b, hp, s), torch.float32) if want_lse else None
-    rc = binding.ulys_attn_fwd(qd.data_ptr(), kd.data_ptr(), vd.data_ptr(), o.tensor.data_ptr(),
-                               lse.tensor.data_ptr() if lse else None, s, b, h, h_kv, d, P,
-                               int(causal), binding.ULYS_BF16 if dtype == "bf16" else
-                               binding.ULYS_F32, torch.cuda.current_stream().cuda_stream)
+    code = binding.ULYS_BF16 if dtype == "bf16" else binding.ULYS_F32
+    stream = torch.cuda.current_stream().cuda_stream
+    wsbuf = None
+    if ws:
+        nbytes = binding.ulys_attn_fwd_workspace_size(s, b, h, h_kv, d, P, int(causal), code)
+        assert nbytes >= 0
+        wsbuf = Guarded((max(nbytes, 16),), torch.uint8)
+        rc = binding.ulys_attn_fwd_ws(qd.data_ptr(), kd.data_ptr(), vd.data_ptr(),
+                                      o.tensor.data_ptr(), lse.tensor.data_ptr() if lse else None,
+                                      s, b, h, h_kv, d, P, int(causal), code,
+                                      wsbuf.tensor.data_ptr(), nbytes, stream)
+    else:
+        rc = binding.ulys_attn_fwd(qd.data_ptr(), kd.data_ptr(), vd.data_ptr(),
+                                   o.tensor.data_ptr(), lse.tensor.data_ptr() if lse else None,
+                                   s, b, h, h_kv, d, P, int(causal), code, stream)
     assert rc == 0, binding.ulys_status_string(rc)
     torch.cuda.synchronize()
     assert o.guards_intact()
     if lse:
         assert lse.guards_intact()
+    if wsbuf is not None:
+        assert wsbuf.guards_intact()
     return from_dev(o.tensor), (from_dev(lse.tensor) if lse else None)
 
 
@@ -51,12 +66,13 @@ for dtype, d in [("bf16", 128), ("bf16", 64), ("f32", 64), ("f32", 128)]:
                 SMALL.append((dtype, d, s, b, h, h_kv, P, causal))
 
 
+@pytest.mark.parametrize("ws", [False, True], ids=["plain", "ws"])
 @pytest.mark.parametrize("dtype,d,s,b,h,h_kv,P,causal", SMALL)
-def test_small_full_parity(dtype, d, s, b, h, h_kv, P, causal):
-    print(f"case {dtype} d={d} s={s} b={b} h={h} h_kv={h_kv} P={P} causal={causal}",
+def test_small_full_parity(dtype, d, s, b, h, h_kv, P, causal, ws):
+    print(f"case {dtype} d={d} s={s} b={b} h={h} h_kv={h_kv} P={P} causal={causal} ws={ws}",
           flush=True)
     q, k, v = share_inputs(7, s, b, h // P, h_kv // P, d, dtype)
-    o, lse = gpu_attn(q, k, v, s, b, h, h_kv, d, P, causal, dtype)
+    o, lse = gpu_attn(q, k, v, s, b, h, h_kv, d, P, causal, dtype, ws=ws)
     o_ref, lse_ref = oracle.attn(q, k, v, s, b, h, h_kv, d, P, causal)
     err = np.max(np.abs(as_f64(o) - o_ref))
     assert err <= TOL[dtype], err
@@ -87,7 +103,9 @@ def test_full_size_sampled_parity(name):
     w = WORKLOADS[name]
     print(f"case {name}: s={w.s} b={w.b} hp={w.hp} hkvp={w.hkvp} causal={w.causal}", flush=True)
     q, k, v = share_inputs(w.c, w.s, w.b, w.hp, w.hkvp, w.d, w.dtype)
-    o, lse = gpu_attn(q, k, v, w.s, w.b, w.h, w.h_kv, w.d, w.P, w.causal, w.dtype)
+    # the workspace entry point, as the bench calls it (it splits only where
+    # the causal work would otherwise be unbalanced, e.g. the 32K share)
+    o, lse = gpu_attn(q, k, v, w.s, w.b, w.h, w.h_kv, w.d, w.P, w.causal, w.dtype, ws=True)
     rows = synth.row_sample(100 * w.c + 7, w.s, w.b, w.hp, tile_bounds=(64, 128),
                             **FULL[name])
     o_ref, lse_ref = oracle.attn_rows(q, k, v, rows, w.s, w.b, w.h, w.h_kv, w.d, w.P,
@@ -167,3 +185,18 @@ def test_head_independence_chain():
     got = np.concatenate([from_dev(x) for x in back], axis=0)
     o_ref, _ = oracle.attn(qg, kg, vg, s, b, h, h_kv, d, 1, True)
     assert np.max(np.abs(as_f64(got) - o_ref)) <= TOL["bf16"]
+
+
+def test_workspace_split_matches_plain_32k():
+    """At the 32K share the workspace path splits every q-block's keys in two;
+    it must agree with the unsplit kernel to bf16 rounding."""
+    w = WORKLOADS["gpt1.2b-32k"]
+    code = binding.ULYS_BF16
+    assert binding.ulys_attn_fwd_workspace_size(w.s, w.b, w.h, w.h_kv, w.d, w.P, 1, code) > 0
+    q, k, v = share_inputs(w.c, w.s, w.b, w.hp, w.hkvp, w.d, w.dtype)
+    o1, l1 = gpu_attn(q, k, v, w.s, w.b, w.h, w.h_kv, w.d, w.P, True, w.dtype, ws=False)
+    o2, l2 = gpu_attn(q, k, v, w.s, w.b, w.h, w.h_kv, w.d, w.P, True, w.dtype, ws=True)
+    assert np.max(np.abs(as_f64(o1) - as_f64(o2))) <= 2 ** -7  # one bf16 ulp at |O| < 1
+    assert np.max(np.abs(l1.astype(np.float64) - l2)) <= 1e-4
+    o3, l3 = gpu_attn(q, k, v, w.s, w.b, w.h, w.h_kv, w.d, w.P, True, w.dtype, ws=True)
+    assert np.array_equal(o2, o3) and np.array_equal(l2, l3)  # deterministic

@@ -7,5 +7,5 @@ libulysses.so on first use and raises if it has not been built.
 """
 from .binding import (  # noqa: F401
     ULYS_BF16, ULYS_F32, UlyssesError, attn_fwd, pack_seq2head, ulys_abi_version,
-    ulys_attn_fwd, ulys_pack_seq2head, ulys_status_string, ulys_unpack_head2seq,
+    ulys_attn_fwd, ulys_attn_fwd_ws, ulys_attn_fwd_workspace_size, ulys_pack_seq2head, ulys_status_string, ulys_unpack_head2seq,
     unpack_head2seq)

@@ -20,8 +20,8 @@ ULYS_ERR_NULL, ULYS_ERR_DIM, ULYS_ERR_DIVISIBILITY = -1, -2, -3
 ULYS_ERR_UNSUPPORTED, ULYS_ERR_ALIGNMENT, ULYS_ERR_ALIAS, ULYS_ERR_HIP = -4, -5, -6, -7
 
 # every symbol include/ulysses.h declares
-EXPORTED = ("ulys_pack_seq2head", "ulys_unpack_head2seq", "ulys_attn_fwd",
-            "ulys_status_string", "ulys_abi_version")
+EXPORTED = ("ulys_pack_seq2head", "ulys_unpack_head2seq", "ulys_attn_fwd", "ulys_attn_fwd_ws",
+            "ulys_attn_fwd_workspace_size", "ulys_status_string", "ulys_abi_version")
 
 _lib = None
 
@@ -49,6 +49,11 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.ulys_unpack_head2seq.restype = ctypes.c_int
     lib.ulys_attn_fwd.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i32, i32, i32, vp]
     lib.ulys_attn_fwd.restype = ctypes.c_int
+    lib.ulys_attn_fwd_ws.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i32, i32, i32,
+                                     vp, i64, vp]
+    lib.ulys_attn_fwd_ws.restype = ctypes.c_int
+    lib.ulys_attn_fwd_workspace_size.argtypes = [i64, i64, i64, i64, i64, i32, i32, i32]
+    lib.ulys_attn_fwd_workspace_size.restype = ctypes.c_int64
     lib.ulys_status_string.argtypes = [ctypes.c_int]
     lib.ulys_status_string.restype = ctypes.c_char_p
     lib.ulys_abi_version.argtypes = []
@@ -68,6 +73,16 @@ def ulys_unpack_head2seq(y, x, s, b, h, d_h, P, dtype, stream=None) -> int:
 
 def ulys_attn_fwd(q, k, v, o, lse, s, b, h, h_kv, d_h, P, causal, dtype, stream=None) -> int:
     return load().ulys_attn_fwd(q, k, v, o, lse, s, b, h, h_kv, d_h, P, causal, dtype, stream)
+
+
+def ulys_attn_fwd_ws(q, k, v, o, lse, s, b, h, h_kv, d_h, P, causal, dtype, workspace,
+                     workspace_bytes, stream=None) -> int:
+    return load().ulys_attn_fwd_ws(q, k, v, o, lse, s, b, h, h_kv, d_h, P, causal, dtype,
+                                   workspace, workspace_bytes, stream)
+
+
+def ulys_attn_fwd_workspace_size(s, b, h, h_kv, d_h, P, causal, dtype) -> int:
+    return load().ulys_attn_fwd_workspace_size(s, b, h, h_kv, d_h, P, causal, dtype)
 
 
 def ulys_status_string(status: int) -> str:
@@ -130,6 +145,7 @@ def attn_fwd(q, k, v, P: int = 1, causal: bool = False, out=None, lse=False, str
     """One rank's share: q [s, b, h/P, d], k/v [s, b, h_kv/P, d] -> o [s, b, h/P, d].
 
     ``lse`` may be False (skip), True (allocate [b, h/P, s] float32) or a tensor.
+    Allocates (with torch) the workspace ulys_attn_fwd_ws asks for, if any.
     Returns (o, lse or None)."""
     torch = _torch()
     s, b, hp, d = q.shape
@@ -141,9 +157,14 @@ def attn_fwd(q, k, v, P: int = 1, causal: bool = False, out=None, lse=False, str
         lse_t = torch.empty((b, hp, s), dtype=torch.float32, device=q.device)
     elif lse is not False and lse is not None:
         lse_t = lse
-    rc = ulys_attn_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
-                       lse_t.data_ptr() if lse_t is not None else None,
-                       s, b, hp * P, hkvp * P, d, P, int(bool(causal)), dtype_code(q),
-                       _stream(stream))
-    _check(rc, "ulys_attn_fwd")
+    h, h_kv, code = hp * P, hkvp * P, dtype_code(q)
+    ws_bytes = ulys_attn_fwd_workspace_size(s, b, h, h_kv, d, P, int(bool(causal)), code)
+    if ws_bytes < 0:
+        raise UlyssesError(int(ws_bytes), "ulys_attn_fwd_workspace_size")
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=q.device) if ws_bytes > 0 else None
+    rc = ulys_attn_fwd_ws(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                          lse_t.data_ptr() if lse_t is not None else None,
+                          s, b, h, h_kv, d, P, int(bool(causal)), code,
+                          ws.data_ptr() if ws is not None else None, ws_bytes, _stream(stream))
+    _check(rc, "ulys_attn_fwd_ws")
     return out, lse_t

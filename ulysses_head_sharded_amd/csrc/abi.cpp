@@ -84,10 +84,13 @@ int ulys_unpack_head2seq(const void* y, void* x, int64_t s, int64_t b, int64_t h
   return e == hipSuccess ? ULYS_OK : ULYS_ERR_HIP;
 }
 
-int ulys_attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int64_t s,
-                  int64_t b, int64_t h, int64_t h_kv, int64_t d_h, int32_t P, int32_t causal,
-                  int32_t dtype, void* stream) {
-  if (!q || !k || !v || !o) return ULYS_ERR_NULL;
+}  // extern "C"
+
+namespace {
+
+// Size, divisibility and dtype checks of the attention entry points.
+int check_attn_shape(int64_t s, int64_t b, int64_t h, int64_t h_kv, int64_t d_h, int32_t P,
+                     int32_t dtype, int64_t* nq, int64_t* nkv, int64_t* nl) {
   if (s <= 0 || b <= 0 || h <= 0 || h_kv <= 0 || d_h <= 0 || P <= 0) return ULYS_ERR_DIM;
   if (s > kMaxDim || b > kMaxDim || h > kMaxDim || h_kv > kMaxDim || d_h > kMaxDim)
     return ULYS_ERR_DIM;
@@ -96,26 +99,24 @@ int ulys_attn_fwd(const void* q, const void* k, const void* v, void* o, float* l
   if (elt == 0) return ULYS_ERR_UNSUPPORTED;
   if (d_h != 64 && d_h != 128) return ULYS_ERR_UNSUPPORTED;
   const int64_t hp = h / P, hkvp = h_kv / P;
-  const int64_t nq = checked_product({s, b, hp, d_h, (int64_t)elt});
-  const int64_t nkv = checked_product({s, b, hkvp, d_h, (int64_t)elt});
-  const int64_t nl = checked_product({b, hp, s, (int64_t)sizeof(float)});
-  if (nq < 0 || nkv < 0 || nl < 0) return ULYS_ERR_DIM;
+  *nq = checked_product({s, b, hp, d_h, (int64_t)elt});
+  *nkv = checked_product({s, b, hkvp, d_h, (int64_t)elt});
+  *nl = checked_product({b, hp, s, (int64_t)sizeof(float)});
+  if (*nq < 0 || *nkv < 0 || *nl < 0) return ULYS_ERR_DIM;
   // the kernels index tokens and work items with 32-bit integers
   if (s > 0x7FFFFFFF || b * hp > 0x7FFFFFFF || b * hp * s > (int64_t(1) << 40))
     return ULYS_ERR_DIM;
   // the bf16 kernel addresses each tensor with 32-bit byte offsets (plus one
   // tile of keys past the end, which its buffer loads read as zero)
-  if (dtype == ULYS_BF16 && (nq + 2 * 64 * b * hp * d_h * 2 >= (int64_t(1) << 31) ||
-                             nkv + 2 * 64 * b * hkvp * d_h * 2 >= (int64_t(1) << 31)))
+  if (dtype == ULYS_BF16 && (*nq + 2 * 64 * b * hp * d_h * 2 >= (int64_t(1) << 31) ||
+                             *nkv + 2 * 64 * b * hkvp * d_h * 2 >= (int64_t(1) << 31)))
     return ULYS_ERR_DIM;
-  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o)) return ULYS_ERR_ALIGNMENT;
-  if (lse && !aligned16(lse)) return ULYS_ERR_ALIGNMENT;
-  if (overlaps(o, nq, q, nq) || overlaps(o, nq, k, nkv) || overlaps(o, nq, v, nkv))
-    return ULYS_ERR_ALIAS;
-  if (lse && (overlaps(lse, nl, q, nq) || overlaps(lse, nl, k, nkv) ||
-              overlaps(lse, nl, v, nkv) || overlaps(lse, nl, o, nq)))
-    return ULYS_ERR_ALIAS;
+  return ULYS_OK;
+}
 
+ulys::AttnArgs make_args(const void* q, const void* k, const void* v, void* o, float* lse,
+                         int64_t s, int64_t b, int64_t h, int64_t h_kv, int64_t d_h, int32_t P,
+                         int32_t causal) {
   ulys::AttnArgs a;
   a.q = q;
   a.k = k;
@@ -124,13 +125,69 @@ int ulys_attn_fwd(const void* q, const void* k, const void* v, void* o, float* l
   a.lse = lse;
   a.s = s;
   a.b = b;
-  a.hp = hp;
-  a.hkvp = hkvp;
+  a.hp = h / P;
+  a.hkvp = h_kv / P;
   a.d = d_h;
   a.causal = causal != 0;
+  a.workspace = nullptr;
+  a.workspace_bytes = 0;
+  return a;
+}
+
+}  // namespace
+
+extern "C" {
+
+int ulys_attn_fwd_ws(const void* q, const void* k, const void* v, void* o, float* lse,
+                     int64_t s, int64_t b, int64_t h, int64_t h_kv, int64_t d_h, int32_t P,
+                     int32_t causal, int32_t dtype, void* workspace, int64_t workspace_bytes,
+                     void* stream) {
+  if (!q || !k || !v || !o) return ULYS_ERR_NULL;
+  int64_t nq = 0, nkv = 0, nl = 0;
+  const int rc = check_attn_shape(s, b, h, h_kv, d_h, P, dtype, &nq, &nkv, &nl);
+  if (rc != ULYS_OK) return rc;
+  if (workspace && workspace_bytes < 0) return ULYS_ERR_DIM;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o)) return ULYS_ERR_ALIGNMENT;
+  if (lse && !aligned16(lse)) return ULYS_ERR_ALIGNMENT;
+  if (workspace && !aligned16(workspace)) return ULYS_ERR_ALIGNMENT;
+  if (overlaps(o, nq, q, nq) || overlaps(o, nq, k, nkv) || overlaps(o, nq, v, nkv))
+    return ULYS_ERR_ALIAS;
+  if (lse && (overlaps(lse, nl, q, nq) || overlaps(lse, nl, k, nkv) ||
+              overlaps(lse, nl, v, nkv) || overlaps(lse, nl, o, nq)))
+    return ULYS_ERR_ALIAS;
+  if (workspace && workspace_bytes > 0) {
+    const int64_t w = workspace_bytes;
+    if (overlaps(workspace, w, q, nq) || overlaps(workspace, w, k, nkv) ||
+        overlaps(workspace, w, v, nkv) || overlaps(workspace, w, o, nq) ||
+        (lse && overlaps(workspace, w, lse, nl)))
+      return ULYS_ERR_ALIAS;
+  }
+  ulys::AttnArgs a = make_args(q, k, v, o, lse, s, b, h, h_kv, d_h, P, causal);
+  if (workspace && workspace_bytes > 0) {
+    a.workspace = workspace;
+    a.workspace_bytes = workspace_bytes;
+  }
   const hipError_t e = (dtype == ULYS_BF16) ? ulys::launch_attn_bf16(a, (hipStream_t)stream)
                                             : ulys::launch_attn_f32(a, (hipStream_t)stream);
   return e == hipSuccess ? ULYS_OK : ULYS_ERR_HIP;
+}
+
+int ulys_attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int64_t s,
+                  int64_t b, int64_t h, int64_t h_kv, int64_t d_h, int32_t P, int32_t causal,
+                  int32_t dtype, void* stream) {
+  return ulys_attn_fwd_ws(q, k, v, o, lse, s, b, h, h_kv, d_h, P, causal, dtype, nullptr, 0,
+                          stream);
+}
+
+int64_t ulys_attn_fwd_workspace_size(int64_t s, int64_t b, int64_t h, int64_t h_kv, int64_t d_h,
+                                     int32_t P, int32_t causal, int32_t dtype) {
+  int64_t nq = 0, nkv = 0, nl = 0;
+  const int rc = check_attn_shape(s, b, h, h_kv, d_h, P, dtype, &nq, &nkv, &nl);
+  if (rc != ULYS_OK) return rc;
+  if (dtype != ULYS_BF16) return 0;
+  const ulys::AttnArgs a = make_args(nullptr, nullptr, nullptr, nullptr, nullptr, s, b, h, h_kv,
+                                     d_h, P, causal);
+  return ulys::attn_bf16_workspace_size(a);
 }
 
 const char* ulys_status_string(int status) {

@@ -65,6 +65,10 @@ struct Cfg {
   // direct global->LDS loads: one wave instruction fills 1 KiB = ROWS_PER_LOAD rows
   static constexpr int ROWS_PER_LOAD = 1024 / ROW_BYTES;
   static constexpr int LOADS = kBN / (ROWS_PER_LOAD * kWaves);  // per wave per tensor
+  // one partial state of a work unit: per wave and lane, the D/2 O^T
+  // accumulator slots, the running max m and the lane's running sum l
+  static constexpr int PART_SLOTS = D / 2 + 2;
+  static constexpr int PART_FLOATS = kWaves * 64 * PART_SLOTS;
   static_assert(LOADS * ROWS_PER_LOAD * kWaves == kBN, "tile split");
 };
 
@@ -81,6 +85,8 @@ struct Params {
   int n_qblk;  // ceil(s / QB)
   int nsub;    // G / QH
   int slots;   // workgroups resident at once (CUs x workgroups per CU), 0 = no pairing
+  int nsplit;  // 1: one unit per item; 2: each item's key tiles split in two halves
+  float* ws;   // nsplit == 2: partial states, PART_FLOATS per (item, half)
   int q_tok_bytes, kv_tok_bytes;  // bytes between consecutive tokens
   int q_bytes, kv_bytes;  // tensor sizes in bytes (bounds of the buffer resources)
   float c;     // log2(e) / sqrt(d_h)
@@ -137,6 +143,56 @@ __device__ __forceinline__ void load_lds16(__amdgpu_buffer_rsrc_t r, uint8_t* ld
 __device__ __forceinline__ int k_swz(int r) { return r & 7; }
 __device__ __forceinline__ int v_swz(int r) { return 2 * (r & 3); }
 
+// Work item `rank` (longest causal q-block first, then batch, KV head, head
+// subgroup) as seen by one wave: its batch, KV head, query head and first query.
+struct Item {
+  int qblk, be, kvg, head, q0;
+};
+__device__ __forceinline__ Item decode_item(const Params& p, int rank, int wave, bool causal) {
+  Item it;
+  const int per_q = p.b * p.hkvp * p.nsub;
+  const int qi = rank / per_q;
+  int rest = rank - qi * per_q;
+  it.qblk = causal ? (p.n_qblk - 1 - qi) : qi;
+  const int sub = rest % p.nsub;
+  rest /= p.nsub;
+  it.kvg = rest % p.hkvp;
+  it.be = rest / p.hkvp;
+  const int wph = kWaves / p.QH;  // waves per query head
+  it.head = it.kvg * p.G + sub * p.QH + wave / wph;
+  it.q0 = it.qblk * p.QB + (wave % wph) * kQW;
+  return it;
+}
+
+// O = A / l rounded once to bf16, and lse in natural log, for this lane's
+// query (rows past s fall outside the buffer resource and are dropped).
+template <int D>
+__device__ __forceinline__ void store_output(const Params& p, const f32x16* oacc, float m_run,
+                                             float l_run, int be, int head, int my_q, int hh) {
+  const float l_tot = xsum32(l_run);
+  const float inv = 1.f / l_tot;
+  const __amdgpu_buffer_rsrc_t ro = rsrc(p.o, p.q_bytes);
+  const int ooff = my_q * p.q_tok_bytes + (be * p.hp + head) * D * 2 + hh * 8;
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+    for (int g4 = 0; g4 < 4; ++g4) {
+      const __bf16 x0 = (__bf16)(oacc[db][4 * g4 + 0] * inv);
+      const __bf16 x1 = (__bf16)(oacc[db][4 * g4 + 1] * inv);
+      const __bf16 x2 = (__bf16)(oacc[db][4 * g4 + 2] * inv);
+      const __bf16 x3 = (__bf16)(oacc[db][4 * g4 + 3] * inv);
+      const uint32_t w0 = (uint32_t)__builtin_bit_cast(uint16_t, x0) |
+                          ((uint32_t)__builtin_bit_cast(uint16_t, x1) << 16);
+      const uint32_t w1 = (uint32_t)__builtin_bit_cast(uint16_t, x2) |
+                          ((uint32_t)__builtin_bit_cast(uint16_t, x3) << 16);
+      __builtin_amdgcn_raw_buffer_store_b64(u32x2{w0, w1}, ro, ooff + (db * 32 + 8 * g4) * 2, 0,
+                                            0);
+    }
+  if (p.lse && hh == 0 && my_q < p.s)
+    p.lse[(int64_t)(be * p.hp + head) * p.s + my_q] =
+        (m_run * p.c + __builtin_amdgcn_logf(l_tot)) * 0.69314718055994531f;
+}
+
 template <int D, bool CAUSAL>
 __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(Params p) {
   using C = Cfg<D>;
@@ -146,26 +202,22 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(Params p) {
   const int lane = tid & 63, wave = tid >> 6;
   const int l32 = lane & 31, hh = lane >> 5;
 
-  // ---- work item.  Items are ranked longest causal q-block first (then batch,
-  // KV head, head subgroup).  The first `slots` workgroups are resident at once;
-  // the dispatcher gives workgroups p and p + slots/2 the same CU, so the second
-  // half of that first wave takes the ranks in reverse, pairing the longest item
-  // with the shortest on each CU.  Later workgroups start as slots free up and
-  // take the remaining ranks longest-first.
+  // ---- work unit.  With nsplit == 2, unit u is half u % 2 of item u / 2 (the
+  // items ranked longest first, so unit sizes never increase).  Otherwise the
+  // unit is the item; the first `slots` workgroups are resident at once and
+  // the dispatcher gives workgroups p and p + slots/2 the same CU, so the
+  // second half of that first wave takes the ranks in reverse, pairing the
+  // longest item with the shortest on each CU.
   int rank = blockIdx.x;
-  if (CAUSAL && p.slots > 0 && rank < p.slots && rank >= p.slots / 2)
+  int half_id = 0;
+  if (p.nsplit == 2) {
+    half_id = rank & 1;
+    rank >>= 1;
+  } else if (CAUSAL && p.slots > 0 && rank < p.slots && rank >= p.slots / 2) {
     rank = p.slots + p.slots / 2 - 1 - rank;
-  const int per_q = p.b * p.hkvp * p.nsub;
-  const int qi = rank / per_q;
-  int rest = rank - qi * per_q;
-  const int qblk = CAUSAL ? (p.n_qblk - 1 - qi) : qi;
-  const int sub = rest % p.nsub;
-  rest /= p.nsub;
-  const int kvg = rest % p.hkvp;
-  const int be = rest / p.hkvp;
-  const int wph = kWaves / p.QH;  // waves per query head
-  const int head = kvg * p.G + sub * p.QH + wave / wph;
-  const int q0 = qblk * p.QB + (wave % wph) * kQW;  // first query of this wave
+  }
+  const Item item = decode_item(p, rank, wave, CAUSAL);
+  const int qblk = item.qblk, be = item.be, kvg = item.kvg, head = item.head, q0 = item.q0;
   const int my_q = q0 + l32;
 
   const __amdgpu_buffer_rsrc_t rq = rsrc(p.q, p.q_bytes);
@@ -189,7 +241,11 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(Params p) {
   }
 
   const int q_hi = min(p.s, (qblk + 1) * p.QB);
-  const int n_tiles = CAUSAL ? (q_hi + kBN - 1) / kBN : (p.s + kBN - 1) / kBN;
+  const int n_item_tiles = CAUSAL ? (q_hi + kBN - 1) / kBN : (p.s + kBN - 1) / kBN;
+  // key tiles [t_lo, n_tiles) of this unit
+  const int t_split = (n_item_tiles + 1) >> 1;
+  const int t_lo = (p.nsplit == 2 && half_id == 1) ? t_split : 0;
+  const int n_tiles = (p.nsplit == 2 && half_id == 0) ? t_split : n_item_tiles;
   const int wave_last_q = min(q0 + kQW, p.s) - 1;
   const int wave_tiles = (q0 >= p.s) ? 0 : (CAUSAL ? wave_last_q / kBN + 1 : n_tiles);
 
@@ -237,12 +293,12 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(Params p) {
     v_rd[j] = vr * C::ROW_BYTES + ((c ^ v_swz(vr)) << 4) + 8 * (lane & 1);
   }
 
-  load_tile(0, 0);
+  if (t_lo < n_tiles) load_tile(t_lo, 0);
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
 
-  for (int t = 0; t < n_tiles; ++t) {
-    const int cur = t & 1;
+  for (int t = t_lo; t < n_tiles; ++t) {
+    const int cur = (t - t_lo) & 1;
     if (t + 1 < n_tiles) load_tile(t + 1, cur ^ 1);
 
     if (t < wave_tiles) {
@@ -343,30 +399,73 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(Params p) {
     __syncthreads();
   }
 
-  // ---- epilogue: O = A / l, rounded once to bf16; lse in natural log.  Rows
-  // past s fall outside the buffer resource and are dropped by the stores.
-  const float l_tot = xsum32(l_run);
-  const float inv = 1.f / l_tot;
-  const __amdgpu_buffer_rsrc_t ro = rsrc(p.o, p.q_bytes);
-  const int ooff = my_q * p.q_tok_bytes + q_head_off + hh * 8;
+  if (p.nsplit == 2) {
+    // partial state of this half, lanes contiguous: [wave][slot][lane]
+    float* part = p.ws + (int64_t)blockIdx.x * C::PART_FLOATS + wave * (C::PART_SLOTS * 64) + lane;
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) part[(db * 16 + r) * 64] = oacc[db][r];
+    part[(D / 2) * 64] = m_run;
+    part[(D / 2 + 1) * 64] = l_run;
+    return;
+  }
+  store_output<D>(p, oacc, m_run, l_run, be, head, my_q, hh);
+}
+
+// Workgroups of this kernel resident at once on the current device (CUs x
+// workgroups per CU, set by its LDS and VGPR use), or 0 if unknown.
+int64_t resident_slots(int64_t d) {
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+    return 0;
+  return (int64_t)cus * (d == 128 ? 2 : 3);
+}
+
+int64_t count_items(const AttnArgs& a) {
+  const int64_t G = a.hp / a.hkvp;
+  const int64_t QH = (G % 4 == 0) ? 4 : (G % 2 == 0) ? 2 : 1;
+  const int64_t QB = kQW * (kWaves / QH);
+  return (a.s + QB - 1) / QB * a.b * a.hkvp * (G / QH);
+}
+
+// Bytes of workspace the split mode needs: causal work with too few items to
+// fill the resident slots twice (the longest item alone would set the run
+// time) is split into two halves per item.  0 when no split is used.
+int64_t attn_bf16_workspace_bytes(const AttnArgs& a) {
+  const int64_t items = count_items(a);
+  const int64_t slots = resident_slots(a.d);
+  if (!a.causal || slots <= 0 || items >= 2 * slots) return 0;
+  const int64_t part = (int64_t)kWaves * 64 * (a.d / 2 + 2) * 4;
+  return items * 2 * part;
+}
+
+// Merge of the two halves of every item: the same rescaling as the online
+// softmax, applied once to two partial states over disjoint key ranges.
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(kThreads) void attn_merge_kernel(Params p) {
+  using C = Cfg<D>;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int l32 = lane & 31, hh = lane >> 5;
+  const Item item = decode_item(p, blockIdx.x, wave, CAUSAL);
+  const float* p0 = p.ws + (int64_t)(2 * blockIdx.x) * C::PART_FLOATS +
+                    wave * (C::PART_SLOTS * 64) + lane;
+  const float* p1 = p0 + C::PART_FLOATS;
+  const float m0 = p0[(D / 2) * 64], m1 = p1[(D / 2) * 64];
+  const float m = fmaxf(m0, m1);
+  // the first half always holds key 0, so m is finite for every real query
+  const float a0 = __builtin_amdgcn_exp2f((m0 - m) * p.c);
+  const float a1 = __builtin_amdgcn_exp2f((m1 - m) * p.c);
+  const float l = p0[(D / 2 + 1) * 64] * a0 + p1[(D / 2 + 1) * 64] * a1;
+  f32x16 oacc[D / 32];
 #pragma unroll
   for (int db = 0; db < D / 32; ++db)
 #pragma unroll
-    for (int g4 = 0; g4 < 4; ++g4) {
-      const __bf16 x0 = (__bf16)(oacc[db][4 * g4 + 0] * inv);
-      const __bf16 x1 = (__bf16)(oacc[db][4 * g4 + 1] * inv);
-      const __bf16 x2 = (__bf16)(oacc[db][4 * g4 + 2] * inv);
-      const __bf16 x3 = (__bf16)(oacc[db][4 * g4 + 3] * inv);
-      const uint32_t w0 = (uint32_t)__builtin_bit_cast(uint16_t, x0) |
-                          ((uint32_t)__builtin_bit_cast(uint16_t, x1) << 16);
-      const uint32_t w1 = (uint32_t)__builtin_bit_cast(uint16_t, x2) |
-                          ((uint32_t)__builtin_bit_cast(uint16_t, x3) << 16);
-      __builtin_amdgcn_raw_buffer_store_b64(u32x2{w0, w1}, ro, ooff + (db * 32 + 8 * g4) * 2, 0,
-                                            0);
-    }
-  if (p.lse && hh == 0 && my_q < p.s)
-    p.lse[(int64_t)(be * p.hp + head) * p.s + my_q] =
-        (m_run * p.c + __builtin_amdgcn_logf(l_tot)) * 0.69314718055994531f;
+    for (int r = 0; r < 16; ++r)
+      oacc[db][r] = p0[(db * 16 + r) * 64] * a0 + p1[(db * 16 + r) * 64] * a1;
+  store_output<D>(p, oacc, m, l, item.be, item.head, item.q0 + l32, hh);
 }
 
 template <int D>
@@ -395,24 +494,33 @@ hipError_t launch_d(const AttnArgs& a, hipStream_t stream) {
   if (items <= 0) return hipSuccess;
   if (items > 0x7FFFFFFF) return hipErrorInvalidValue;
   // pairing applies when the whole first resident wave is present
-  int dev = 0, cus = 0;
-  p.slots = 0;
-  if (hipGetDevice(&dev) == hipSuccess &&
-      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess) {
-    const int per_cu = (D == 128) ? 2 : 3;  // LDS- and VGPR-limited residency of this kernel
-    const int64_t slots = (int64_t)cus * per_cu;
-    if (items >= slots && (slots % 2) == 0) p.slots = (int)slots;
-  }
+  const int64_t slots = resident_slots(D);
+  p.slots = (slots > 0 && items >= slots && (slots % 2) == 0) ? (int)slots : 0;
+  // split halves (see attn_bf16_workspace_bytes) when the caller gave room
+  const int64_t ws_need = attn_bf16_workspace_bytes(a);
+  const int nsplit = (ws_need > 0 && a.workspace && a.workspace_bytes >= ws_need) ? 2 : 1;
+  p.nsplit = nsplit;
+  p.ws = nsplit == 2 ? (float*)a.workspace : nullptr;
   if (a.causal)
-    hipLaunchKernelGGL((attn_bf16_kernel<D, true>), dim3((unsigned)items), dim3(kThreads), 0,
+    hipLaunchKernelGGL((attn_bf16_kernel<D, true>), dim3((unsigned)(items * nsplit)),
+                       dim3(kThreads), 0, stream, p);
+  else
+    hipLaunchKernelGGL((attn_bf16_kernel<D, false>), dim3((unsigned)(items * nsplit)),
+                       dim3(kThreads), 0, stream, p);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || nsplit == 1) return e;
+  if (a.causal)
+    hipLaunchKernelGGL((attn_merge_kernel<D, true>), dim3((unsigned)items), dim3(kThreads), 0,
                        stream, p);
   else
-    hipLaunchKernelGGL((attn_bf16_kernel<D, false>), dim3((unsigned)items), dim3(kThreads), 0,
+    hipLaunchKernelGGL((attn_merge_kernel<D, false>), dim3((unsigned)items), dim3(kThreads), 0,
                        stream, p);
   return hipGetLastError();
 }
 
 }  // namespace
+
+int64_t attn_bf16_workspace_size(const AttnArgs& a) { return attn_bf16_workspace_bytes(a); }
 
 hipError_t launch_attn_bf16(const AttnArgs& a, hipStream_t stream) {
   if (a.d == 128) return launch_d<128>(a, stream);

@@ -48,9 +48,13 @@ struct AttnArgs {
   int64_t hkvp;     // KV heads of the share
   int64_t d;        // head size
   int causal;
+  void* workspace;          // may be null
+  int64_t workspace_bytes;
 };
 
 hipError_t launch_attn_bf16(const AttnArgs& a, hipStream_t stream);
+// workspace bytes launch_attn_bf16 would use to balance causal work (0: none)
+int64_t attn_bf16_workspace_size(const AttnArgs& a);
 hipError_t launch_attn_f32(const AttnArgs& a, hipStream_t stream);
 
 }  // namespace ulys
