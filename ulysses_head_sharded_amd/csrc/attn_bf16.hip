@@ -134,14 +134,30 @@ __device__ __forceinline__ void load_lds16(__amdgpu_buffer_rsrc_t r, uint8_t* ld
                                            16, voff, 0, 0, 0);
 }
 
-// LDS tiles are unpadded, with the 16-byte chunks of row r XOR-swizzled:
-//  * K: chunk c is stored at c ^ (r & 7).  The QK MFMA reads 8 consecutive rows
-//    at one logical chunk, which then land in 8 different bank groups.
-//  * V: chunk c is stored at c ^ 2 (r & 3).  A transposing read takes 4
-//    consecutive rows x 32 bytes per 16 lanes, which then land in 4 different
-//    32-byte bank groups.
-__device__ __forceinline__ int k_swz(int r) { return r & 7; }
-__device__ __forceinline__ int v_swz(int r) { return 2 * (r & 3); }
+// LDS tiles are unpadded, with the 16-byte chunks of row r XOR-swizzled so
+// that reads are free of bank conflicts on gfx950's LDS, which serves 256
+// bytes (64 banks) per clock: 16 lanes of a 16-byte read, 32 lanes of an
+// 8-byte read.
+//  * K: the QK MFMA operand read takes 16 consecutive rows at one logical
+//    chunk per clock.  With 256-byte rows (D = 128) chunk c is stored at
+//    c ^ (r & 15): 16 distinct chunks.  With 128-byte rows (D = 64) rows pair
+//    up in one 256-byte bank line, so even rows use c ^ (r/2 & 7) and odd rows
+//    c ^ ((r/2 & 7) ^ 4): 16 distinct (half-line, chunk) slots.
+//  * V: a transposing read takes 4 consecutive rows x 64 bytes per 32 lanes
+//    (4 chunks 4 db .. 4 db + 3).  With 256-byte rows chunk c is stored at
+//    c ^ (10 (r & 3) mod 16): the 4 rows' chunk groups land on 4 different
+//    64-byte quarters of the bank line, and on different 32-byte halves of
+//    128 bytes too.  With 128-byte rows c ^ 2 (r & 3) does the same.
+template <int D>
+__device__ __forceinline__ int k_swz(int r) {
+  if constexpr (D == 128) return r & 15;
+  else return ((r >> 1) ^ ((r & 1) << 2)) & 7;
+}
+template <int D>
+__device__ __forceinline__ int v_swz(int r) {
+  if constexpr (D == 128) return (10 * (r & 3)) & 15;
+  else return 2 * (r & 3);
+}
 
 // Work item `rank` (longest causal q-block first, then batch, KV head, head
 // subgroup) as seen by one wave: its batch, KV head, query head and first query.
@@ -258,8 +274,8 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(Params p) {
   for (int i = 0; i < C::LOADS; ++i) {
     const int row = (wave * C::LOADS + i) * C::ROWS_PER_LOAD + lane / C::CHUNKS;
     const int pc = lane % C::CHUNKS;
-    k_src[i] = row * p.kv_tok_bytes + kv_head_off + ((pc ^ k_swz(row)) << 4);
-    v_src[i] = row * p.kv_tok_bytes + kv_head_off + ((pc ^ v_swz(row)) << 4);
+    k_src[i] = row * p.kv_tok_bytes + kv_head_off + ((pc ^ k_swz<D>(row)) << 4);
+    v_src[i] = row * p.kv_tok_bytes + kv_head_off + ((pc ^ v_swz<D>(row)) << 4);
   }
   f32x16 oacc[D / 32];
 #pragma unroll
@@ -278,19 +294,22 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(Params p) {
       load_lds16(rv, lds + C::V_BASE + buf * C::TILE_BYTES + dst, v_src[i] + koff);
     }
   };
-  // lane parts of the LDS read addresses (bytes).  K: row kb*32 + l32, chunk
-  // (2 dk + hh) ^ (l32 & 7); the bit of the chunk above 7 passes the swizzle.
-  int k_rd[4];
+  // lane parts of the LDS read addresses (bytes), one per operand column
+  // block.  K, step dk: row kb*32 + l32 (kb*32 leaves the swizzle unchanged),
+  // logical chunk 2 dk + hh.
+  int k_rd[D / 16];
 #pragma unroll
-  for (int j = 0; j < 4; ++j) k_rd[j] = l32 * C::ROW_BYTES + (((2 * j + hh) ^ (l32 & 7)) << 4);
-  // V (transposing reads): row 4 hh + (l%16)/4 of a 16-key step (the keys this
-  // lane's P^T registers hold), byte column 64 db + 32 ((l/16)%2) + 8 (l%4)
+  for (int dk = 0; dk < D / 16; ++dk)
+    k_rd[dk] = l32 * C::ROW_BYTES + (((2 * dk + hh) ^ k_swz<D>(l32)) << 4);
+  // V (transposing reads), feature block db: row 4 hh + (l%16)/4 of a 16-key
+  // step (the keys this lane's P^T registers hold; 16 ks and +8 leave the
+  // swizzle unchanged), byte column 64 db + 32 ((l/16)%2) + 8 (l%4)
   const int vr = 4 * hh + ((lane & 15) >> 2);
-  int v_rd[2];
+  int v_rd[D / 32];
 #pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    const int c = 4 * j + 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1);
-    v_rd[j] = vr * C::ROW_BYTES + ((c ^ v_swz(vr)) << 4) + 8 * (lane & 1);
+  for (int db = 0; db < D / 32; ++db) {
+    const int c = 4 * db + 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1);
+    v_rd[db] = vr * C::ROW_BYTES + ((c ^ v_swz<D>(vr)) << 4) + 8 * (lane & 1);
   }
 
   if (t_lo < n_tiles) load_tile(t_lo, 0);
@@ -317,8 +336,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(Params p) {
       for (int dk = 0; dk < D / 16; ++dk)
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) {
-          const bf16x8 a = *(const bf16x8*)(kl + kb * 32 * C::ROW_BYTES + (dk >> 2) * 128 +
-                                            k_rd[dk & 3]);
+          const bf16x8 a = *(const bf16x8*)(kl + kb * 32 * C::ROW_BYTES + k_rd[dk]);
           sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[dk], sacc[kb], 0, 0, 0);
         }
       // keep four K operand reads in flight ahead of the MFMAs that use them:
@@ -386,7 +404,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(Params p) {
       for (int ks = 0; ks < kBN / 16; ++ks)
 #pragma unroll
         for (int db = 0; db < D / 32; ++db) {
-          const uint8_t* vb = vl + (ks * 16) * C::ROW_BYTES + (db >> 1) * 128 + v_rd[db & 1];
+          const uint8_t* vb = vl + (ks * 16) * C::ROW_BYTES + v_rd[db];
           const u32x2 lo = lds_read_tr(reinterpret_cast<const uint16_t*>(vb));
           const u32x2 hi = lds_read_tr(reinterpret_cast<const uint16_t*>(vb + 8 * C::ROW_BYTES));
           const bf16x8 a = as_bf16x8(u32x4{lo[0], lo[1], hi[0], hi[1]});
