@@ -9,9 +9,10 @@
 // l = 0, A = 0, finish O = A / l), so the s x s score matrix never exists.
 //
 // How it maps onto gfx950:
-//  * A workgroup is 4 waves; each wave owns 32 queries of one head.  For GQA
-//    the 4 waves may cover up to 4 query heads of one KV group, so a K/V tile
-//    is fetched once for all of them.
+//  * A workgroup is 8 waves (one per CU; two per SIMD) and each wave owns 32
+//    queries of one head, so every K/V tile brought into LDS serves 256
+//    queries.  For GQA the waves may cover up to 8 query heads of one KV
+//    group, so a K/V tile is fetched once for all of them.
 //  * Scores are computed transposed, S^T = K Q^T, with
 //    v_mfma_f32_32x32x16_bf16: K (from LDS) is the A operand and the wave's
 //    Q^T (kept in registers for the whole loop) the B operand.  In the 32x32
@@ -22,18 +23,22 @@
 //    O^T += V^T P^T with the same instruction.  V stays row-major in LDS; its
 //    A operand comes from ds_read_b64_tr_b16, which transposes 4x4 blocks of
 //    16-bit values across lanes as it reads.
-//  * K and V tiles of 64 keys are double-buffered in LDS (two workgroups per
-//    CU) and filled by direct global->LDS buffer loads (no staging
-//    registers); the next tile's loads are in flight during the current
-//    tile's MFMAs.  Loads go through raw buffer resources, so rows past the
-//    sequence read as zero and the ragged tail needs no branch.  Tile rows
-//    are unpadded with XOR-swizzled 16-byte chunks chosen so the MFMA K reads
-//    and the transposing V reads both hit distinct banks.
+//  * K and V tiles of 64 keys are double-buffered in LDS and filled by direct
+//    global->LDS buffer loads (no staging registers).  The loop is software
+//    pipelined: step t issues the loads of K_{t+2} and V_{t+1}, the MFMAs of
+//    S_{t+1}, the softmax of S_t and the MFMAs of V_t^T P_t^T, so the score
+//    MFMAs of the next tile overlap the exp work of this one.  Loads go
+//    through raw buffer resources, so rows past the sequence read as zero
+//    and the ragged tail needs no branch.  Tile rows are unpadded with
+//    XOR-swizzled 16-byte chunks chosen so the MFMA K reads and the
+//    transposing V reads are free of bank conflicts.
 //  * exp2 with log2(e)/sqrt(d_h) folded into one FMA per score; the online
 //    rescale runs only when some row's max grew; causal tiles above a wave's
 //    diagonal are skipped and only diagonal / tail tiles are masked.
-//  * Work items are ordered longest-first (causal); in the first resident
-//    wave the longest and shortest items share a CU.
+//  * Work items are ordered longest-first (causal), which the dispatcher turns
+//    into a longest-processing-time-first schedule; with a workspace, causal
+//    shares with few items split every item's keys in two halves that a
+//    second kernel merges.
 #include <math.h>
 
 #include "internal.h"
@@ -46,7 +51,7 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
-constexpr int kWaves = 4;
+constexpr int kWaves = 8;
 constexpr int kThreads = 64 * kWaves;
 constexpr int kBN = 64;  // keys per tile
 constexpr int kQW = 32;  // queries per wave
@@ -80,11 +85,10 @@ struct Params {
   float* lse;
   int s, b, hp, hkvp;
   int G;       // query heads per KV head
-  int QH;      // query heads per workgroup (divides G, <= 4)
-  int QB;      // queries per head per workgroup = 32 * 4 / QH
+  int QH;      // query heads per workgroup (divides G, <= 8)
+  int QB;      // queries per head per workgroup = 32 * 8 / QH
   int n_qblk;  // ceil(s / QB)
   int nsub;    // G / QH
-  int slots;   // workgroups resident at once (CUs x workgroups per CU), 0 = no pairing
   int nsplit;  // 1: one unit per item; 2: each item's key tiles split in two halves
   float* ws;   // nsplit == 2: partial states, PART_FLOATS per (item, half)
   int q_tok_bytes, kv_tok_bytes;  // bytes between consecutive tokens
@@ -120,7 +124,7 @@ __device__ __forceinline__ float xsum32(float x) {
 // column c0 + 4 (s%4) of a row-major tile, output lane L therefore holds
 // rows r0 .. r0+3 of column c0 + L: four consecutive keys of one feature,
 // i.e. one half of an MFMA operand taken straight from row-major V.
-__device__ __forceinline__ u32x2 lds_read_tr(const uint16_t* p) {
+__device__ __forceinline__ u32x2 lds_read_tr(const uint16_t* __restrict__ p) {
   typedef short i16x4 __attribute__((ext_vector_type(4)));
   const i16x4 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
       (__attribute__((address_space(3))) i16x4*)(p));
@@ -210,7 +214,7 @@ __device__ __forceinline__ void store_output(const Params& p, const f32x16* oacc
 }
 
 template <int D, bool CAUSAL>
-__global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(Params p) {
+__global__ __launch_bounds__(kThreads, 1) void attn_bf16_kernel(Params p) {
   using C = Cfg<D>;
   __shared__ __attribute__((aligned(16))) uint8_t lds[C::LDS_BYTES];
 
@@ -218,19 +222,15 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(Params p) {
   const int lane = tid & 63, wave = tid >> 6;
   const int l32 = lane & 31, hh = lane >> 5;
 
-  // ---- work unit.  With nsplit == 2, unit u is half u % 2 of item u / 2 (the
-  // items ranked longest first, so unit sizes never increase).  Otherwise the
-  // unit is the item; the first `slots` workgroups are resident at once and
-  // the dispatcher gives workgroups p and p + slots/2 the same CU, so the
-  // second half of that first wave takes the ranks in reverse, pairing the
-  // longest item with the shortest on each CU.
+  // ---- work unit.  With nsplit == 2, unit u is half u % 2 of item u / 2.
+  // Items are ranked longest first, so unit sizes never increase and the
+  // dispatcher, which hands the next unit to the first CU that frees up,
+  // schedules longest-processing-time first.
   int rank = blockIdx.x;
   int half_id = 0;
   if (p.nsplit == 2) {
     half_id = rank & 1;
     rank >>= 1;
-  } else if (CAUSAL && p.slots > 0 && rank < p.slots && rank >= p.slots / 2) {
-    rank = p.slots + p.slots / 2 - 1 - rank;
   }
   const Item item = decode_item(p, rank, wave, CAUSAL);
   const int qblk = item.qblk, be = item.be, kvg = item.kvg, head = item.head, q0 = item.q0;
@@ -285,14 +285,21 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(Params p) {
   float m_run = -INFINITY;  // running max of raw scores (q.k)
   float l_run = 0.f;        // this lane's share of the running sum
 
-  auto load_tile = [&](int t, int buf) {
-    const int koff = t * kBN * p.kv_tok_bytes;
+  // K tile t goes to K buffer t % 2 and V tile t to V buffer t % 2.  Past
+  // the unit's last tile the source is clamped to it while the buffer stays
+  // that of t, which no later step reads.
+  const int t_last = n_tiles - 1;
+  auto load_k = [&](int t) {
+    const int koff = min(t, t_last) * kBN * p.kv_tok_bytes;
+    uint8_t* dst = lds + C::K_BASE + (t & 1) * C::TILE_BYTES + wave * C::LOADS * 1024;
 #pragma unroll
-    for (int i = 0; i < C::LOADS; ++i) {
-      const int dst = (wave * C::LOADS + i) * 1024;
-      load_lds16(rk, lds + C::K_BASE + buf * C::TILE_BYTES + dst, k_src[i] + koff);
-      load_lds16(rv, lds + C::V_BASE + buf * C::TILE_BYTES + dst, v_src[i] + koff);
-    }
+    for (int i = 0; i < C::LOADS; ++i) load_lds16(rk, dst + i * 1024, k_src[i] + koff);
+  };
+  auto load_v = [&](int t) {
+    const int koff = min(t, t_last) * kBN * p.kv_tok_bytes;
+    uint8_t* dst = lds + C::V_BASE + (t & 1) * C::TILE_BYTES + wave * C::LOADS * 1024;
+#pragma unroll
+    for (int i = 0; i < C::LOADS; ++i) load_lds16(rv, dst + i * 1024, v_src[i] + koff);
   };
   // lane parts of the LDS read addresses (bytes), one per operand column
   // block.  K, step dk: row kb*32 + l32 (kb*32 leaves the swizzle unchanged),
@@ -312,107 +319,138 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(Params p) {
     v_rd[db] = vr * C::ROW_BYTES + ((c ^ v_swz<D>(vr)) << 4) + 8 * (lane & 1);
   }
 
-  if (t_lo < n_tiles) load_tile(t_lo, 0);
+  // S^T block kb of tile t: keys 64 t + 32 kb + (8 (r/4) + 4 hh + r%4), query
+  // my_q.  The two blocks' MFMA chains are interleaved.
+  auto qk = [&](int t, f32x16* sc) {
+    const uint8_t* kl = lds + C::K_BASE + (t & 1) * C::TILE_BYTES;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) sc[kb][r] = 0.f;
+#pragma unroll
+    for (int dk = 0; dk < D / 16; ++dk)
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        const bf16x8 a = *(const bf16x8*)(kl + kb * 32 * C::ROW_BYTES + k_rd[dk]);
+        sc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[dk], sc[kb], 0, 0, 0);
+      }
+  };
+  // O^T += V^T P^T for tile t.  Key step ks: this lane's P^T registers hold
+  // keys 16 ks + 8 j + 4 hh + (0..3) in slots 4 j .. 4 j + 3 (j = 0, 1).  The
+  // feature blocks' MFMA chains are interleaved.
+  auto pv = [&](int t, const bf16x8* pb) {
+    const uint8_t* vl = lds + C::V_BASE + (t & 1) * C::TILE_BYTES;
+#pragma unroll
+    for (int ks = 0; ks < kBN / 16; ++ks)
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db) {
+        const uint8_t* vb = vl + (ks * 16) * C::ROW_BYTES + v_rd[db];
+        const u32x2 lo = lds_read_tr(reinterpret_cast<const uint16_t*>(vb));
+        const u32x2 hi = lds_read_tr(reinterpret_cast<const uint16_t*>(vb + 8 * C::ROW_BYTES));
+        const bf16x8 a = as_bf16x8(u32x4{lo[0], lo[1], hi[0], hi[1]});
+        oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[ks], oacc[db], 0, 0, 0);
+      }
+  };
+  // online-softmax step on the scores of one tile: new running max, rescale
+  // of the running sum and accumulator only when some row's max grew (rows
+  // whose max is unchanged keep a factor of exactly 1); returns m_new * c
+  auto update_max = [&](const f32x16* sc) -> float {
+    float mx = -INFINITY;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sc[kb][r]);
+    mx = xmax32(mx);
+    const float m_new = fmaxf(m_run, mx);
+    const float base = (m_new == -INFINITY) ? 0.f : m_new * p.c;
+    if (__ballot(m_new > m_run) != 0) {
+      const float alpha = (m_new > m_run) ? __builtin_amdgcn_exp2f(m_run * p.c - base) : 1.f;
+      l_run *= alpha;
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
+    }
+    m_run = m_new;
+    return base;
+  };
+  // probabilities exp2(s c - m c) of one tile, summed into l_run and packed to
+  // bf16 as the P^T operands: 16-key step ks uses registers 8 (ks%2) .. +7 of
+  // block ks/2
+  auto probs = [&](f32x16* sc, float base, bf16x8* pb) {
+    float ps = 0.f;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const float e = __builtin_amdgcn_exp2f(fmaf(sc[kb][r], p.c, -base));
+        sc[kb][r] = e;
+        ps += e;
+      }
+    l_run += ps;
+#pragma unroll
+    for (int ks = 0; ks < kBN / 16; ++ks)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) pb[ks][e] = (__bf16)sc[ks >> 1][(ks & 1) * 8 + e];
+  };
+
+  // ---- software pipeline over the unit's key tiles [t_lo, n_tiles).  On
+  // entry to step t the scores S_t are in sacc, K_{t+1} and V_t are in LDS.
+  // Step t issues the loads of K_{t+2} (into the buffer K_t used) and V_{t+1}
+  // (into the buffer V_{t-1} used), computes S_{t+1} = K_{t+1} Q^T, turns S_t
+  // into probabilities and accumulates V_t^T P_t^T; the next step starts after
+  // its loads landed and every wave passed the barrier.  The MFMAs of S_{t+1}
+  // are independent of the exp / sum / convert work on S_t, so the two
+  // interleave.  Buffer reuse: K_{t+2} overwrites K_t, last read by step
+  // t - 1 (or, for the first step, by the prologue, hence its barrier), and
+  // V_{t+1} overwrites V_{t-1}, last read by step t - 1.
+  f32x16 sacc[2];
+  if (t_lo < n_tiles) {
+    load_k(t_lo);
+    load_v(t_lo);
+    load_k(t_lo + 1);
+  }
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
+  if (t_lo < wave_tiles) qk(t_lo, sacc);
+  __syncthreads();  // every wave's reads of K_{t_lo} precede the first step's loads
 
   for (int t = t_lo; t < n_tiles; ++t) {
-    const int cur = (t - t_lo) & 1;
-    if (t + 1 < n_tiles) load_tile(t + 1, cur ^ 1);
-
-    if (t < wave_tiles) {
-      const uint8_t* kl = lds + C::K_BASE + cur * C::TILE_BYTES;
-      const uint8_t* vl = lds + C::V_BASE + cur * C::TILE_BYTES;
-      const int k0 = t * kBN;
-
-      // S^T block kb: keys k0 + 32 kb + (8 (r/4) + 4 hh + r%4), query my_q.
-      // The two blocks' MFMA chains are interleaved.
-      f32x16 sacc[2];
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) sacc[kb][r] = 0.f;
-#pragma unroll
-      for (int dk = 0; dk < D / 16; ++dk)
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
-          const bf16x8 a = *(const bf16x8*)(kl + kb * 32 * C::ROW_BYTES + k_rd[dk]);
-          sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[dk], sacc[kb], 0, 0, 0);
-        }
-      // keep four K operand reads in flight ahead of the MFMAs that use them:
-      // four LDS reads, then alternate one MFMA / one LDS read, then the last
-      // four MFMAs (measured best of 4, 8 and 16 reads ahead)
-      __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
-#pragma unroll
-      for (int i = 0; i < 2 * D / 16 - 4; ++i) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-      }
-      __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
-
-      const bool need_mask = (k0 + kBN > p.s) || (CAUSAL && k0 + kBN - 1 > q0);
-      if (need_mask) {
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int key = k0 + kb * 32 + 8 * (r >> 2) + 4 * hh + (r & 3);
-            if (key >= p.s || (CAUSAL && key > my_q)) sacc[kb][r] = -INFINITY;
-          }
-      }
-      float mx = -INFINITY;
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[kb][r]);
-      mx = xmax32(mx);
-      const float m_new = fmaxf(m_run, mx);
-      const float base = (m_new == -INFINITY) ? 0.f : m_new * p.c;
-      // rescale the running sum and accumulator only when some row's max grew;
-      // rows whose max is unchanged keep a factor of exactly 1
-      if (__ballot(m_new > m_run) != 0) {
-        const float alpha = (m_new > m_run) ? __builtin_amdgcn_exp2f(m_run * p.c - base) : 1.f;
-        l_run *= alpha;
-#pragma unroll
-        for (int db = 0; db < D / 32; ++db)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
-      }
-      m_run = m_new;
-      float ps = 0.f;
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const float e = __builtin_amdgcn_exp2f(fmaf(sacc[kb][r], p.c, -base));
-          sacc[kb][r] = e;
-          ps += e;
-        }
-      l_run += ps;
-
-      // P^T operands: 16-key step ks uses registers 8 (ks%2) .. +7 of block ks/2
+    const int k0 = t * kBN;
+    const bool need_mask = (k0 + kBN > p.s) || (CAUSAL && k0 + kBN - 1 > q0);
+    if (t < wave_tiles && !need_mask && t + 1 < wave_tiles) {
+      // steady state: one basic block after the rescale test
+      const float base = update_max(sacc);
+      f32x16 snext[2];
+      qk(t + 1, snext);
       bf16x8 pb[kBN / 16];
+      probs(sacc, base, pb);
+      load_k(t + 2);
+      load_v(t + 1);
+      pv(t, pb);
+      sacc[0] = snext[0];
+      sacc[1] = snext[1];
+    } else {
+      load_k(t + 2);
+      load_v(t + 1);
+      if (t < wave_tiles) {
+        if (need_mask) {
 #pragma unroll
-      for (int ks = 0; ks < kBN / 16; ++ks)
+          for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-        for (int e = 0; e < 8; ++e) pb[ks][e] = (__bf16)sacc[ks >> 1][(ks & 1) * 8 + e];
-
-      // O^T += V^T P^T.  Key step ks: this lane's P^T registers hold keys
-      // 16 ks + 8 j + 4 hh + (0..3) in slots 4 j .. 4 j + 3 (j = 0, 1).  The
-      // feature blocks' MFMA chains are interleaved.
-#pragma unroll
-      for (int ks = 0; ks < kBN / 16; ++ks)
-#pragma unroll
-        for (int db = 0; db < D / 32; ++db) {
-          const uint8_t* vb = vl + (ks * 16) * C::ROW_BYTES + v_rd[db];
-          const u32x2 lo = lds_read_tr(reinterpret_cast<const uint16_t*>(vb));
-          const u32x2 hi = lds_read_tr(reinterpret_cast<const uint16_t*>(vb + 8 * C::ROW_BYTES));
-          const bf16x8 a = as_bf16x8(u32x4{lo[0], lo[1], hi[0], hi[1]});
-          oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[ks], oacc[db], 0, 0, 0);
+            for (int r = 0; r < 16; ++r) {
+              const int key = k0 + kb * 32 + 8 * (r >> 2) + 4 * hh + (r & 3);
+              if (key >= p.s || (CAUSAL && key > my_q)) sacc[kb][r] = -INFINITY;
+            }
         }
+        const float base = update_max(sacc);
+        bf16x8 pb[kBN / 16];
+        probs(sacc, base, pb);
+        if (t + 1 < wave_tiles) qk(t + 1, sacc);
+        pv(t, pb);
+      }
     }
-
-    // the next tile's direct loads must have landed before anyone reads it
+    // this step's loads must have landed before anyone reads them
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
   }
@@ -431,19 +469,19 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(Params p) {
   store_output<D>(p, oacc, m_run, l_run, be, head, my_q, hh);
 }
 
-// Workgroups of this kernel resident at once on the current device (CUs x
-// workgroups per CU, set by its LDS and VGPR use), or 0 if unknown.
-int64_t resident_slots(int64_t d) {
+// Workgroups of this kernel resident at once on the current device: one per
+// CU (8 waves of up to 256 VGPRs fill a CU's register file), or 0 if unknown.
+int64_t resident_slots() {
   int dev = 0, cus = 0;
   if (hipGetDevice(&dev) != hipSuccess ||
       hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
     return 0;
-  return (int64_t)cus * (d == 128 ? 2 : 3);
+  return (int64_t)cus;
 }
 
 int64_t count_items(const AttnArgs& a) {
   const int64_t G = a.hp / a.hkvp;
-  const int64_t QH = (G % 4 == 0) ? 4 : (G % 2 == 0) ? 2 : 1;
+  const int64_t QH = (G % 8 == 0) ? 8 : (G % 4 == 0) ? 4 : (G % 2 == 0) ? 2 : 1;
   const int64_t QB = kQW * (kWaves / QH);
   return (a.s + QB - 1) / QB * a.b * a.hkvp * (G / QH);
 }
@@ -453,7 +491,7 @@ int64_t count_items(const AttnArgs& a) {
 // time) is split into two halves per item.  0 when no split is used.
 int64_t attn_bf16_workspace_bytes(const AttnArgs& a) {
   const int64_t items = count_items(a);
-  const int64_t slots = resident_slots(a.d);
+  const int64_t slots = resident_slots();
   if (!a.causal || slots <= 0 || items >= 2 * slots) return 0;
   const int64_t part = (int64_t)kWaves * 64 * (a.d / 2 + 2) * 4;
   return items * 2 * part;
@@ -499,7 +537,7 @@ hipError_t launch_d(const AttnArgs& a, hipStream_t stream) {
   p.hp = (int)a.hp;
   p.hkvp = (int)a.hkvp;
   p.G = (int)(a.hp / a.hkvp);
-  p.QH = (p.G % 4 == 0) ? 4 : (p.G % 2 == 0) ? 2 : 1;
+  p.QH = (p.G % 8 == 0) ? 8 : (p.G % 4 == 0) ? 4 : (p.G % 2 == 0) ? 2 : 1;
   p.QB = kQW * (kWaves / p.QH);
   p.n_qblk = (p.s + p.QB - 1) / p.QB;
   p.nsub = p.G / p.QH;
@@ -511,9 +549,6 @@ hipError_t launch_d(const AttnArgs& a, hipStream_t stream) {
   const int64_t items = (int64_t)p.n_qblk * p.b * p.hkvp * p.nsub;
   if (items <= 0) return hipSuccess;
   if (items > 0x7FFFFFFF) return hipErrorInvalidValue;
-  // pairing applies when the whole first resident wave is present
-  const int64_t slots = resident_slots(D);
-  p.slots = (slots > 0 && items >= slots && (slots % 2) == 0) ? (int)slots : 0;
   // split halves (see attn_bf16_workspace_bytes) when the caller gave room
   const int64_t ws_need = attn_bf16_workspace_bytes(a);
   const int nsplit = (ws_need > 0 && a.workspace && a.workspace_bytes >= ws_need) ? 2 : 1;
