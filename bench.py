@@ -33,8 +33,10 @@ PROFILE_DIR = os.path.join(ROOT, "profiles")
 def parse_args():
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=3)
+    # the 32k share's step is under a millisecond: a few hundred warm-up steps
+    # let the GPU clock settle before the timed ones
+    ap.add_argument("--steps", type=int, default=500)
+    ap.add_argument("--warmup", type=int, default=200)
     ap.add_argument("--workload", default="gpt1.2b-32k")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="wall-time budget of the oracle's cpu_baseline sample")
