@@ -41,6 +41,10 @@ def parse_args():
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="wall-time budget of the oracle's cpu_baseline sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--inputs", choices=("normal", "constant"), default="normal",
+                    help="normal: the seeded N(0,1) tensors (the workload); constant: the "
+                         "same work on constant tensors, a diagnostic of how much the GPU "
+                         "clock depends on the data the matrix cores see (not a result)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain device-to-device copy of known size (for scaling "
                          "rocprofv3 FETCH_SIZE/WRITE_SIZE to bytes) and exit")
@@ -151,6 +155,12 @@ def main():
     xq_h = synth.tensor(100 * w.c + 1, (sl, w.b, w.h, w.d), w.dtype)
     xk_h = synth.tensor(100 * w.c + 2, (sl, w.b, w.h_kv, w.d), w.dtype)
     xv_h = synth.tensor(100 * w.c + 3, (sl, w.b, w.h_kv, w.d), w.dtype)
+    if args.inputs == "constant":
+        for a, val in ((xq_h, 0.5), (xk_h, 0.25), (xv_h, 1.0)):
+            if a.dtype == np.uint16:
+                a[...] = synth.f32_to_bf16_bits(np.full(1, val, dtype=np.float32))[0]
+            else:
+                a[...] = val
     xq, xk, xv = upload(xq_h), upload(xk_h), upload(xv_h)
     yq = torch.empty((w.P, sl, w.b, hp, w.d), dtype=tdt, device=dev)
     yk = torch.empty((w.P, sl, w.b, hkvp, w.d), dtype=tdt, device=dev)
@@ -237,7 +247,8 @@ def main():
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": w.dtype,
-        "data": "synthetic (seeded N(0,1), SplitMix64 + Box-Muller)",
+        "data": ("synthetic (seeded N(0,1), SplitMix64 + Box-Muller)" if args.inputs == "normal"
+                 else "constant tensors (diagnostic, not the workload)"),
         "config": {"workload": w.name, "P": w.P, "s": w.s, "b": w.b, "h": w.h, "h_kv": w.h_kv,
                    "d_h": w.d, "causal": w.causal, "share": f"[{w.s},{w.b},{hp},{w.d}]"},
         "attn": {"ms": round(attn_ms, 4), "tflops": round(attn_tflops, 2),

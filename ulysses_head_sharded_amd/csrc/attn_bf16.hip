@@ -285,19 +285,19 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bf16_kernel(Params p) {
   float m_run = -INFINITY;  // running max of raw scores (q.k)
   float l_run = 0.f;        // this lane's share of the running sum
 
-  // K tile t goes to K buffer t % 2 and V tile t to V buffer t % 2.  Past
-  // the unit's last tile the source is clamped to it while the buffer stays
-  // that of t, which no later step reads.
+  // K tile t goes to K buffer (t - t_lo) % 2 and V tile t to V buffer
+  // (t - t_lo) % 2.  Past the unit's last tile the source is clamped to it
+  // while the buffer stays that of t, which no later step reads.
   const int t_last = n_tiles - 1;
   auto load_k = [&](int t) {
     const int koff = min(t, t_last) * kBN * p.kv_tok_bytes;
-    uint8_t* dst = lds + C::K_BASE + (t & 1) * C::TILE_BYTES + wave * C::LOADS * 1024;
+    uint8_t* dst = lds + C::K_BASE + ((t - t_lo) & 1) * C::TILE_BYTES + wave * C::LOADS * 1024;
 #pragma unroll
     for (int i = 0; i < C::LOADS; ++i) load_lds16(rk, dst + i * 1024, k_src[i] + koff);
   };
   auto load_v = [&](int t) {
     const int koff = min(t, t_last) * kBN * p.kv_tok_bytes;
-    uint8_t* dst = lds + C::V_BASE + (t & 1) * C::TILE_BYTES + wave * C::LOADS * 1024;
+    uint8_t* dst = lds + C::V_BASE + ((t - t_lo) & 1) * C::TILE_BYTES + wave * C::LOADS * 1024;
 #pragma unroll
     for (int i = 0; i < C::LOADS; ++i) load_lds16(rv, dst + i * 1024, v_src[i] + koff);
   };
@@ -322,7 +322,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bf16_kernel(Params p) {
   // S^T block kb of tile t: keys 64 t + 32 kb + (8 (r/4) + 4 hh + r%4), query
   // my_q.  The two blocks' MFMA chains are interleaved.
   auto qk = [&](int t, f32x16* sc) {
-    const uint8_t* kl = lds + C::K_BASE + (t & 1) * C::TILE_BYTES;
+    const uint8_t* kl = lds + C::K_BASE + ((t - t_lo) & 1) * C::TILE_BYTES;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
@@ -339,7 +339,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bf16_kernel(Params p) {
   // keys 16 ks + 8 j + 4 hh + (0..3) in slots 4 j .. 4 j + 3 (j = 0, 1).  The
   // feature blocks' MFMA chains are interleaved.
   auto pv = [&](int t, const bf16x8* pb) {
-    const uint8_t* vl = lds + C::V_BASE + (t & 1) * C::TILE_BYTES;
+    const uint8_t* vl = lds + C::V_BASE + ((t - t_lo) & 1) * C::TILE_BYTES;
 #pragma unroll
     for (int ks = 0; ks < kBN / 16; ++ks)
 #pragma unroll
@@ -404,32 +404,19 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bf16_kernel(Params p) {
   // interleave.  Buffer reuse: K_{t+2} overwrites K_t, last read by step
   // t - 1 (or, for the first step, by the prologue, hence its barrier), and
   // V_{t+1} overwrites V_{t-1}, last read by step t - 1.
-  f32x16 sacc[2];
-  if (t_lo < n_tiles) {
-    load_k(t_lo);
-    load_v(t_lo);
-    load_k(t_lo + 1);
-  }
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  __syncthreads();
-  if (t_lo < wave_tiles) qk(t_lo, sacc);
-  __syncthreads();  // every wave's reads of K_{t_lo} precede the first step's loads
-
-  for (int t = t_lo; t < n_tiles; ++t) {
+  // one step; cur holds S_t on entry, nxt receives S_{t+1}
+  auto step = [&](int t, f32x16* cur, f32x16* nxt) {
     const int k0 = t * kBN;
     const bool need_mask = (k0 + kBN > p.s) || (CAUSAL && k0 + kBN - 1 > q0);
     if (t < wave_tiles && !need_mask && t + 1 < wave_tiles) {
       // steady state: one basic block after the rescale test
-      const float base = update_max(sacc);
-      f32x16 snext[2];
-      qk(t + 1, snext);
+      const float base = update_max(cur);
+      qk(t + 1, nxt);
       bf16x8 pb[kBN / 16];
-      probs(sacc, base, pb);
+      probs(cur, base, pb);
       load_k(t + 2);
       load_v(t + 1);
       pv(t, pb);
-      sacc[0] = snext[0];
-      sacc[1] = snext[1];
     } else {
       load_k(t + 2);
       load_v(t + 1);
@@ -440,19 +427,37 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bf16_kernel(Params p) {
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
               const int key = k0 + kb * 32 + 8 * (r >> 2) + 4 * hh + (r & 3);
-              if (key >= p.s || (CAUSAL && key > my_q)) sacc[kb][r] = -INFINITY;
+              if (key >= p.s || (CAUSAL && key > my_q)) cur[kb][r] = -INFINITY;
             }
         }
-        const float base = update_max(sacc);
+        const float base = update_max(cur);
         bf16x8 pb[kBN / 16];
-        probs(sacc, base, pb);
-        if (t + 1 < wave_tiles) qk(t + 1, sacc);
+        probs(cur, base, pb);
+        if (t + 1 < wave_tiles) qk(t + 1, nxt);
         pv(t, pb);
       }
     }
     // this step's loads must have landed before anyone reads them
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
+  };
+
+  f32x16 sa[2], sb[2];
+  if (t_lo < n_tiles) {
+    load_k(t_lo);
+    load_v(t_lo);
+    load_k(t_lo + 1);
+  }
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+  if (t_lo < wave_tiles) qk(t_lo, sa);
+  __syncthreads();  // every wave's reads of K_{t_lo} precede the first step's loads
+  // unrolled by two so the score registers swap roles instead of being
+  // copied, and every buffer parity is a compile-time constant
+  for (int i = 0; t_lo + 2 * i < n_tiles; ++i) {
+    const int t = t_lo + 2 * i;
+    step(t, sa, sb);
+    if (t + 1 < n_tiles) step(t + 1, sb, sa);
   }
 
   if (p.nsplit == 2) {
