@@ -67,6 +67,14 @@ def _bind(lib: ctypes.CDLL) -> ctypes.CDLL:
                                   _c_i64, _c_i64, _c_i64, _c_i64, ctypes.c_int,
                                   ctypes.c_int, ctypes.c_int]
     lib.orc_attn_rows.restype = ctypes.c_int
+    lib.orc_attn_bwd.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _c_i64, _c_i64, _c_i64,
+                                 _c_i64, _c_i64, _c_i64, ctypes.c_int, ctypes.c_int,
+                                 ctypes.c_int]
+    lib.orc_attn_bwd.restype = ctypes.c_int
+    lib.orc_attn_bwd_rows.argtypes = [_vp, _vp, _vp, _vp, _vp, _c_i64, _vp, _c_i64, _vp, _vp,
+                                      _vp, _c_i64, _c_i64, _c_i64, _c_i64, _c_i64, _c_i64,
+                                      ctypes.c_int, ctypes.c_int, ctypes.c_int]
+    lib.orc_attn_bwd_rows.restype = ctypes.c_int
     return lib
 
 
@@ -168,3 +176,43 @@ def attn_rows(q, k, v, rows, s, b, h, h_kv, d, P, causal, nthreads=None, lib=Non
     _check(rc, "attn_rows")
     return o, lse
 
+
+
+# ----------------------------------------------------------------------------- backward
+def attn_bwd(q, k, v, dout, s, b, h, h_kv, d, P, causal, nthreads=None, lib=None):
+    """Gradients of one rank's share: q, dout [s,b,h/P,d], k/v [s,b,h_kv/P,d] (float32 or
+    bf16 bits as uint16).  Returns (dq [s,b,h/P,d], dk, dv [s,b,h_kv/P,d]) float64."""
+    lib = lib or load()
+    q, k, v, dout = _contig(q), _contig(k), _contig(v), _contig(dout)
+    dt = _dtype_code(q)
+    assert _dtype_code(k) == dt and _dtype_code(v) == dt and _dtype_code(dout) == dt
+    hp, hkvp = h // P, h_kv // P
+    dq = np.empty((s, b, hp, d), dtype=np.float64)
+    dk = np.empty((s, b, hkvp, d), dtype=np.float64)
+    dv = np.empty((s, b, hkvp, d), dtype=np.float64)
+    rc = lib.orc_attn_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(dout), _ptr(dq), _ptr(dk), _ptr(dv),
+                          s, b, h, h_kv, d, P, int(bool(causal)), dt,
+                          nthreads or default_threads())
+    _check(rc, "attn_bwd")
+    return dq, dk, dv
+
+
+def attn_bwd_rows(q, k, v, dout, qrows, krows, s, b, h, h_kv, d, P, causal, nthreads=None,
+                  lib=None):
+    """Gradients at listed places only: qrows int64 [n,3] of (beta, local head, t) -> dq [n,d];
+    krows int64 [m,3] of (beta, local KV head, j) -> dk, dv [m,d].  float64."""
+    lib = lib or load()
+    q, k, v, dout = _contig(q), _contig(k), _contig(v), _contig(dout)
+    qrows = np.ascontiguousarray(qrows, dtype=np.int64).reshape(-1, 3)
+    krows = np.ascontiguousarray(krows, dtype=np.int64).reshape(-1, 3)
+    dt = _dtype_code(q)
+    assert _dtype_code(k) == dt and _dtype_code(v) == dt and _dtype_code(dout) == dt
+    n, m = qrows.shape[0], krows.shape[0]
+    dq = np.empty((max(n, 1), d), dtype=np.float64)
+    dk = np.empty((max(m, 1), d), dtype=np.float64)
+    dv = np.empty((max(m, 1), d), dtype=np.float64)
+    rc = lib.orc_attn_bwd_rows(_ptr(q), _ptr(k), _ptr(v), _ptr(dout), _ptr(qrows), n,
+                               _ptr(krows), m, _ptr(dq), _ptr(dk), _ptr(dv), s, b, h, h_kv, d,
+                               P, int(bool(causal)), dt, nthreads or default_threads())
+    _check(rc, "attn_bwd_rows")
+    return dq[:n], dk[:m], dv[:m]

@@ -338,3 +338,293 @@ int orc_attn_rows(const void *q, const void *k, const void *v, const int64_t *ro
   return run_attention(q, k, v, o, lse, s, b, h / P, h_kv / P, d, causal, dtype, rows, nrows,
                        nthreads);
 }
+
+/* ------------------------------------------------------------------------ */
+/* Attention backward on one rank's share                                   */
+/* ------------------------------------------------------------------------ */
+
+/*
+ * [ATLAS] §5: both all-to-alls are linear, so their backward is the same
+ * exchange with the split and concatenation axes swapped, and the local
+ * attention's backward is the ordinary attention backward.  The pages print
+ * no formula for the latter; it is the gradient of the forward definition
+ * (attn_row above).  For one query row with visible keys J, scores
+ * S_j = q.k_j / sqrt(d), P = softmax(S) and o = sum_j P_j v_j, a cotangent
+ * dout on o gives, by the chain rule through the softmax Jacobian
+ * diag(P) - P P^T:
+ *   dv_j += P_j dout
+ *   dP_j  = dout . v_j
+ *   D     = sum_j P_j dP_j            (= dout . o)
+ *   dS_j  = P_j (dP_j - D)
+ *   dq    = sum_j dS_j k_j / sqrt(d)
+ *   dk_j += dS_j q / sqrt(d)
+ * dk and dv of a KV head sum the contributions of every query head of its
+ * GQA group and every query row that sees the key ([SPCP] notes that one
+ * K_j, V_j serving many queries receives the sum of their gradients).
+ */
+typedef struct {
+  const double *q, *k, *v, *dout; /* q, dout [s,b,nq,d]; k, v [s,b,nkv,d] */
+  int64_t s, b, nq, nkv, d;
+  int causal;
+  double *dq, *dk, *dv; /* dq [s,b,nq,d]; dk, dv [s,b,nkv,d] */
+  int64_t first, last;  /* range of (beta, kv head) pairs of this thread */
+  int status;
+} bwd_job;
+
+/* Softmax row of query (be, i, t): fills p[0..nkeys) and returns nkeys. */
+static int64_t softmax_row(const double *q, const double *k, int64_t s, int64_t b, int64_t nq,
+                           int64_t nkv, int64_t d, int causal, int64_t be, int64_t i, int64_t t,
+                           double *p) {
+  const int64_t g = i / (nq / nkv);
+  const int64_t nkeys = causal ? t + 1 : s;
+  const double scale = 1.0 / sqrt((double)d);
+  const double *qrow = q + ((t * b + be) * nq + i) * d;
+  double m = -INFINITY;
+  for (int64_t j = 0; j < nkeys; ++j) {
+    const double *krow = k + ((j * b + be) * nkv + g) * d;
+    double acc = 0.0;
+    for (int64_t e = 0; e < d; ++e) acc += qrow[e] * krow[e];
+    p[j] = acc * scale;
+    if (p[j] > m) m = p[j];
+  }
+  double l = 0.0;
+  for (int64_t j = 0; j < nkeys; ++j) {
+    p[j] = exp(p[j] - m);
+    l += p[j];
+  }
+  for (int64_t j = 0; j < nkeys; ++j) p[j] /= l;
+  return nkeys;
+}
+
+/* dP_j = dout_t . v_j for every visible key, and D = sum_j P_j dP_j. */
+static double dp_row(const double *v, const double *dout, int64_t b, int64_t nq, int64_t nkv,
+                     int64_t d, int64_t be, int64_t i, int64_t t, const double *p, int64_t nkeys,
+                     double *dp) {
+  const int64_t g = i / (nq / nkv);
+  const double *drow = dout + ((t * b + be) * nq + i) * d;
+  double D = 0.0;
+  for (int64_t j = 0; j < nkeys; ++j) {
+    const double *vrow = v + ((j * b + be) * nkv + g) * d;
+    double acc = 0.0;
+    for (int64_t e = 0; e < d; ++e) acc += drow[e] * vrow[e];
+    dp[j] = acc;
+    D += p[j] * acc;
+  }
+  return D;
+}
+
+static void *bwd_worker(void *arg) {
+  bwd_job *J = (bwd_job *)arg;
+  const int64_t s = J->s, b = J->b, nq = J->nq, nkv = J->nkv, d = J->d, G = nq / nkv;
+  const double scale = 1.0 / sqrt((double)d);
+  double *p = (double *)malloc((size_t)s * sizeof(double));
+  double *dp = (double *)malloc((size_t)s * sizeof(double));
+  if (!p || !dp) {
+    free(p); free(dp);
+    J->status = ORC_ENOMEM;
+    return NULL;
+  }
+  for (int64_t w = J->first; w < J->last; ++w) {
+    const int64_t be = w / nkv, g = w % nkv;
+    for (int64_t i = g * G; i < (g + 1) * G; ++i) {
+      for (int64_t t = 0; t < s; ++t) {
+        const int64_t nkeys = softmax_row(J->q, J->k, s, b, nq, nkv, d, J->causal, be, i, t, p);
+        const double D = dp_row(J->v, J->dout, b, nq, nkv, d, be, i, t, p, nkeys, dp);
+        const double *qrow = J->q + ((t * b + be) * nq + i) * d;
+        const double *drow = J->dout + ((t * b + be) * nq + i) * d;
+        double *dqrow = J->dq + ((t * b + be) * nq + i) * d;
+        for (int64_t e = 0; e < d; ++e) dqrow[e] = 0.0;
+        for (int64_t j = 0; j < nkeys; ++j) {
+          const double ds = p[j] * (dp[j] - D);
+          const double *krow = J->k + ((j * b + be) * nkv + g) * d;
+          double *dkrow = J->dk + ((j * b + be) * nkv + g) * d;
+          double *dvrow = J->dv + ((j * b + be) * nkv + g) * d;
+          for (int64_t e = 0; e < d; ++e) {
+            dqrow[e] += ds * krow[e] * scale;
+            dkrow[e] += ds * qrow[e] * scale;
+            dvrow[e] += p[j] * drow[e];
+          }
+        }
+      }
+    }
+  }
+  free(p); free(dp);
+  J->status = ORC_OK;
+  return NULL;
+}
+
+/*
+ * Backward of the head-sharded attention on one rank's share.
+ *   q, dout [s, b, h/P, d]; k, v [s, b, h_kv/P, d] (dtype 0 fp32, 1 bf16 bits)
+ *   dq [s, b, h/P, d], dk, dv [s, b, h_kv/P, d] fp64
+ */
+int orc_attn_bwd(const void *q, const void *k, const void *v, const void *dout, double *dq,
+                 double *dk, double *dv, int64_t s, int64_t b, int64_t h, int64_t h_kv, int64_t d,
+                 int64_t P, int causal, int dtype, int nthreads) {
+  if (P <= 0 || h % P != 0 || h_kv <= 0 || h_kv % P != 0) return ORC_EARG;
+  const int64_t nq = h / P, nkv = h_kv / P;
+  if (s <= 0 || b <= 0 || nq <= 0 || nkv <= 0 || d <= 0) return ORC_EARG;
+  if (nq % nkv != 0 || (dtype != 0 && dtype != 1)) return ORC_EARG;
+  if (!q || !k || !v || !dout || !dq || !dk || !dv) return ORC_EARG;
+  if (nthreads < 1) nthreads = 1;
+  double *qd = widen_all(q, dtype, s * b * nq * d);
+  double *kd = widen_all(k, dtype, s * b * nkv * d);
+  double *vd = widen_all(v, dtype, s * b * nkv * d);
+  double *dd = widen_all(dout, dtype, s * b * nq * d);
+  bwd_job *jobs = (bwd_job *)calloc((size_t)nthreads, sizeof(bwd_job));
+  pthread_t *tid = (pthread_t *)calloc((size_t)nthreads, sizeof(pthread_t));
+  int rc = ORC_OK;
+  if (!qd || !kd || !vd || !dd || !jobs || !tid) {
+    rc = ORC_ENOMEM;
+    goto done;
+  }
+  for (int64_t n = 0; n < s * b * nkv * d; ++n) dk[n] = dv[n] = 0.0;
+  const int64_t pairs = b * nkv;
+  for (int n = 0; n < nthreads; ++n) {
+    bwd_job *J = &jobs[n];
+    J->q = qd; J->k = kd; J->v = vd; J->dout = dd;
+    J->s = s; J->b = b; J->nq = nq; J->nkv = nkv; J->d = d;
+    J->causal = causal;
+    J->dq = dq; J->dk = dk; J->dv = dv;
+    J->first = pairs * n / nthreads;
+    J->last = pairs * (n + 1) / nthreads;
+    J->status = ORC_ENOMEM;
+  }
+  if (nthreads == 1) {
+    bwd_worker(&jobs[0]);
+  } else {
+    for (int n = 0; n < nthreads; ++n) pthread_create(&tid[n], NULL, bwd_worker, &jobs[n]);
+    for (int n = 0; n < nthreads; ++n) pthread_join(tid[n], NULL);
+  }
+  for (int n = 0; n < nthreads; ++n)
+    if (jobs[n].status != ORC_OK) rc = jobs[n].status;
+done:
+  free(qd); free(kd); free(vd); free(dd); free(jobs); free(tid);
+  return rc;
+}
+
+/*
+ * The same gradients evaluated only where listed: qrows holds nqr triples
+ * (beta, local query head i, query t) whose dq rows go to dq [nqr, d]; krows
+ * holds nkr triples (beta, local KV head g, key j) whose dk and dv rows go
+ * to dk, dv [nkr, d].  A key's gradients visit every query row that sees it
+ * (t >= j when causal), each with its whole softmax row, so late keys of a
+ * causal share are cheap and early ones cost a full pass.  Single-threaded
+ * per listed item, threads over items.
+ */
+typedef struct {
+  const double *q, *k, *v, *dout;
+  int64_t s, b, nq, nkv, d;
+  int causal;
+  const int64_t *qrows, *krows;
+  int64_t nqr, nkr;
+  double *dq, *dk, *dv;
+  int64_t first, last; /* items [0, nqr) are query rows, [nqr, nqr + nkr) keys */
+  int status;
+} bwd_rows_job;
+
+static void *bwd_rows_worker(void *arg) {
+  bwd_rows_job *J = (bwd_rows_job *)arg;
+  const int64_t s = J->s, b = J->b, nq = J->nq, nkv = J->nkv, d = J->d, G = nq / nkv;
+  const double scale = 1.0 / sqrt((double)d);
+  double *p = (double *)malloc((size_t)s * sizeof(double));
+  double *dp = (double *)malloc((size_t)s * sizeof(double));
+  if (!p || !dp) {
+    free(p); free(dp);
+    J->status = ORC_ENOMEM;
+    return NULL;
+  }
+  for (int64_t w = J->first; w < J->last; ++w) {
+    if (w < J->nqr) {
+      const int64_t be = J->qrows[3 * w], i = J->qrows[3 * w + 1], t = J->qrows[3 * w + 2];
+      const int64_t g = i / G;
+      const int64_t nkeys = softmax_row(J->q, J->k, s, b, nq, nkv, d, J->causal, be, i, t, p);
+      const double D = dp_row(J->v, J->dout, b, nq, nkv, d, be, i, t, p, nkeys, dp);
+      double *dqrow = J->dq + w * d;
+      for (int64_t e = 0; e < d; ++e) dqrow[e] = 0.0;
+      for (int64_t j = 0; j < nkeys; ++j) {
+        const double ds = p[j] * (dp[j] - D);
+        const double *krow = J->k + ((j * b + be) * nkv + g) * d;
+        for (int64_t e = 0; e < d; ++e) dqrow[e] += ds * krow[e] * scale;
+      }
+    } else {
+      const int64_t u = w - J->nqr;
+      const int64_t be = J->krows[3 * u], g = J->krows[3 * u + 1], j = J->krows[3 * u + 2];
+      double *dkrow = J->dk + u * d;
+      double *dvrow = J->dv + u * d;
+      for (int64_t e = 0; e < d; ++e) dkrow[e] = dvrow[e] = 0.0;
+      for (int64_t i = g * G; i < (g + 1) * G; ++i) {
+        for (int64_t t = J->causal ? j : 0; t < s; ++t) {
+          const int64_t nkeys = softmax_row(J->q, J->k, s, b, nq, nkv, d, J->causal, be, i, t, p);
+          const double D = dp_row(J->v, J->dout, b, nq, nkv, d, be, i, t, p, nkeys, dp);
+          const double ds = p[j] * (dp[j] - D);
+          const double *qrow = J->q + ((t * b + be) * nq + i) * d;
+          const double *drow = J->dout + ((t * b + be) * nq + i) * d;
+          for (int64_t e = 0; e < d; ++e) {
+            dkrow[e] += ds * qrow[e] * scale;
+            dvrow[e] += p[j] * drow[e];
+          }
+        }
+      }
+    }
+  }
+  free(p); free(dp);
+  J->status = ORC_OK;
+  return NULL;
+}
+
+int orc_attn_bwd_rows(const void *q, const void *k, const void *v, const void *dout,
+                      const int64_t *qrows, int64_t nqr, const int64_t *krows, int64_t nkr,
+                      double *dq, double *dk, double *dv, int64_t s, int64_t b, int64_t h,
+                      int64_t h_kv, int64_t d, int64_t P, int causal, int dtype, int nthreads) {
+  if (P <= 0 || h % P != 0 || h_kv <= 0 || h_kv % P != 0 || nqr < 0 || nkr < 0) return ORC_EARG;
+  const int64_t nq = h / P, nkv = h_kv / P;
+  if (s <= 0 || b <= 0 || nq <= 0 || nkv <= 0 || d <= 0) return ORC_EARG;
+  if (nq % nkv != 0 || (dtype != 0 && dtype != 1)) return ORC_EARG;
+  if (!q || !k || !v || !dout) return ORC_EARG;
+  if ((nqr > 0 && (!qrows || !dq)) || (nkr > 0 && (!krows || !dk || !dv))) return ORC_EARG;
+  for (int64_t w = 0; w < nqr; ++w)
+    if (qrows[3 * w] < 0 || qrows[3 * w] >= b || qrows[3 * w + 1] < 0 ||
+        qrows[3 * w + 1] >= nq || qrows[3 * w + 2] < 0 || qrows[3 * w + 2] >= s)
+      return ORC_EARG;
+  for (int64_t u = 0; u < nkr; ++u)
+    if (krows[3 * u] < 0 || krows[3 * u] >= b || krows[3 * u + 1] < 0 ||
+        krows[3 * u + 1] >= nkv || krows[3 * u + 2] < 0 || krows[3 * u + 2] >= s)
+      return ORC_EARG;
+  if (nqr + nkr == 0) return ORC_OK;
+  if (nthreads < 1) nthreads = 1;
+  double *qd = widen_all(q, dtype, s * b * nq * d);
+  double *kd = widen_all(k, dtype, s * b * nkv * d);
+  double *vd = widen_all(v, dtype, s * b * nkv * d);
+  double *dd = widen_all(dout, dtype, s * b * nq * d);
+  bwd_rows_job *jobs = (bwd_rows_job *)calloc((size_t)nthreads, sizeof(bwd_rows_job));
+  pthread_t *tid = (pthread_t *)calloc((size_t)nthreads, sizeof(pthread_t));
+  int rc = ORC_OK;
+  if (!qd || !kd || !vd || !dd || !jobs || !tid) {
+    rc = ORC_ENOMEM;
+    goto done;
+  }
+  const int64_t total = nqr + nkr;
+  for (int n = 0; n < nthreads; ++n) {
+    bwd_rows_job *J = &jobs[n];
+    J->q = qd; J->k = kd; J->v = vd; J->dout = dd;
+    J->s = s; J->b = b; J->nq = nq; J->nkv = nkv; J->d = d;
+    J->causal = causal;
+    J->qrows = qrows; J->krows = krows; J->nqr = nqr; J->nkr = nkr;
+    J->dq = dq; J->dk = dk; J->dv = dv;
+    J->first = total * n / nthreads;
+    J->last = total * (n + 1) / nthreads;
+    J->status = ORC_ENOMEM;
+  }
+  if (nthreads == 1) {
+    bwd_rows_worker(&jobs[0]);
+  } else {
+    for (int n = 0; n < nthreads; ++n) pthread_create(&tid[n], NULL, bwd_rows_worker, &jobs[n]);
+    for (int n = 0; n < nthreads; ++n) pthread_join(tid[n], NULL);
+  }
+  for (int n = 0; n < nthreads; ++n)
+    if (jobs[n].status != ORC_OK) rc = jobs[n].status;
+done:
+  free(qd); free(kd); free(vd); free(dd); free(jobs); free(tid);
+  return rc;
+}

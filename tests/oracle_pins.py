@@ -339,9 +339,148 @@ def pin_rows_match_full(lib):
         assert np.array_equal(lrows, lse[rows[:, 0], rows[:, 1], rows[:, 2]])
 
 
+# ---------------------------------------------------------------------------- backward pins
+def torch_attention_grads(q, k, v, dout, causal):
+    """Independent reference for the backward: torch float64 autograd through
+    scaled_dot_product_attention.  Shapes as torch_attention; returns
+    (dq [s,b,nq,d], dk, dv [s,b,nkv,d]) with KV gradients summed over each
+    contiguous GQA group."""
+    s, b, nq, d = q.shape
+    nkv = k.shape[2]
+    G = nq // nkv
+    to_t = lambda a: torch.from_numpy(np.ascontiguousarray(a.transpose(1, 2, 0, 3)))  # noqa: E731
+    qt = to_t(q).requires_grad_(True)
+    kt = to_t(k).requires_grad_(True)
+    vt = to_t(v).requires_grad_(True)
+    o = torch.nn.functional.scaled_dot_product_attention(
+        qt, kt.repeat_interleave(G, 1), vt.repeat_interleave(G, 1), is_causal=bool(causal))
+    o.backward(to_t(dout))
+    back = lambda t: t.grad.numpy().transpose(2, 0, 1, 3)  # noqa: E731
+    return back(qt), back(kt), back(vt)
+
+
+def _rand_bwd(seed, s, b, nq, nkv, d, dtype):
+    q, k, v = _rand_share(seed, s, b, nq, nkv, d, dtype)
+    dout = synth.tensor(seed + 4, (s, b, nq, d), dtype)
+    return q, k, v, dout
+
+
+def pin_bwd_finite_differences(lib):
+    """Every gradient element against a central difference of
+    L = sum(dout * attn(q, k, v)) evaluated with the (pinned) forward oracle:
+    the derivative of the definition, computed without the backward formulas.
+    fp32 inputs; the step is taken between fp32 neighbours, so the forward sees
+    the exact perturbed values."""
+    for (s, b, nq, nkv, d, causal) in ((5, 1, 2, 1, 4, True), (4, 2, 2, 2, 3, False)):
+        q, k, v, dout = _rand_bwd(1300 + s, s, b, nq, nkv, d, "f32")
+        dq, dk, dv = oracle.attn_bwd(q, k, v, dout, s, b, nq, nkv, d, 1, causal, lib=lib)
+        dd = dout.astype(np.float64)
+
+        def loss(q_, k_, v_):
+            o, _ = oracle.attn(q_, k_, v_, s, b, nq, nkv, d, 1, causal, lib=lib)
+            return float((o * dd).sum())
+
+        for name, arr, grad in (("q", q, dq), ("k", k, dk), ("v", v, dv)):
+            for idx in np.ndindex(arr.shape):
+                hi, lo = arr.copy(), arr.copy()
+                x = np.float64(arr[idx])
+                hi[idx] = np.float32(x + 1e-3)
+                lo[idx] = np.float32(x - 1e-3)
+                args_hi = {"q": (hi, k, v), "k": (q, hi, v), "v": (q, k, hi)}[name]
+                args_lo = {"q": (lo, k, v), "k": (q, lo, v), "v": (q, k, lo)}[name]
+                fd = (loss(*args_hi) - loss(*args_lo)) / (np.float64(hi[idx]) - np.float64(lo[idx]))
+                assert abs(fd - grad[idx]) < 1e-5 * (1.0 + abs(fd)), (name, idx, fd, grad[idx])
+
+
+def pin_bwd_vs_torch(lib):
+    """Random tiny shares, dense and causal, MHA and GQA, fp32 and bf16 inputs,
+    against torch's float64 autograd: max error 1e-12."""
+    cases = [  # s, b, nq, nkv, d, dtype
+        (1, 1, 2, 2, 4, "f32"), (9, 1, 2, 2, 8, "f32"), (17, 2, 4, 2, 8, "bf16"),
+        (12, 1, 8, 1, 16, "bf16"), (20, 2, 6, 3, 4, "f32"), (11, 1, 2, 1, 128, "bf16"),
+    ]
+    for n, (s, b, nq, nkv, d, dtype) in enumerate(cases):
+        q, k, v, dout = _rand_bwd(1400 + 10 * n, s, b, nq, nkv, d, dtype)
+        for causal in (False, True):
+            got = oracle.attn_bwd(q, k, v, dout, s, b, nq, nkv, d, 1, causal, lib=lib)
+            ref = torch_attention_grads(widen(q), widen(k), widen(v), widen(dout), causal)
+            for name, g, r in zip(("dq", "dk", "dv"), got, ref):
+                err = np.max(np.abs(g - r))
+                assert err < 1e-12, (n, causal, name, err)
+
+
+def pin_bwd_closed_forms(lib):
+    """dout = 0 gives zero gradients; s = 1 gives dq = dk = 0 and dv = the
+    group's summed dout; Q = 0 (uniform causal weights) gives
+    dv_j = sum_{t >= j} dout_t / (t + 1); and the keys' dk always sum to zero
+    (each softmax row's dS sums to zero)."""
+    s, b, nq, nkv, d = 9, 2, 4, 2, 8
+    G = nq // nkv
+    q, k, v, dout = _rand_bwd(1500, s, b, nq, nkv, d, "f32")
+    zero = np.zeros_like(dout)
+    for causal in (False, True):
+        for g in oracle.attn_bwd(q, k, v, zero, s, b, nq, nkv, d, 1, causal, lib=lib):
+            assert np.max(np.abs(g)) == 0.0
+        dq, dk, dv = oracle.attn_bwd(q, k, v, dout, s, b, nq, nkv, d, 1, causal, lib=lib)
+        assert np.max(np.abs(dk.sum(axis=0))) < 1e-12
+    q1, k1, v1, d1 = _rand_bwd(1510, 1, b, nq, nkv, d, "bf16")
+    dq, dk, dv = oracle.attn_bwd(q1, k1, v1, d1, 1, b, nq, nkv, d, 1, True, lib=lib)
+    assert np.max(np.abs(dq)) < 1e-15 and np.max(np.abs(dk)) < 1e-15
+    dw = widen(d1)
+    for g in range(nkv):
+        assert np.max(np.abs(dv[0, :, g] - dw[0, :, g * G:(g + 1) * G].sum(axis=1))) < 1e-12
+    q0 = np.zeros_like(q)
+    _, _, dv = oracle.attn_bwd(q0, k, v, dout, s, b, nq, nkv, d, 1, True, lib=lib)
+    dd = dout.astype(np.float64) / np.arange(1, s + 1)[:, None, None, None]
+    tail = np.cumsum(dd[::-1], axis=0)[::-1]  # sum over t >= j
+    for g in range(nkv):
+        ref = tail[:, :, g * G:(g + 1) * G].sum(axis=2)
+        assert np.max(np.abs(dv[:, :, g] - ref)) < 1e-12
+
+
+def pin_bwd_rows_match_full(lib):
+    """attn_bwd_rows at sampled query rows and keys equals the full evaluation."""
+    s, b, nq, nkv, d = 30, 2, 4, 2, 8
+    q, k, v, dout = _rand_bwd(1600, s, b, nq, nkv, d, "bf16")
+    qrows = synth.row_sample(1607, s, b, nq, n_random=6, edge=2, tile_bounds=(16,))
+    krows = synth.row_sample(1608, s, b, nkv, n_random=6, edge=2, tile_bounds=(16,))
+    for causal in (False, True):
+        dq, dk, dv = oracle.attn_bwd(q, k, v, dout, s, b, nq, nkv, d, 1, causal, lib=lib)
+        rq, rk, rv = oracle.attn_bwd_rows(q, k, v, dout, qrows, krows, s, b, nq, nkv, d, 1,
+                                          causal, lib=lib)
+        assert np.array_equal(rq, dq[qrows[:, 2], qrows[:, 0], qrows[:, 1]])
+        assert np.array_equal(rk, dk[krows[:, 2], krows[:, 0], krows[:, 1]])
+        assert np.array_equal(rv, dv[krows[:, 2], krows[:, 0], krows[:, 1]])
+
+
+def pin_bwd_sharded_chain(lib):
+    """The backward of the whole Ulysses layer: the gradients of unsharded
+    attention over all heads equal, per rank, the share's gradients computed
+    after the seq->head exchange of q, k, v and dout and returned with the
+    head->seq exchange (the backward exchanges are the forward ones with their
+    axes swapped), bit-exact."""
+    s, b, h, h_kv, d, P = 12, 2, 8, 4, 8, 2
+    qg, kg, vg, dg = (synth.tensor(1700 + n, (s, b, hh, d), "bf16")
+                      for n, hh in enumerate((h, h_kv, h_kv, h)))
+    sh = lambda g, hh: g.reshape(P, s // P, b, hh, d)  # noqa: E731 - contiguous token chunks
+    for causal in (False, True):
+        dq_f, dk_f, dv_f = oracle.attn_bwd(qg, kg, vg, dg, s, b, h, h_kv, d, 1, causal, lib=lib)
+        qs = oracle.seq2head(sh(qg, h), s, b, h, d, P, lib=lib)
+        ks = oracle.seq2head(sh(kg, h_kv), s, b, h_kv, d, P, lib=lib)
+        vs = oracle.seq2head(sh(vg, h_kv), s, b, h_kv, d, P, lib=lib)
+        ds = oracle.seq2head(sh(dg, h), s, b, h, d, P, lib=lib)
+        grads = [oracle.attn_bwd(qs[r], ks[r], vs[r], ds[r], s, b, h, h_kv, d, P, causal, lib=lib)
+                 for r in range(P)]
+        for n, (full, hh) in enumerate(((dq_f, h), (dk_f, h_kv), (dv_f, h_kv))):
+            back = oracle.head2seq(np.stack([g[n] for g in grads]), s, b, hh, d, P, lib=lib)
+            assert np.array_equal(back.reshape(s, b, hh, d), full), (n, causal)
+
+
 LAYOUT_PINS = [pin_alltoall_worked_example, pin_two_card_blocks, pin_conservation_4card,
                pin_inverse_random_bits, pin_brute_force_tiny, pin_pack_then_route_is_seq2head]
 ATTN_PINS = [pin_attn_vs_torch, pin_attn_large_scores, pin_attn_closed_forms,
              pin_attn_rows_sum_to_one, pin_attn_equivariance, pin_head_independence,
              pin_rows_match_full]
-ALL_PINS = LAYOUT_PINS + ATTN_PINS
+BWD_PINS = [pin_bwd_finite_differences, pin_bwd_vs_torch, pin_bwd_closed_forms,
+            pin_bwd_rows_match_full, pin_bwd_sharded_chain]
+ALL_PINS = LAYOUT_PINS + ATTN_PINS + BWD_PINS

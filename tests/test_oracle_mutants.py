@@ -15,11 +15,12 @@ SRC = os.path.join(os.path.dirname(oracle.__file__), "ulys_oracle.c")
 MUTANTS = [
     ("drop_scale", "scores[j] = acc * scale;", "scores[j] = acc;"),
     ("causal_excludes_diagonal", "J->causal ? t + 1 : J->s", "J->causal ? t : J->s"),
-    ("gqa_round_robin", "const int64_t g = i / (nq / nkv);", "const int64_t g = i % nkv;"),
+    ("gqa_round_robin", "const int64_t g = i / (nq / nkv);\n  const int64_t nkeys = J->causal",
+     "const int64_t g = i % nkv;\n  const int64_t nkeys = J->causal"),
     ("no_max_shift_in_lse", "*lse_out = m + log(l);", "*lse_out = log(l);"),
     ("drop_normalisation", "o_row[e] /= l;", "o_row[e] /= 1.0;"),
-    ("k_row_uses_query_head", "J->k + ((j * b + be) * nkv + g) * d",
-     "J->k + ((j * b + be) * nkv + (i % nkv)) * d"),
+    ("k_row_uses_query_head", "const double *krow = J->k + ((j * b + be) * nkv + g) * d;\n    double acc",
+     "const double *krow = J->k + ((j * b + be) * nkv + (i % nkv)) * d;\n    double acc"),
     ("pack_heads_strided", "int64_t xi = ((t * b + be) * h + (r * hp + k)) * d + e;\n"
      "            memcpy(dst + yi * elt",
      "int64_t xi = ((t * b + be) * h + (k * P + r)) * d + e;\n"
@@ -33,6 +34,24 @@ MUTANTS = [
      "            int64_t yi = (((r * sl + t) * b + be) * hp + k) * d + e;\n"
      "            memcpy(dst + xi"),
     ("bf16_widen_wrong_shift", "<< 16;", "<< 15;"),
+    # backward
+    ("bwd_drop_scale_dq", "dqrow[e] += ds * krow[e] * scale;\n            dkrow[e]",
+     "dqrow[e] += ds * krow[e];\n            dkrow[e]"),
+    ("bwd_drop_D", "const double ds = p[j] * (dp[j] - D);\n          const double *krow = J->k",
+     "const double ds = p[j] * dp[j];\n          const double *krow = J->k"),
+    ("bwd_dv_uses_ds", "dvrow[e] += p[j] * drow[e];\n          }\n        }\n      }\n    }\n  }\n"
+     "  free(p); free(dp);\n  J->status = ORC_OK;\n  return NULL;\n}\n\n/*\n * Backward of",
+     "dvrow[e] += ds * drow[e];\n          }\n        }\n      }\n    }\n  }\n"
+     "  free(p); free(dp);\n  J->status = ORC_OK;\n  return NULL;\n}\n\n/*\n * Backward of"),
+    ("bwd_gqa_first_head_only",
+     "for (int64_t i = g * G; i < (g + 1) * G; ++i) {\n      for (int64_t t = 0; t < s; ++t) {",
+     "for (int64_t i = g * G; i < g * G + 1; ++i) {\n      for (int64_t t = 0; t < s; ++t) {"),
+    ("bwd_dp_shifted_feature", "for (int64_t e = 0; e < d; ++e) acc += drow[e] * vrow[e];",
+     "for (int64_t e = 0; e < d; ++e) acc += drow[e] * vrow[(e + 1) % d];"),
+    ("bwd_rows_causal_skips_diagonal", "for (int64_t t = J->causal ? j : 0; t < s; ++t) {",
+     "for (int64_t t = J->causal ? j + 1 : 0; t < s; ++t) {"),
+    ("bwd_dk_uses_dout", "dqrow[e] += ds * krow[e] * scale;\n            dkrow[e] += ds * qrow[e] * scale;",
+     "dqrow[e] += ds * krow[e] * scale;\n            dkrow[e] += ds * drow[e] * scale;"),
 ]
 
 
