@@ -144,13 +144,58 @@ int ulys_attn_fwd_ws(const void* q, const void* k, const void* v, void* o, float
 int64_t ulys_attn_fwd_workspace_size(int64_t s, int64_t b, int64_t h, int64_t h_kv, int64_t d_h,
                                      int32_t P, int32_t causal, int32_t dtype);
 
+/*
+ * Backward of the head-sharded attention on one rank's share.
+ * [ATLAS] §5: both all-to-alls are linear and their backward is the same
+ * exchange with the split and concatenation axes swapped, so the gradient of
+ * the layer's output is brought to head-sharded form with
+ * ulys_pack_seq2head (plus the exchange) and dq, dk, dv go back with
+ * ulys_unpack_head2seq; the local attention's backward is the ordinary
+ * attention backward, i.e. the gradient of ulys_attn_fwd's result:
+ *   P = exp(S - lse) with S = q k^T / sqrt(d_h) (causal: keys j <= t),
+ *   dP = dout v^T, D = rowsum(dout * o), dS = P * (dP - D),
+ *   dq = dS k / sqrt(d_h), dk = dS^T q / sqrt(d_h), dv = P^T dout,
+ * with dk and dv summed over the query heads of each GQA group (contiguous
+ * groups, as in ulys_attn_fwd; [SPCP] notes that a K/V row used by many
+ * queries receives the sum of their gradients).
+ *
+ *   q, o, dout : [s, b, hp, d_h]; o and lse are ulys_attn_fwd's outputs for
+ *                the same q, k, v
+ *   k, v       : [s, b, hkvp, d_h]
+ *   lse        : [b, hp, s] fp32 (required)
+ *   dq         : [s, b, hp, d_h]   dk, dv : [s, b, hkvp, d_h]   (dtype of q)
+ *   workspace  : device, 16-byte aligned, at least
+ *                ulys_attn_bwd_workspace_size() bytes (per-row statistics);
+ *                contents ignored on entry, undefined on return.
+ * Gradients are accumulated in fp32 and rounded once (nearest-even).  No
+ * atomics: the result does not depend on scheduling.
+ * Supported: ULYS_BF16 with d_h = 128.
+ * Errors: as ulys_attn_fwd, plus ULYS_ERR_NULL for any missing pointer
+ * (lse and workspace included), ULYS_ERR_UNSUPPORTED for another dtype or
+ * head size, ULYS_ERR_DIM for a workspace smaller than required, and
+ * ULYS_ERR_ALIAS when an output or the workspace overlaps an input or
+ * another output.
+ */
+int ulys_attn_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
+                  const float* lse, void* dq, void* dk, void* dv, int64_t s, int64_t b, int64_t h,
+                  int64_t h_kv, int64_t d_h, int32_t P, int32_t causal, int32_t dtype,
+                  void* workspace, int64_t workspace_bytes, void* stream);
+
+/*
+ * Workspace bytes ulys_attn_bwd needs for these arguments; negative
+ * ULYS_ERR_* for arguments it would reject on size, divisibility, dtype or
+ * head size.
+ */
+int64_t ulys_attn_bwd_workspace_size(int64_t s, int64_t b, int64_t h, int64_t h_kv, int64_t d_h,
+                                     int32_t P, int32_t causal, int32_t dtype);
+
 /* Static, human-readable text for a status code (never NULL). */
 const char* ulys_status_string(int status);
 
 /* ABI version of this header: (major << 16) | minor. */
 int ulys_abi_version(void);
 
-#define ULYS_ABI_VERSION ((1 << 16) | 1)
+#define ULYS_ABI_VERSION ((1 << 16) | 2)
 
 #ifdef __cplusplus
 }

@@ -36,7 +36,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_version(lib):
-    assert B.ulys_abi_version() == (1 << 16) | 1
+    assert B.ulys_abi_version() == (1 << 16) | 2
 
 
 def test_status_strings(lib):
@@ -138,3 +138,46 @@ def test_workspace_size_rejects(lib, args, expect):
 
 def test_workspace_size_fp32_is_zero(lib):
     assert B.ulys_attn_fwd_workspace_size(16, 1, 8, 8, 64, 4, 0, B.ULYS_F32) == 0
+
+
+# ---------------------------------------------------------------------- backward
+DO, DQ, DK, DV, WS = (0x7F0000000000 + i * (1 << 32) for i in range(6, 11))
+BWD_OK = (Q, K, V, O, DO, L, DQ, DK, DV, 64, 1, 8, 8, 128, 4, 1, B.ULYS_BF16, WS, 1 << 20)
+
+
+def bwd_args(**kw):
+    names = ("q", "k", "v", "o", "dout", "lse", "dq", "dk", "dv", "s", "b", "h", "h_kv", "d",
+             "P", "causal", "dtype", "ws", "nbytes")
+    a = dict(zip(names, BWD_OK))
+    a.update(kw)
+    return tuple(a[n] for n in names)
+
+
+@pytest.mark.parametrize("kw,expect", [
+    (dict(q=None), B.ULYS_ERR_NULL),
+    (dict(lse=None), B.ULYS_ERR_NULL),
+    (dict(dv=None), B.ULYS_ERR_NULL),
+    (dict(ws=None), B.ULYS_ERR_NULL),
+    (dict(s=0), B.ULYS_ERR_DIM),
+    (dict(s=66), B.ULYS_ERR_DIVISIBILITY),
+    (dict(h_kv=2), B.ULYS_ERR_DIVISIBILITY),
+    (dict(d=64), B.ULYS_ERR_UNSUPPORTED),
+    (dict(dtype=B.ULYS_F32), B.ULYS_ERR_UNSUPPORTED),
+    (dict(nbytes=16), B.ULYS_ERR_DIM),
+    (dict(dk=DK + 4), B.ULYS_ERR_ALIGNMENT),
+    (dict(dq=Q + 256), B.ULYS_ERR_ALIAS),
+    (dict(dv=DK + 64), B.ULYS_ERR_ALIAS),
+    (dict(ws=DO), B.ULYS_ERR_ALIAS),
+    (dict(dq=L), B.ULYS_ERR_ALIAS),
+])
+def test_attn_bwd_rejects(lib, kw, expect):
+    assert B.ulys_attn_bwd(*bwd_args(**kw)) == expect
+
+
+def test_attn_bwd_workspace_size(lib):
+    # D and lse * log2(e) per query row, rows padded to 4 queries
+    assert B.ulys_attn_bwd_workspace_size(64, 1, 8, 8, 128, 4, 1, B.ULYS_BF16) == 2 * 2 * 64 * 4
+    assert B.ulys_attn_bwd_workspace_size(66, 1, 8, 8, 128, 2, 1, B.ULYS_BF16) == 2 * 4 * 68 * 4
+    assert B.ulys_attn_bwd_workspace_size(64, 1, 8, 8, 64, 4, 1, B.ULYS_BF16) == B.ULYS_ERR_UNSUPPORTED
+    assert B.ulys_attn_bwd_workspace_size(64, 1, 8, 8, 128, 4, 1, B.ULYS_F32) == B.ULYS_ERR_UNSUPPORTED
+    assert B.ulys_attn_bwd_workspace_size(0, 1, 8, 8, 128, 4, 1, B.ULYS_BF16) == B.ULYS_ERR_DIM

@@ -21,7 +21,8 @@ ULYS_ERR_UNSUPPORTED, ULYS_ERR_ALIGNMENT, ULYS_ERR_ALIAS, ULYS_ERR_HIP = -4, -5,
 
 # every symbol include/ulysses.h declares
 EXPORTED = ("ulys_pack_seq2head", "ulys_unpack_head2seq", "ulys_attn_fwd", "ulys_attn_fwd_ws",
-            "ulys_attn_fwd_workspace_size", "ulys_status_string", "ulys_abi_version")
+            "ulys_attn_fwd_workspace_size", "ulys_attn_bwd", "ulys_attn_bwd_workspace_size",
+            "ulys_status_string", "ulys_abi_version")
 
 _lib = None
 
@@ -54,6 +55,10 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.ulys_attn_fwd_ws.restype = ctypes.c_int
     lib.ulys_attn_fwd_workspace_size.argtypes = [i64, i64, i64, i64, i64, i32, i32, i32]
     lib.ulys_attn_fwd_workspace_size.restype = ctypes.c_int64
+    lib.ulys_attn_bwd.argtypes = [vp] * 9 + [i64] * 5 + [i32] * 3 + [vp, i64, vp]
+    lib.ulys_attn_bwd.restype = ctypes.c_int
+    lib.ulys_attn_bwd_workspace_size.argtypes = [i64, i64, i64, i64, i64, i32, i32, i32]
+    lib.ulys_attn_bwd_workspace_size.restype = ctypes.c_int64
     lib.ulys_status_string.argtypes = [ctypes.c_int]
     lib.ulys_status_string.restype = ctypes.c_char_p
     lib.ulys_abi_version.argtypes = []
@@ -83,6 +88,16 @@ def ulys_attn_fwd_ws(q, k, v, o, lse, s, b, h, h_kv, d_h, P, causal, dtype, work
 
 def ulys_attn_fwd_workspace_size(s, b, h, h_kv, d_h, P, causal, dtype) -> int:
     return load().ulys_attn_fwd_workspace_size(s, b, h, h_kv, d_h, P, causal, dtype)
+
+
+def ulys_attn_bwd(q, k, v, o, dout, lse, dq, dk, dv, s, b, h, h_kv, d_h, P, causal, dtype,
+                  workspace, workspace_bytes, stream=None) -> int:
+    return load().ulys_attn_bwd(q, k, v, o, dout, lse, dq, dk, dv, s, b, h, h_kv, d_h, P, causal,
+                                dtype, workspace, workspace_bytes, stream)
+
+
+def ulys_attn_bwd_workspace_size(s, b, h, h_kv, d_h, P, causal, dtype) -> int:
+    return load().ulys_attn_bwd_workspace_size(s, b, h, h_kv, d_h, P, causal, dtype)
 
 
 def ulys_status_string(status: int) -> str:
@@ -168,3 +183,23 @@ def attn_fwd(q, k, v, P: int = 1, causal: bool = False, out=None, lse=False, str
                           ws.data_ptr() if ws is not None else None, ws_bytes, _stream(stream))
     _check(rc, "ulys_attn_fwd_ws")
     return out, lse_t
+
+
+def attn_bwd(q, k, v, o, dout, lse, P: int = 1, causal: bool = False, stream=None):
+    """Gradients of one rank's share: q, o, dout [s, b, h/P, d], k/v [s, b, h_kv/P, d],
+    lse [b, h/P, s] float32 (ulys_attn_fwd's outputs for the same q, k, v).
+    Allocates (with torch) the outputs and the workspace; returns (dq, dk, dv)."""
+    torch = _torch()
+    s, b, hp, d = q.shape
+    hkvp = k.shape[2]
+    h, h_kv, code = hp * P, hkvp * P, dtype_code(q)
+    ws_bytes = ulys_attn_bwd_workspace_size(s, b, h, h_kv, d, P, int(bool(causal)), code)
+    if ws_bytes < 0:
+        raise UlyssesError(int(ws_bytes), "ulys_attn_bwd_workspace_size")
+    ws = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=q.device)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    rc = ulys_attn_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), dout.data_ptr(),
+                       lse.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), s, b, h, h_kv,
+                       d, P, int(bool(causal)), code, ws.data_ptr(), ws_bytes, _stream(stream))
+    _check(rc, "ulys_attn_bwd")
+    return dq, dk, dv

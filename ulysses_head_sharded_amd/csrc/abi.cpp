@@ -106,10 +106,10 @@ int check_attn_shape(int64_t s, int64_t b, int64_t h, int64_t h_kv, int64_t d_h,
   // the kernels index tokens and work items with 32-bit integers
   if (s > 0x7FFFFFFF || b * hp > 0x7FFFFFFF || b * hp * s > (int64_t(1) << 40))
     return ULYS_ERR_DIM;
-  // the bf16 kernel addresses each tensor with 32-bit byte offsets (plus one
-  // tile of keys past the end, which its buffer loads read as zero)
-  if (dtype == ULYS_BF16 && (*nq + 2 * 64 * b * hp * d_h * 2 >= (int64_t(1) << 31) ||
-                             *nkv + 2 * 64 * b * hkvp * d_h * 2 >= (int64_t(1) << 31)))
+  // the bf16 kernels address each tensor with 32-bit byte offsets, up to one
+  // 256-row workgroup block past the end (read as zero, stores dropped)
+  if (dtype == ULYS_BF16 && (*nq + 256 * b * hp * d_h * 2 >= (int64_t(1) << 31) ||
+                             *nkv + 256 * b * hkvp * d_h * 2 >= (int64_t(1) << 31)))
     return ULYS_ERR_DIM;
   return ULYS_OK;
 }
@@ -188,6 +188,73 @@ int64_t ulys_attn_fwd_workspace_size(int64_t s, int64_t b, int64_t h, int64_t h_
   const ulys::AttnArgs a = make_args(nullptr, nullptr, nullptr, nullptr, nullptr, s, b, h, h_kv,
                                      d_h, P, causal);
   return ulys::attn_bf16_workspace_size(a);
+}
+
+int64_t ulys_attn_bwd_workspace_size(int64_t s, int64_t b, int64_t h, int64_t h_kv, int64_t d_h,
+                                     int32_t P, int32_t causal, int32_t dtype) {
+  int64_t nq = 0, nkv = 0, nl = 0;
+  const int rc = check_attn_shape(s, b, h, h_kv, d_h, P, dtype, &nq, &nkv, &nl);
+  if (rc != ULYS_OK) return rc;
+  if (dtype != ULYS_BF16 || d_h != 128) return ULYS_ERR_UNSUPPORTED;
+  ulys::AttnBwdArgs a;
+  a.s = s;
+  a.b = b;
+  a.hp = h / P;
+  a.hkvp = h_kv / P;
+  a.d = d_h;
+  a.causal = causal != 0;
+  const int64_t need = ulys::attn_bwd_bf16_workspace_size(a);
+  // the kernels address the per-row statistics with 32-bit byte offsets
+  if (need >= (int64_t(1) << 31)) return ULYS_ERR_DIM;
+  return need;
+}
+
+int ulys_attn_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
+                  const float* lse, void* dq, void* dk, void* dv, int64_t s, int64_t b, int64_t h,
+                  int64_t h_kv, int64_t d_h, int32_t P, int32_t causal, int32_t dtype,
+                  void* workspace, int64_t workspace_bytes, void* stream) {
+  if (!q || !k || !v || !o || !dout || !lse || !dq || !dk || !dv || !workspace)
+    return ULYS_ERR_NULL;
+  const int64_t need = ulys_attn_bwd_workspace_size(s, b, h, h_kv, d_h, P, causal, dtype);
+  if (need < 0) return (int)need;
+  if (workspace_bytes < need) return ULYS_ERR_DIM;
+  int64_t nq = 0, nkv = 0, nl = 0;
+  const int rc = check_attn_shape(s, b, h, h_kv, d_h, P, dtype, &nq, &nkv, &nl);
+  if (rc != ULYS_OK) return rc;
+  const void* ins[] = {q, k, v, o, dout, lse};
+  const int64_t in_bytes[] = {nq, nkv, nkv, nq, nq, nl};
+  void* outs[] = {dq, dk, dv, workspace};
+  const int64_t out_bytes[] = {nq, nkv, nkv, need};
+  for (const void* p : ins)
+    if (!aligned16(p)) return ULYS_ERR_ALIGNMENT;
+  for (const void* p : outs)
+    if (!aligned16(p)) return ULYS_ERR_ALIGNMENT;
+  for (int i = 0; i < 4; ++i) {
+    for (int j = 0; j < 6; ++j)
+      if (overlaps(outs[i], out_bytes[i], ins[j], in_bytes[j])) return ULYS_ERR_ALIAS;
+    for (int j = 0; j < i; ++j)
+      if (overlaps(outs[i], out_bytes[i], outs[j], out_bytes[j])) return ULYS_ERR_ALIAS;
+  }
+  ulys::AttnBwdArgs a;
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.o = o;
+  a.dout = dout;
+  a.lse = lse;
+  a.dq = dq;
+  a.dk = dk;
+  a.dv = dv;
+  a.s = s;
+  a.b = b;
+  a.hp = h / P;
+  a.hkvp = h_kv / P;
+  a.d = d_h;
+  a.causal = causal != 0;
+  a.workspace = workspace;
+  a.workspace_bytes = workspace_bytes;
+  const hipError_t e = ulys::launch_attn_bwd_bf16(a, (hipStream_t)stream);
+  return e == hipSuccess ? ULYS_OK : ULYS_ERR_HIP;
 }
 
 const char* ulys_status_string(int status) {

@@ -41,22 +41,16 @@
 //    second kernel merges.
 #include <math.h>
 
+#include "cdna4.h"
 #include "internal.h"
 
 namespace ulys {
 namespace {
 
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef float f32x16 __attribute__((ext_vector_type(16)));
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
-
 constexpr int kWaves = 8;
 constexpr int kThreads = 64 * kWaves;
 constexpr int kBN = 64;  // keys per tile
 constexpr int kQW = 32;  // queries per wave
-// dword 3 of a raw buffer resource (no swizzle, 32-bit data format) on gfx9
-constexpr int kRsrcWord3 = 0x00020000;
 
 template <int D>
 struct Cfg {
@@ -95,48 +89,6 @@ struct Params {
   int q_bytes, kv_bytes;  // tensor sizes in bytes (bounds of the buffer resources)
   float c;     // log2(e) / sqrt(d_h)
 };
-
-__device__ __forceinline__ bf16x8 as_bf16x8(u32x4 x) { return __builtin_bit_cast(bf16x8, x); }
-
-// Raw buffer resource over a whole tensor: loads past num_bytes return 0 and
-// stores past it are dropped, which handles the ragged tail without branches.
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* base, int num_bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, num_bytes,
-                                           kRsrcWord3);
-}
-
-// The value of x in the partner lane (l ^ 32) combined with max / sum.
-__device__ __forceinline__ float xmax32(float x) {
-  const uint32_t u = __builtin_bit_cast(uint32_t, x);
-  const auto sw = __builtin_amdgcn_permlane32_swap(u, u, false, false);
-  return fmaxf(__builtin_bit_cast(float, (uint32_t)sw[0]),
-               __builtin_bit_cast(float, (uint32_t)sw[1]));
-}
-__device__ __forceinline__ float xsum32(float x) {
-  const uint32_t u = __builtin_bit_cast(uint32_t, x);
-  const auto sw = __builtin_amdgcn_permlane32_swap(u, u, false, false);
-  return __builtin_bit_cast(float, (uint32_t)sw[0]) + __builtin_bit_cast(float, (uint32_t)sw[1]);
-}
-
-// Transposing LDS read (ds_read_b64_tr_b16).  Within each group of 16 lanes,
-// output lane 4a+e receives element e of the 8-byte reads of source lanes a,
-// a+4, a+8, a+12.  When source lane s reads 4 elements at row r0 + s/4,
-// column c0 + 4 (s%4) of a row-major tile, output lane L therefore holds
-// rows r0 .. r0+3 of column c0 + L: four consecutive keys of one feature,
-// i.e. one half of an MFMA operand taken straight from row-major V.
-__device__ __forceinline__ u32x2 lds_read_tr(const uint16_t* __restrict__ p) {
-  typedef short i16x4 __attribute__((ext_vector_type(4)));
-  const i16x4 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-      (__attribute__((address_space(3))) i16x4*)(p));
-  return __builtin_bit_cast(u32x2, r);
-}
-
-// One direct global->LDS load: every lane's 16 bytes at byte offset voff of
-// the resource land at lds_dst + 16 * lane (out-of-range lanes write zeros).
-__device__ __forceinline__ void load_lds16(__amdgpu_buffer_rsrc_t r, uint8_t* lds_dst, int voff) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds_dst,
-                                           16, voff, 0, 0, 0);
-}
 
 // LDS tiles are unpadded, with the 16-byte chunks of row r XOR-swizzled so
 // that reads are free of bank conflicts on gfx950's LDS, which serves 256

@@ -57,4 +57,23 @@ hipError_t launch_attn_bf16(const AttnArgs& a, hipStream_t stream);
 int64_t attn_bf16_workspace_size(const AttnArgs& a);
 hipError_t launch_attn_f32(const AttnArgs& a, hipStream_t stream);
 
+struct AttnBwdArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* o;
+  const void* dout;
+  const float* lse;
+  void* dq;
+  void* dk;
+  void* dv;
+  int64_t s, b, hp, hkvp, d;
+  int causal;
+  void* workspace;
+  int64_t workspace_bytes;
+};
+
+hipError_t launch_attn_bwd_bf16(const AttnBwdArgs& a, hipStream_t stream);
+int64_t attn_bwd_bf16_workspace_size(const AttnBwdArgs& a);
+
 }  // namespace ulys
