@@ -41,6 +41,9 @@ def parse_args():
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="wall-time budget of the oracle's cpu_baseline sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--bwd-steps", type=int, default=100,
+                    help="timed backward steps (pack dO, attention backward, unpack dQ, dK, "
+                         "dV) reported under 'backward'; 0 skips them")
     ap.add_argument("--inputs", choices=("normal", "constant"), default="normal",
                     help="normal: the seeded N(0,1) tensors (the workload); constant: the "
                          "same work on constant tensors, a diagnostic of how much the GPU "
@@ -120,6 +123,86 @@ def cpu_baseline(w, q, k, v, budget_s: float):
         "value": flops / t_used / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
         "sample": f"{rows_done} uniformly drawn query rows of the {w.name} share "
                   f"(fp64 oracle, {t_used:.1f} s wall, algorithmic flops of the sample)",
+    }
+
+
+def bench_backward(args, w, binding, torch, np, q, k, v, code, stream):
+    """The backward of the same step: the output gradient's pack (seq->head),
+    the attention backward on the share, the unpack (head->seq) of dQ, dK and
+    dV: the exchanges' backward is the same pair of layout kernels with the
+    directions swapped.  q, k, v are the forward's packed shares."""
+    from ulysses_head_sharded_amd import synth
+
+    dev = q.device
+    sl, hp, hkvp = w.s // w.P, w.hp, w.hkvp
+    sh = stream.cuda_stream
+    qs = q.view(w.s, w.b, hp, w.d)
+    ks = k.view(w.s, w.b, hkvp, w.d)
+    vs = v.view(w.s, w.b, hkvp, w.d)
+    o, lse = binding.attn_fwd(qs, ks, vs, P=w.P, causal=w.causal, lse=True)
+    gx = torch.from_numpy(synth.tensor(100 * w.c + 4, (sl, w.b, w.h, w.d), w.dtype)
+                          .view(np.int16)).to(dev).view(torch.bfloat16)
+    gy = torch.empty((w.s, w.b, hp, w.d), dtype=q.dtype, device=dev)
+    dq, dk, dv = torch.empty_like(qs), torch.empty_like(ks), torch.empty_like(vs)
+    xdq = torch.empty((sl, w.b, w.h, w.d), dtype=q.dtype, device=dev)
+    xdk = torch.empty((sl, w.b, w.h_kv, w.d), dtype=q.dtype, device=dev)
+    xdv = torch.empty_like(xdk)
+    nbytes = binding.ulys_attn_bwd_workspace_size(w.s, w.b, w.h, w.h_kv, w.d, w.P,
+                                                  int(w.causal), code)
+    if nbytes < 0:
+        raise RuntimeError(f"backward workspace: {binding.ulys_status_string(int(nbytes))}")
+    ws = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=dev)
+
+    def call(rc, what):
+        if rc != 0:
+            raise RuntimeError(f"{what}: {binding.ulys_status_string(rc)}")
+
+    marks = []
+
+    def step(record):
+        e = [torch.cuda.Event(enable_timing=True) for _ in range(3)] if record else None
+        if record:
+            e[0].record(stream)
+        call(binding.ulys_pack_seq2head(gx.data_ptr(), gy.data_ptr(), w.s, w.b, w.h, w.d, w.P,
+                                        code, sh), "pack dO")
+        if record:
+            e[1].record(stream)
+        call(binding.ulys_attn_bwd(qs.data_ptr(), ks.data_ptr(), vs.data_ptr(), o.data_ptr(),
+                                   gy.data_ptr(), lse.data_ptr(), dq.data_ptr(), dk.data_ptr(),
+                                   dv.data_ptr(), w.s, w.b, w.h, w.h_kv, w.d, w.P,
+                                   int(w.causal), code, ws.data_ptr(), nbytes, sh), "attn bwd")
+        if record:
+            e[2].record(stream)
+        for src, dst, hh in ((dq, xdq, w.h), (dk, xdk, w.h_kv), (dv, xdv, w.h_kv)):
+            call(binding.ulys_unpack_head2seq(src.data_ptr(), dst.data_ptr(), w.s, w.b, hh, w.d,
+                                              w.P, code, sh), "unpack grad")
+        if record:
+            e.append(torch.cuda.Event(enable_timing=True))
+            e[3].record(stream)
+            marks.append(e)
+
+    for _ in range(max(3, args.bwd_steps // 5)):
+        step(False)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.bwd_steps):
+        step(True)
+    torch.cuda.synchronize()
+    ms_step = (time.perf_counter() - t0) * 1e3 / args.bwd_steps
+    attn_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in marks]))
+    layout_ms = float(np.mean([e[0].elapsed_time(e[1]) + e[2].elapsed_time(e[3]) for e in marks]))
+    flops = w.attn_bwd_flops()
+    layout_bytes = 2 * (2 * w.shard_bytes() + 2 * w.shard_bytes(kv=True))
+    return {
+        "steps": args.bwd_steps, "ms_per_step": round(ms_step, 4),
+        "tflops_step": round(flops / (ms_step * 1e-3) / 1e12, 2),
+        "attn_bwd": {"ms": round(attn_ms, 4), "tflops": round(flops / (attn_ms * 1e-3) / 1e12, 2),
+                     "frac_peak": round(flops / (attn_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+                     "flops": flops, "flops_rule": "10 d b hp pairs (five products)",
+                     "workspace_bytes": int(nbytes)},
+        "layout": {"pack_do_unpack_dqkv_us": round(layout_ms * 1e3, 2),
+                   "gbps": round(layout_bytes / (layout_ms * 1e-3) / 1e9, 1),
+                   "bytes": layout_bytes},
     }
 
 
@@ -263,6 +346,8 @@ def main():
                      "unit": "TFLOP/s", "frac": round(attn_tflops / peak, 4),
                      "traffic": counter_traffic(kernel_src, w.name)},
     }
+    if args.bwd_steps > 0 and w.dtype == "bf16":
+        rec["backward"] = bench_backward(args, w, binding, torch, np, yq, yk, yv, code, stream)
     if not args.no_cpu_baseline:
         # the oracle gets its own seeded share-shaped inputs (same distribution)
         q_h = synth.tensor(100 * w.c + 1, (w.s, w.b, hp, w.d), w.dtype)

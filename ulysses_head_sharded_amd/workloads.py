@@ -43,6 +43,12 @@ class Workload:
         """Algorithmic FLOPs: 2 per multiply-add of QK^T and of PV over visible pairs."""
         return 4.0 * self.d * self.b * self.hp * self.pairs()
 
+    def attn_bwd_flops(self) -> float:
+        """Algorithmic FLOPs of the attention backward: the five products over
+        visible pairs (S = QK^T recomputed, dP = dO V^T, dV = P^T dO, dQ = dS K,
+        dK = dS^T Q), 2 per multiply-add; 2.5 times the forward."""
+        return 10.0 * self.d * self.b * self.hp * self.pairs()
+
     def shard_bytes(self, kv: bool = False) -> int:
         """Bytes of one rank-local [s/P, b, heads, d] shard."""
         heads = self.h_kv if kv else self.h
