@@ -88,6 +88,7 @@ struct Params {
   int q_tok_bytes, kv_tok_bytes;  // bytes between consecutive tokens
   int q_bytes, kv_bytes;  // tensor sizes in bytes (bounds of the buffer resources)
   float c;     // log2(e) / sqrt(d_h)
+  float lazy;  // 8 / c: margin (raw score units) by which a row max may pass m_run
 };
 
 // LDS tiles are unpadded, with the 16-byte chunks of row r XOR-swizzled so
@@ -303,9 +304,13 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bf16_kernel(Params p) {
         oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[ks], oacc[db], 0, 0, 0);
       }
   };
-  // online-softmax step on the scores of one tile: new running max, rescale
-  // of the running sum and accumulator only when some row's max grew (rows
-  // whose max is unchanged keep a factor of exactly 1); returns m_new * c
+  // online-softmax step on the scores of one tile.  The reference max m_run
+  // that the exponents subtract moves only when a row's tile max exceeds it
+  // by more than p.lazy (8 in log2 units): any m_run at least the true max
+  // minus that margin gives the same softmax (the factor cancels between the
+  // sum and the accumulator) and keeps every exponent at most 8, far from
+  // overflow.  After the first tiles of a row the rescale of the running sum
+  // and accumulator then almost never runs.  Returns m_run * c.
   auto update_max = [&](const f32x16* sc) -> float {
     float mx = -INFINITY;
 #pragma unroll
@@ -313,22 +318,22 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bf16_kernel(Params p) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sc[kb][r]);
     mx = xmax32(mx);
-    const float m_new = fmaxf(m_run, mx);
-    const float base = (m_new == -INFINITY) ? 0.f : m_new * p.c;
-    if (__ballot(m_new > m_run) != 0) {
-      const float alpha = (m_new > m_run) ? __builtin_amdgcn_exp2f(m_run * p.c - base) : 1.f;
+    const bool grow = mx > m_run + p.lazy;  // m_run = -inf: any finite max
+    if (__ballot(grow) != 0) {
+      const float m_new = grow ? mx : m_run;
+      const float alpha = grow ? __builtin_amdgcn_exp2f((m_run - m_new) * p.c) : 1.f;
       l_run *= alpha;
 #pragma unroll
       for (int db = 0; db < D / 32; ++db)
 #pragma unroll
         for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
+      m_run = m_new;
     }
-    m_run = m_new;
-    return base;
+    return (m_run == -INFINITY) ? 0.f : m_run * p.c;
   };
-  // probabilities exp2(s c - m c) of one tile, summed into l_run and packed to
-  // bf16 as the P^T operands: 16-key step ks uses registers 8 (ks%2) .. +7 of
-  // block ks/2
+  // probabilities exp2(s c - m c) of one tile, summed in fp32 into l_run and
+  // packed to bf16 as the P^T operands: 16-key step ks uses registers
+  // 8 (ks%2) .. +7 of block ks/2
   auto probs = [&](f32x16* sc, float base, bf16x8* pb) {
     float ps = 0.f;
 #pragma unroll
@@ -503,6 +508,7 @@ hipError_t launch_d(const AttnArgs& a, hipStream_t stream) {
   p.q_bytes = (int)(a.s * a.b * a.hp * D * 2);
   p.kv_bytes = (int)(a.s * a.b * a.hkvp * D * 2);
   p.c = (float)(1.4426950408889634 / sqrt((double)D));
+  p.lazy = 8.f / p.c;
   const int64_t items = (int64_t)p.n_qblk * p.b * p.hkvp * p.nsub;
   if (items <= 0) return hipSuccess;
   if (items > 0x7FFFFFFF) return hipErrorInvalidValue;
