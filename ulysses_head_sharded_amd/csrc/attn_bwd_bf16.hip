@@ -12,18 +12,27 @@
 // dk and dv summed over the query heads of each GQA group (contiguous
 // groups, as in the forward).
 //
-// Three kernels, no atomics (the result does not depend on scheduling):
-//  * prep: D and lse * log2(e) per query row, into the caller's workspace;
-//  * dq: one workgroup of 8 waves per 256 queries (as the forward), looping
-//    over 64-key K/V tiles in LDS: S^T = K Q^T and dP^T = V dout^T with the
-//    wave's Q^T and dout^T fragments in registers, dS^T = P^T (dP^T - D),
-//    dq^T += K^T dS^T with K^T read transposed from LDS;
-//  * dkv: one workgroup of 4 waves per 128 keys of one KV head, each wave
-//    owning 32 keys, looping over the group's query heads and 32-query tiles
-//    of Q and dout in LDS: S = Q K^T (K^T fragments in registers),
-//    dP = dout V^T (V^T from the workgroup's V block in LDS), then
-//    dv^T += dout^T P and dk^T += Q^T dS with dout^T and Q^T read transposed.
-// S and dP are therefore computed twice (once per kernel).
+// Kernels, no atomics (the result does not depend on scheduling):
+//  * prep: -D and -lse * sqrt(d_h) per query row, into the caller's
+//    workspace (the dkv kernel starts its dP and S accumulators from them,
+//    so that exp2(c S) is P and dP - D comes out of the MFMA);
+//  * dq: a workgroup of 8 waves owns 256 queries (as the forward: up to 8
+//    query heads of one KV group), streaming 64-key K/V tiles through LDS:
+//    S^T = K Q^T and dP^T = V dout^T with the wave's Q^T and dout^T
+//    fragments in registers, dS^T = P^T (dP^T - D), dq^T += K^T dS^T with
+//    K^T read transposed from LDS;
+//  * dkv: a workgroup of 8 waves owns 256 keys of one KV head (32 per wave,
+//    K^T fragments in registers, V rows in LDS for the whole loop), streaming
+//    64-query tiles of Q, dout and their statistics through LDS for every
+//    query head of the group: S = Q K^T, dP = dout V^T, then dv^T += dout^T P
+//    and dk^T += Q^T dS with dout^T and Q^T read transposed;
+//  * merge (dq, dkv): when a causal share has too few work items to fill the
+//    GPU twice, every item is run as two halves (keys for dq, queries for
+//    dkv) that leave fp32 partial sums in the workspace, and a merge adds the
+//    two halves in a fixed order, scales and rounds.
+// S and dP are computed by both kernels.  Each kernel has a branch-free fast
+// path for tiles with no masked entry and a masked path for diagonal and
+// tail tiles.
 //
 // Every tile read both row-wise (16-byte MFMA operand reads of 16
 // consecutive rows) and transposed (ds_read_b64_tr_b16 over 4 consecutive
@@ -41,7 +50,8 @@ namespace {
 constexpr int D = 128;               // head size served here
 constexpr int ROW = D * 2;           // bytes of one bf16 row
 constexpr int CHUNKS = ROW / 16;     // 16-byte chunks per row
-constexpr float kLog2e = 1.4426950408889634f;
+constexpr int kWaves = 8;
+constexpr int kThreads = 64 * kWaves;
 
 __device__ __forceinline__ int dswz(int r) {
   const int i = r & 3;
@@ -50,13 +60,15 @@ __device__ __forceinline__ int dswz(int r) {
 
 // ------------------------------------------------------------------ prep
 // 16 lanes per query row (8 bf16 each); rows enumerated in memory order
-// r = (t * b + be) * hp + i of the [s, b, hp, d] tensors.
+// r = (t * b + be) * hp + i of the [s, b, hp, d] tensors.  Writes
+// ndelta = -D and nlse = -lse * sqrt(d_h): with c = log2(e) / sqrt(d_h),
+// P = exp2(c (q.k + nlse)).
 __global__ __launch_bounds__(256) void bwd_prep_kernel(const uint16_t* __restrict__ o,
                                                        const uint16_t* __restrict__ dout,
                                                        const float* __restrict__ lse,
-                                                       float* __restrict__ delta,
-                                                       float* __restrict__ lse2, int rows,
-                                                       int s, int s_pad, int bhp) {
+                                                       float* __restrict__ ndelta,
+                                                       float* __restrict__ nlse, int rows,
+                                                       int s, int s_pad, int bhp, float sqrt_d) {
   const int gid = blockIdx.x * 256 + threadIdx.x;
   const int r = gid >> 4, part = gid & 15;
   float acc = 0.f;
@@ -71,8 +83,8 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(const uint16_t* __restric
   for (int w = 8; w >= 1; w >>= 1) acc += __shfl_xor(acc, w, 16);
   if (r < rows && part == 0) {
     const int t = r / bhp, rem = r - t * bhp;  // rem = be * hp + i
-    delta[(int64_t)rem * s_pad + t] = acc;
-    lse2[(int64_t)rem * s_pad + t] = lse[(int64_t)rem * s + t] * kLog2e;
+    ndelta[(int64_t)rem * s_pad + t] = -acc;
+    nlse[(int64_t)rem * s_pad + t] = -lse[(int64_t)rem * s + t] * sqrt_d;
   }
 }
 
@@ -81,20 +93,23 @@ struct BwdParams {
   const uint16_t* k;
   const uint16_t* v;
   const uint16_t* dout;
-  const float* delta;  // [b, hp, s_pad]
-  const float* lse2;   // [b, hp, s_pad], lse * log2(e)
+  const float* ndelta;  // [b, hp, s_pad], -D
+  const float* nlse;    // [b, hp, s_pad], -lse * sqrt(d_h)
   uint16_t* dq;
   uint16_t* dk;
   uint16_t* dv;
+  float* part;         // partial sums of split units (fp32), when a split is used
   int s, b, hp, hkvp, G;
-  int s_pad;  // row length of delta and lse2: s rounded up to 4 (16-byte rows)
+  int s_pad;  // row length of ndelta and nlse: s rounded up to 4 (16-byte rows)
   int q_tok_bytes, kv_tok_bytes, q_bytes, kv_bytes, stat_bytes;
   float c;       // log2(e) / sqrt(d_h)
   float inv_sd;  // 1 / sqrt(d_h)
   // dq kernel: items = n_qblk * b * hkvp * nsub (as the forward)
   int QH, QB, n_qblk, nsub;
-  // dkv kernel: items = n_kblk * b * hkvp; pairing of the first resident wave
-  int n_kblk, slots;
+  int q_split;   // 1: every dq item runs as two halves of its key tiles
+  // dkv kernel: items = n_kblk * b * hkvp
+  int n_kblk;
+  int kv_split;  // 1: every dkv item runs as two halves of its query steps
 };
 
 // Transposed 32 x 32 accumulator (rows = features, column = lane % 32) scaled
@@ -120,6 +135,28 @@ __device__ __forceinline__ void store_t(__amdgpu_buffer_rsrc_t r, const f32x16* 
     }
 }
 
+// Partial sums of a split unit: n accumulator blocks per lane, stored lane
+// contiguous ([wave][slot][lane]) so both writes and reads coalesce.
+template <int N>
+__device__ __forceinline__ void store_part(float* unit_base, const f32x16* acc, int wave,
+                                           int lane) {
+  float* dst = unit_base + wave * (N * 16 * 64) + lane;
+#pragma unroll
+  for (int n = 0; n < N; ++n)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) dst[(n * 16 + r) * 64] = acc[n][r];
+}
+template <int N>
+__device__ __forceinline__ void add_parts(const float* u0, const float* u1, f32x16* acc, int wave,
+                                          int lane) {
+  const float* a = u0 + wave * (N * 16 * 64) + lane;
+  const float* b = u1 + wave * (N * 16 * 64) + lane;
+#pragma unroll
+  for (int n = 0; n < N; ++n)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[n][r] = a[(n * 16 + r) * 64] + b[(n * 16 + r) * 64];
+}
+
 // Lane parts of the LDS addresses into a swizzled tile of 256-byte rows.
 //  row reads (A operand of 32 rows x 16 features): row l%32 of a 32-row
 //  block, logical chunk 2 dk + hh;
@@ -127,15 +164,17 @@ __device__ __forceinline__ void store_t(__amdgpu_buffer_rsrc_t r, const f32x16* 
 //  16-row step: rows 4 hh + (l%16)/4 (lo) and + 8 (hi), byte column
 //  64 db + 32 ((l/16)%2) + 8 (l%4).  Row offsets that are multiples of 16
 //  leave the swizzle unchanged; +8 rows flips bit 1 of g.
+//  Since 2 dk has bit 0 clear, (2 dk + hh) ^ g = 2 (dk ^ (g >> 1)) + ((hh ^ g) & 1),
+//  so the row read of step dk is at row_base ^ (32 dk): one register.
 struct TileAddr {
-  int row_rd[D / 16];
+  int row_base;
   int tr_lo[D / 32], tr_hi[D / 32];
+  __device__ __forceinline__ int row_rd(int dk) const { return row_base ^ (dk << 5); }
 };
 __device__ __forceinline__ TileAddr tile_addr(int lane) {
   TileAddr a;
   const int l32 = lane & 31, hh = lane >> 5;
-#pragma unroll
-  for (int dk = 0; dk < D / 16; ++dk) a.row_rd[dk] = l32 * ROW + (((2 * dk + hh) ^ dswz(l32)) << 4);
+  a.row_base = l32 * ROW + ((hh ^ dswz(l32)) << 4);
   const int vr = 4 * hh + ((lane & 15) >> 2);
 #pragma unroll
   for (int db = 0; db < D / 32; ++db) {
@@ -154,11 +193,10 @@ __device__ __forceinline__ bf16x8 read_tr(const uint8_t* tile, const TileAddr& a
 }
 
 // ------------------------------------------------------------------ dq
-constexpr int kQWaves = 8;
-constexpr int kQThreads = 64 * kQWaves;
 constexpr int kBN = 64;              // keys per tile
-constexpr int kTile = kBN * ROW;     // one K or V tile
-constexpr int kQLoads = kBN * CHUNKS / (64 * kQWaves);  // 16-byte loads per lane per tensor
+constexpr int kTile = kBN * ROW;     // one K or V tile (16 KiB)
+constexpr int kQLoads = kBN * CHUNKS / (64 * kWaves);  // 16-byte loads per lane per tensor
+constexpr int kDqPart = kWaves * 64 * (D / 2);         // floats of one split dq unit
 
 struct QItem {
   int qblk, be, kvg, head, q0;
@@ -168,31 +206,37 @@ __device__ __forceinline__ QItem decode_q_item(const BwdParams& p, int rank, int
   const int per_q = p.b * p.hkvp * p.nsub;
   const int qi = rank / per_q;
   int rest = rank - qi * per_q;
-  it.qblk = causal ? (p.n_qblk - 1 - qi) : qi;
+  it.qblk = causal ? (p.n_qblk - 1 - qi) : qi;  // longest first
   const int sub = rest % p.nsub;
   rest /= p.nsub;
   it.kvg = rest % p.hkvp;
   it.be = rest / p.hkvp;
-  const int wph = kQWaves / p.QH;
+  const int wph = kWaves / p.QH;
   it.head = it.kvg * p.G + sub * p.QH + wave / wph;
   it.q0 = it.qblk * p.QB + (wave % wph) * 32;
   return it;
 }
 
 template <bool CAUSAL>
-__global__ __launch_bounds__(kQThreads, 1) void bwd_dq_kernel(BwdParams p) {
+__global__ __launch_bounds__(kThreads, 1) void bwd_dq_kernel(BwdParams p) {
   // LDS: K0 K1 V0 V1
   __shared__ __attribute__((aligned(16))) uint8_t lds[4 * kTile];
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
   const int l32 = lane & 31, hh = lane >> 5;
-  const QItem it = decode_q_item(p, blockIdx.x, wave, CAUSAL);
+  int rank = blockIdx.x, half = 0;
+  if (p.q_split) {
+    half = rank & 1;
+    rank >>= 1;
+  }
+  const QItem it = decode_q_item(p, rank, wave, CAUSAL);
   const int my_q = it.q0 + l32;
   const __amdgpu_buffer_rsrc_t rq = rsrc(p.q, p.q_bytes);
   const __amdgpu_buffer_rsrc_t rdo = rsrc(p.dout, p.q_bytes);
   const __amdgpu_buffer_rsrc_t rk = rsrc(p.k, p.kv_bytes);
   const __amdgpu_buffer_rsrc_t rv = rsrc(p.v, p.kv_bytes);
-  const __amdgpu_buffer_rsrc_t rst = rsrc(p.lse2, p.stat_bytes);
-  const __amdgpu_buffer_rsrc_t rde = rsrc(p.delta, p.stat_bytes);
+  const __amdgpu_buffer_rsrc_t rst = rsrc(p.nlse, p.stat_bytes);
+  const __amdgpu_buffer_rsrc_t rde = rsrc(p.ndelta, p.stat_bytes);
   const int q_head_off = (it.be * p.hp + it.head) * ROW;
   const int kv_head_off = (it.be * p.hkvp + it.kvg) * ROW;
 
@@ -206,17 +250,24 @@ __global__ __launch_bounds__(kQThreads, 1) void bwd_dq_kernel(BwdParams p) {
       gf[dk] = as_bf16x8(__builtin_amdgcn_raw_buffer_load_b128(rdo, off + dk * 32, 0, 0));
     }
   }
+  // statistics of query my_q (rows past s read whatever lies there: their
+  // results are never stored)
   const int stat = (it.be * p.hp + it.head) * p.s_pad + my_q;
-  const float lse2 = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rst, stat * 4, 0, 0));
-  const float dlt = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rde, stat * 4, 0, 0));
+  const float clse = p.c * __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rst, stat * 4, 0, 0));
+  const float ndlt = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rde, stat * 4, 0, 0));
+  // complete these loads before the loop, so that no wait in the loop is on
+  // anything but the tile loads
 #pragma unroll
   for (int dk = 0; dk < D / 16; ++dk) asm volatile("" ::"v"(qf[dk]), "v"(gf[dk]));
-  asm volatile("" ::"v"(lse2), "v"(dlt));
+  asm volatile("" ::"v"(clse), "v"(ndlt));
 
   const int q_hi = min(p.s, (it.qblk + 1) * p.QB);
-  const int n_tiles = CAUSAL ? (q_hi + kBN - 1) / kBN : (p.s + kBN - 1) / kBN;
+  const int n_item = CAUSAL ? (q_hi + kBN - 1) / kBN : (p.s + kBN - 1) / kBN;
+  const int t_mid = (n_item + 1) >> 1;
+  const int t_lo = (p.q_split && half == 1) ? t_mid : 0;
+  const int t_hi = (p.q_split && half == 0) ? t_mid : n_item;
   const int wave_last_q = min(it.q0 + 32, p.s) - 1;
-  const int wave_tiles = (it.q0 >= p.s) ? 0 : (CAUSAL ? wave_last_q / kBN + 1 : n_tiles);
+  const int wave_tiles = (it.q0 >= p.s) ? 0 : (CAUSAL ? wave_last_q / kBN + 1 : n_item);
 
   // direct loads: wave w, load i fills rows (w*kQLoads + i)*4 .. +3 of a tile
   int src[kQLoads];
@@ -242,102 +293,138 @@ __global__ __launch_bounds__(kQThreads, 1) void bwd_dq_kernel(BwdParams p) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) acc[db][r] = 0.f;
 
-  if (n_tiles > 0) load_tile(0, 0);
+  if (t_lo < t_hi) load_tile(t_lo, 0);
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
-  for (int t = 0; t < n_tiles; ++t) {
-    const int cur = t & 1;
-    if (t + 1 < n_tiles) load_tile(t + 1, cur ^ 1);
+  for (int t = t_lo; t < t_hi; ++t) {
+    const int cur = (t - t_lo) & 1;
+    if (t + 1 < t_hi) load_tile(t + 1, cur ^ 1);
     if (t < wave_tiles) {
       const uint8_t* kl = lds + cur * kTile;
       const uint8_t* vl = lds + (2 + cur) * kTile;
       const int k0 = t * kBN;
-      // S^T and dP^T blocks kb: keys k0 + 32 kb + (8 (r/4) + 4 hh + r%4), query my_q
-      f32x16 sc[2], dp[2];
+      // the tile's two 32-key halves in turn (kept apart to bound registers).
+      // S^T and dP^T of half kb: keys k0 + 32 kb + (8 (r/4) + 4 hh + r%4),
+      // query my_q
+#pragma unroll 1
+      for (int kb = 0; kb < 2; ++kb) {
+        const uint8_t* kh = kl + kb * 32 * ROW;
+        f32x16 sc, dp;
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
+        for (int r = 0; r < 16; ++r) sc[r] = dp[r] = 0.f;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) sc[kb][r] = dp[kb][r] = 0.f;
-#pragma unroll
-      for (int dk = 0; dk < D / 16; ++dk)
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
-          const bf16x8 ka = *(const bf16x8*)(kl + kb * 32 * ROW + ta.row_rd[dk]);
-          const bf16x8 va = *(const bf16x8*)(vl + kb * 32 * ROW + ta.row_rd[dk]);
-          sc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qf[dk], sc[kb], 0, 0, 0);
-          dp[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, gf[dk], dp[kb], 0, 0, 0);
+        for (int dk = 0; dk < D / 16; ++dk) {
+          const bf16x8 ka = *(const bf16x8*)(kh + ta.row_rd(dk));
+          const bf16x8 va = *(const bf16x8*)(vl + kb * 32 * ROW + ta.row_rd(dk));
+          sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qf[dk], sc, 0, 0, 0);
+          dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, gf[dk], dp, 0, 0, 0);
         }
-      const bool need_mask = (k0 + kBN > p.s) || (CAUSAL && k0 + kBN - 1 > it.q0);
-      bf16x8 dsb[kBN / 16];
+        const int kh0 = k0 + 32 * kb;
+        const bool need_mask = (kh0 + 32 > p.s) || (CAUSAL && kh0 + 31 > it.q0);
+        if (!need_mask) {
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const float pr = __builtin_amdgcn_exp2f(fmaf(sc[kb][r], p.c, -lse2));
-          float ds = pr * (dp[kb][r] - dlt);
-          if (need_mask) {
-            const int key = k0 + kb * 32 + 8 * (r >> 2) + 4 * hh + (r & 3);
-            if (key >= p.s || (CAUSAL && key > my_q)) ds = 0.f;
+          for (int r = 0; r < 16; ++r) {
+            const float pr = __builtin_amdgcn_exp2f(fmaf(sc[r], p.c, clse));
+            sc[r] = pr * (dp[r] + ndlt);
           }
-          sc[kb][r] = ds;
+        } else {
+          // masked entries are set to zero, not multiplied by it
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const float pr = __builtin_amdgcn_exp2f(fmaf(sc[r], p.c, clse));
+            const int key = kh0 + 8 * (r >> 2) + 4 * hh + (r & 3);
+            const float ds = pr * (dp[r] + ndlt);
+            sc[r] = (key >= p.s || (CAUSAL && key > my_q)) ? 0.f : ds;
+          }
         }
+        bf16x8 dsb[2];
 #pragma unroll
-      for (int ks = 0; ks < kBN / 16; ++ks)
+        for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
-        for (int e = 0; e < 8; ++e) dsb[ks][e] = (__bf16)sc[ks >> 1][(ks & 1) * 8 + e];
-      // dq^T += K^T dS^T, K^T read transposed from the K tile
+          for (int e = 0; e < 8; ++e) dsb[ks][e] = (__bf16)sc[ks * 8 + e];
+        // dq^T += K^T dS^T, K^T read transposed from the K tile
 #pragma unroll
-      for (int ks = 0; ks < kBN / 16; ++ks)
+        for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
-        for (int db = 0; db < D / 32; ++db)
-          acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(read_tr(kl, ta, ks, db), dsb[ks],
-                                                            acc[db], 0, 0, 0);
+          for (int db = 0; db < D / 32; ++db)
+            acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(read_tr(kh, ta, ks, db), dsb[ks],
+                                                              acc[db], 0, 0, 0);
+      }
     }
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
   }
+  if (p.q_split) {
+    store_part<D / 32>(p.part + (int64_t)blockIdx.x * kDqPart, acc, wave, lane);
+    return;
+  }
   store_t(rsrc(p.dq, p.q_bytes), acc, p.inv_sd, my_q, p.q_tok_bytes, q_head_off, hh);
 }
 
-// ------------------------------------------------------------------ dk, dv
-constexpr int kKWaves = 4;
-constexpr int kKThreads = 64 * kKWaves;
-constexpr int kKB = 32 * kKWaves;      // keys per workgroup
-constexpr int kQT = 32;                // queries per tile
-constexpr int kQTile = kQT * ROW;      // one Q or dout tile
-constexpr int kVBlock = kKB * ROW;     // the workgroup's V rows
-constexpr int kKLoads = kQT * CHUNKS / (64 * kKWaves);  // 16-byte loads per lane per tile tensor
-
+// The two halves of every dq item: added in a fixed order, scaled, rounded.
 template <bool CAUSAL>
-__global__ __launch_bounds__(kKThreads, 2) void bwd_dkv_kernel(BwdParams p) {
-  // LDS: V block, then Q0 Q1 dout0 dout1
-  __shared__ __attribute__((aligned(16))) uint8_t lds[kVBlock + 4 * kQTile];
-  uint8_t* vblk = lds;
-  uint8_t* qt = lds + kVBlock;
+__global__ __launch_bounds__(kThreads) void bwd_dq_merge_kernel(BwdParams p) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int l32 = lane & 31, hh = lane >> 5;
+  const QItem it = decode_q_item(p, blockIdx.x, wave, CAUSAL);
+  const float* u0 = p.part + (int64_t)(2 * blockIdx.x) * kDqPart;
+  f32x16 acc[D / 32];
+  add_parts<D / 32>(u0, u0 + kDqPart, acc, wave, lane);
+  store_t(rsrc(p.dq, p.q_bytes), acc, p.inv_sd, it.q0 + l32, p.q_tok_bytes,
+          (it.be * p.hp + it.head) * ROW, hh);
+}
 
-  // item: key block (lowest first when causal: the longest), then batch, KV
-  // head.  The first `slots` workgroups are resident together and the
-  // dispatcher gives workgroups p and p + slots/2 the same CU, so the second
-  // half of that first wave takes its ranks in reverse (longest with shortest).
-  int rank = blockIdx.x;
-  if (CAUSAL && p.slots > 0 && rank < p.slots && rank >= p.slots / 2)
-    rank = p.slots + p.slots / 2 - 1 - rank;
+// ------------------------------------------------------------------ dk, dv
+constexpr int kKB = 32 * kWaves;        // keys per workgroup
+constexpr int kQT = 64;                 // queries per step
+constexpr int kQTile = kQT * ROW;       // one Q or dout tile (16 KiB)
+constexpr int kVBlock = kKB * ROW;      // the workgroup's V rows (64 KiB)
+constexpr int kStatBuf = 2048;          // nlse (first 256 bytes of 1 KiB) then ndelta
+constexpr int kKLoads = kQT * CHUNKS / (64 * kWaves);   // loads per lane per tile tensor
+constexpr int kVLoads = kVBlock / (1024 * kWaves);      // loads per lane for the V block
+constexpr int kDkvPart = kWaves * 64 * D;               // floats of one split dkv unit
+constexpr int kDkvLds = kVBlock + 4 * kQTile + 2 * kStatBuf;
+
+struct KItem {
+  int kblk, be, kvg;
+};
+__device__ __forceinline__ KItem decode_k_item(const BwdParams& p, int rank) {
+  // key block (lowest first when causal: the longest), then batch, KV head
+  KItem it;
   const int per_k = p.b * p.hkvp;
-  const int kblk = rank / per_k;
-  const int kvg = (rank - kblk * per_k) % p.hkvp;
-  const int be = (rank - kblk * per_k) / p.hkvp;
-  const int kw0 = kblk * kKB + wave * 32;  // this wave's first key
+  it.kblk = rank / per_k;
+  it.kvg = (rank - it.kblk * per_k) % p.hkvp;
+  it.be = (rank - it.kblk * per_k) / p.hkvp;
+  return it;
+}
+
+template <bool CAUSAL>
+__global__ __launch_bounds__(kThreads, 1) void bwd_dkv_kernel(BwdParams p) {
+  // LDS: V block | Q0 Q1 | dout0 dout1 | stats0 stats1
+  __shared__ __attribute__((aligned(16))) uint8_t lds[kDkvLds];
+  uint8_t* vblk = lds;
+  uint8_t* qt = lds + kVBlock;
+  uint8_t* gt = qt + 2 * kQTile;
+  uint8_t* stt = gt + 2 * kQTile;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
+  const int l32 = lane & 31, hh = lane >> 5;
+  int rank = blockIdx.x, half = 0;
+  if (p.kv_split) {
+    half = rank & 1;
+    rank >>= 1;
+  }
+  const KItem it = decode_k_item(p, rank);
+  const int kw0 = it.kblk * kKB + wave * 32;  // this wave's first key
   const int my_key = kw0 + l32;
 
   const __amdgpu_buffer_rsrc_t rq = rsrc(p.q, p.q_bytes);
   const __amdgpu_buffer_rsrc_t rdo = rsrc(p.dout, p.q_bytes);
   const __amdgpu_buffer_rsrc_t rk = rsrc(p.k, p.kv_bytes);
   const __amdgpu_buffer_rsrc_t rv = rsrc(p.v, p.kv_bytes);
-  const __amdgpu_buffer_rsrc_t rst = rsrc(p.lse2, p.stat_bytes);
-  const __amdgpu_buffer_rsrc_t rde = rsrc(p.delta, p.stat_bytes);
-  const int kv_head_off = (be * p.hkvp + kvg) * ROW;
+  const __amdgpu_buffer_rsrc_t rst = rsrc(p.nlse, p.stat_bytes);
+  const __amdgpu_buffer_rsrc_t rde = rsrc(p.ndelta, p.stat_bytes);
+  const int kv_head_off = (it.be * p.hkvp + it.kvg) * ROW;
 
   // K^T fragments (B operand of S = Q K^T): key my_key, features 16 dk + 8 hh .. +7
   bf16x8 kf[D / 16];
@@ -347,23 +434,26 @@ __global__ __launch_bounds__(kKThreads, 2) void bwd_dkv_kernel(BwdParams p) {
     for (int dk = 0; dk < D / 16; ++dk)
       kf[dk] = as_bf16x8(__builtin_amdgcn_raw_buffer_load_b128(rk, off + dk * 32, 0, 0));
   }
-  // the workgroup's V rows into LDS (swizzled like the tiles): 32 KiB, 8 loads per wave
+  // the workgroup's V rows into LDS (swizzled like the tiles)
 #pragma unroll
-  for (int i = 0; i < kVBlock / (1024 * kKWaves); ++i) {
-    const int row = (wave * (kVBlock / (1024 * kKWaves)) + i) * 4 + lane / CHUNKS;
-    load_lds16(rv, vblk + (wave * (kVBlock / (1024 * kKWaves)) + i) * 1024,
-               (kblk * kKB + row) * p.kv_tok_bytes + kv_head_off +
+  for (int i = 0; i < kVLoads; ++i) {
+    const int row = (wave * kVLoads + i) * 4 + lane / CHUNKS;
+    load_lds16(rv, vblk + (wave * kVLoads + i) * 1024,
+               (it.kblk * kKB + row) * p.kv_tok_bytes + kv_head_off +
                    (((lane % CHUNKS) ^ dswz(row)) << 4));
   }
 #pragma unroll
   for (int dk = 0; dk < D / 16; ++dk) asm volatile("" ::"v"(kf[dk]));
 
-  // steps: (query head of the group, 32-query tile); causal tiles start at the
-  // workgroup's first key
-  const int t_first = CAUSAL ? (kblk * kKB) / kQT : 0;
+  // steps: (query head of the group, 64-query tile); causal tiles start at
+  // the workgroup's first key
+  const int t_first = CAUSAL ? (it.kblk * kKB) / kQT : 0;
   const int n_qt = (p.s + kQT - 1) / kQT;
   const int per_head = n_qt - t_first;
-  const int n_steps = (kblk * kKB < p.s) ? p.G * per_head : 0;
+  const int n_steps = (it.kblk * kKB < p.s) ? p.G * per_head : 0;
+  const int st_mid = (n_steps + 1) >> 1;
+  const int st_lo = (p.kv_split && half == 1) ? st_mid : 0;
+  const int st_hi = (p.kv_split && half == 0) ? st_mid : n_steps;
 
   int src[kKLoads];
 #pragma unroll
@@ -371,15 +461,26 @@ __global__ __launch_bounds__(kKThreads, 2) void bwd_dkv_kernel(BwdParams p) {
     const int row = (wave * kKLoads + i) * 4 + lane / CHUNKS;
     src[i] = row * p.q_tok_bytes + (((lane % CHUNKS) ^ dswz(row)) << 4);
   }
-  auto step_head = [&](int st) { return kvg * p.G + st / per_head; };
+  // statistics: lanes 0..15 of waves 0 (nlse) and 1 (ndelta) fetch the 64
+  // rows of the step, 16 bytes each; the other lanes read past the
+  // resource, which lands zeros in the rest of the 1 KiB slot
+  const __amdgpu_buffer_rsrc_t rstat = (wave == 0) ? rst : rde;
+  const int stat_lane = (lane < 16) ? lane * 16 : p.stat_bytes;
+  auto step_head = [&](int st) { return it.kvg * p.G + st / per_head; };
   auto step_q0 = [&](int st) { return (t_first + st % per_head) * kQT; };
   auto load_step = [&](int st, int buf) {
-    const int off = step_q0(st) * p.q_tok_bytes + (be * p.hp + step_head(st)) * ROW;
+    const int head = step_head(st), q0 = step_q0(st);
+    const int off = q0 * p.q_tok_bytes + (it.be * p.hp + head) * ROW;
 #pragma unroll
     for (int i = 0; i < kKLoads; ++i) {
       const int dst = (wave * kKLoads + i) * 1024;
       load_lds16(rq, qt + buf * kQTile + dst, src[i] + off);
-      load_lds16(rdo, qt + (2 + buf) * kQTile + dst, src[i] + off);
+      load_lds16(rdo, gt + buf * kQTile + dst, src[i] + off);
+    }
+    if (wave < 2) {
+      const int soff = (lane < 16) ? ((it.be * p.hp + head) * p.s_pad + q0) * 4 + stat_lane
+                                   : stat_lane;
+      load_lds16(rstat, stt + buf * kStatBuf + wave * 1024, soff);
     }
   };
   const TileAddr ta = tile_addr(lane);
@@ -390,58 +491,69 @@ __global__ __launch_bounds__(kKThreads, 2) void bwd_dkv_kernel(BwdParams p) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) dka[db][r] = dva[db][r] = 0.f;
 
-  if (n_steps > 0) load_step(0, 0);
+  if (st_lo < st_hi) load_step(st_lo, 0);
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
-  for (int st = 0; st < n_steps; ++st) {
-    const int cur = st & 1;
-    if (st + 1 < n_steps) load_step(st + 1, cur ^ 1);
-    const int head = step_head(st), q0 = step_q0(st);
-    // the wave's keys are all above this tile's queries: nothing to add
-    if (!(CAUSAL && q0 + kQT - 1 < kw0) && kw0 < p.s) {
-      const uint8_t* ql = qt + cur * kQTile;
-      const uint8_t* gl = qt + (2 + cur) * kQTile;
-      // lse2 and D of the 16 queries this lane's accumulator rows hold:
-      // q0 + 8 j + 4 hh + (0..3), j = 0..3
-      const int stat = ((be * p.hp + head) * p.s_pad + q0 + 4 * hh) * 4;
-      f32x4 l4[4], d4[4];
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        l4[j] = as_f32x4(__builtin_amdgcn_raw_buffer_load_b128(rst, stat + 32 * j, 0, 0));
-        d4[j] = as_f32x4(__builtin_amdgcn_raw_buffer_load_b128(rde, stat + 32 * j, 0, 0));
-      }
-      // S (queries x keys) and dP: rows q0 + 8 (r/4) + 4 hh + r%4, column my_key
+  const uint8_t* vrow = vblk + wave * 32 * ROW;  // this wave's V rows
+  for (int st = st_lo; st < st_hi; ++st) {
+    const int cur = (st - st_lo) & 1;
+    if (st + 1 < st_hi) load_step(st + 1, cur ^ 1);
+    const int q0 = step_q0(st);
+#pragma unroll 1
+    for (int hq = 0; hq < kQT / 32; ++hq) {
+      const int qr = q0 + 32 * hq;  // first query of this 32-query half
+      // the wave's keys all come after these queries (causal), or either
+      // side lies past the sequence: nothing to add
+      if ((CAUSAL && qr + 31 < kw0) || kw0 >= p.s || qr >= p.s) continue;
+      const uint8_t* ql = qt + cur * kQTile + hq * 32 * ROW;
+      const uint8_t* gl = gt + cur * kQTile + hq * 32 * ROW;
+      const float* sl = reinterpret_cast<const float*>(stt + cur * kStatBuf) + 32 * hq + 4 * hh;
+      // S (queries x keys) and dP: rows qr + 8 (r/4) + 4 hh + r%4, column
+      // my_key.  The accumulators start from the rows' statistics (broadcast
+      // reads), so they end as q.k - lse sqrt(d_h) and dP - D.
       f32x16 sc, dp;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) sc[r] = dp[r] = 0.f;
+      for (int j = 0; j < 4; ++j) {
+        const f32x4 l4 = *reinterpret_cast<const f32x4*>(sl + 8 * j);
+        const f32x4 d4 = *reinterpret_cast<const f32x4*>(sl + 256 + 8 * j);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          sc[4 * j + i] = l4[i];
+          dp[4 * j + i] = d4[i];
+        }
+      }
 #pragma unroll
       for (int dk = 0; dk < D / 16; ++dk) {
-        const bf16x8 qa = *(const bf16x8*)(ql + ta.row_rd[dk]);
-        const bf16x8 ga = *(const bf16x8*)(gl + ta.row_rd[dk]);
-        // V^T fragment of this lane's key from the V block (row-read addressing)
-        const bf16x8 vb = *(const bf16x8*)(vblk + wave * 32 * ROW + ta.row_rd[dk]);
+        const bf16x8 qa = *(const bf16x8*)(ql + ta.row_rd(dk));
+        const bf16x8 ga = *(const bf16x8*)(gl + ta.row_rd(dk));
+        const bf16x8 vb = *(const bf16x8*)(vrow + ta.row_rd(dk));
         sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa, kf[dk], sc, 0, 0, 0);
         dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ga, vb, dp, 0, 0, 0);
       }
-      const bool need_mask = (q0 + kQT > p.s) || (CAUSAL && q0 < kw0 + 31) || (kw0 + 32 > p.s);
-      bf16x8 pb[kQT / 16], dsb[kQT / 16];
+      const bool need_mask = (CAUSAL && qr < kw0 + 31) || (qr + 32 > p.s) || (kw0 + 32 > p.s);
+      if (!need_mask) {
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const float l2 = l4[r >> 2][r & 3];
-        const float dl = d4[r >> 2][r & 3];
-        // masked entries are set to zero, not multiplied by it: the statistics
-        // of query rows past the sequence are not defined
-        float pr = __builtin_amdgcn_exp2f(fmaf(sc[r], p.c, -l2));
-        float ds = pr * (dp[r] - dl);
-        if (need_mask) {
-          const int qq = q0 + 8 * (r >> 2) + 4 * hh + (r & 3);
-          if (qq >= p.s || my_key >= p.s || (CAUSAL && my_key > qq)) pr = ds = 0.f;
+        for (int r = 0; r < 16; ++r) {
+          const float pr = __builtin_amdgcn_exp2f(sc[r] * p.c);
+          sc[r] = pr;
+          dp[r] = pr * dp[r];
         }
-        sc[r] = pr;
-        dp[r] = ds;
-      }
+      } else {
+        // masked entries are set to zero, not multiplied by it: statistics
+        // of query rows past the sequence are not defined
 #pragma unroll
-      for (int ks = 0; ks < kQT / 16; ++ks)
+        for (int r = 0; r < 16; ++r) {
+          const float pr = __builtin_amdgcn_exp2f(sc[r] * p.c);
+          const float ds = pr * dp[r];
+          const int qq = qr + 8 * (r >> 2) + 4 * hh + (r & 3);
+          const bool off = qq >= p.s || my_key >= p.s || (CAUSAL && my_key > qq);
+          sc[r] = off ? 0.f : pr;
+          dp[r] = off ? 0.f : ds;
+        }
+      }
+      bf16x8 pb[2], dsb[2];
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
           pb[ks][e] = (__bf16)sc[ks * 8 + e];
@@ -449,7 +561,7 @@ __global__ __launch_bounds__(kKThreads, 2) void bwd_dkv_kernel(BwdParams p) {
         }
       // dv^T += dout^T P, dk^T += Q^T dS (tiles read transposed)
 #pragma unroll
-      for (int ks = 0; ks < kQT / 16; ++ks)
+      for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
         for (int db = 0; db < D / 32; ++db) {
           dva[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(read_tr(gl, ta, ks, db), pb[ks],
@@ -461,35 +573,94 @@ __global__ __launch_bounds__(kKThreads, 2) void bwd_dkv_kernel(BwdParams p) {
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
   }
+  if (p.kv_split) {
+    float* base = p.part + (int64_t)blockIdx.x * kDkvPart;
+    store_part<D / 32>(base, dka, wave, lane);
+    store_part<D / 32>(base + kDkvPart / 2, dva, wave, lane);
+    return;
+  }
   store_t(rsrc(p.dk, p.kv_bytes), dka, p.inv_sd, my_key, p.kv_tok_bytes, kv_head_off, hh);
   store_t(rsrc(p.dv, p.kv_bytes), dva, 1.f, my_key, p.kv_tok_bytes, kv_head_off, hh);
 }
 
-int64_t bwd_slots() {
+// The two halves of every dkv item: added in a fixed order, scaled, rounded.
+__global__ __launch_bounds__(kThreads) void bwd_dkv_merge_kernel(BwdParams p) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int l32 = lane & 31, hh = lane >> 5;
+  const KItem it = decode_k_item(p, blockIdx.x);
+  const int my_key = it.kblk * kKB + wave * 32 + l32;
+  const int kv_head_off = (it.be * p.hkvp + it.kvg) * ROW;
+  const float* u0 = p.part + (int64_t)(2 * blockIdx.x) * kDkvPart;
+  const float* u1 = u0 + kDkvPart;
+  f32x16 acc[D / 32];
+  add_parts<D / 32>(u0, u1, acc, wave, lane);
+  store_t(rsrc(p.dk, p.kv_bytes), acc, p.inv_sd, my_key, p.kv_tok_bytes, kv_head_off, hh);
+  add_parts<D / 32>(u0 + kDkvPart / 2, u1 + kDkvPart / 2, acc, wave, lane);
+  store_t(rsrc(p.dv, p.kv_bytes), acc, 1.f, my_key, p.kv_tok_bytes, kv_head_off, hh);
+}
+
+// Work layout for one call: statistics, split decisions, partial-sum bytes.
+struct BwdPlan {
+  int64_t s_pad, stat_floats;  // per statistic: b * hp * s_pad
+  int QH, QB, n_qblk, nsub, n_kblk;
+  int64_t q_items, k_items;
+  int q_split, kv_split;
+  int64_t part_offset, part_bytes;  // in the workspace
+};
+
+int64_t device_cus() {
   int dev = 0, cus = 0;
   if (hipGetDevice(&dev) != hipSuccess ||
       hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
     return 0;
-  return (int64_t)cus * 2;  // two 4-wave dkv workgroups per CU
+  return (int64_t)cus;
+}
+
+BwdPlan plan(const AttnBwdArgs& a) {
+  BwdPlan pl;
+  pl.s_pad = (a.s + 3) / 4 * 4;
+  pl.stat_floats = a.b * a.hp * pl.s_pad;
+  const int G = (int)(a.hp / a.hkvp);
+  pl.QH = (G % 8 == 0) ? 8 : (G % 4 == 0) ? 4 : (G % 2 == 0) ? 2 : 1;
+  pl.QB = 32 * (kWaves / pl.QH);
+  pl.n_qblk = (int)((a.s + pl.QB - 1) / pl.QB);
+  pl.nsub = G / pl.QH;
+  pl.n_kblk = (int)((a.s + kKB - 1) / kKB);
+  pl.q_items = (int64_t)pl.n_qblk * a.b * a.hkvp * pl.nsub;
+  pl.k_items = (int64_t)pl.n_kblk * a.b * a.hkvp;
+  // one 8-wave workgroup per CU: causal work with fewer than two items per
+  // CU is split, or the longest item alone would set the run time
+  const int64_t cus = device_cus();
+  pl.q_split = (a.causal && cus > 0 && pl.q_items < 2 * cus) ? 1 : 0;
+  pl.kv_split = (a.causal && cus > 0 && pl.k_items < 2 * cus) ? 1 : 0;
+  // the dq partials are consumed by their merge before the dkv kernel runs,
+  // so both use the same region
+  const int64_t qpart = pl.q_split ? pl.q_items * 2 * kDqPart * 4 : 0;
+  const int64_t kpart = pl.kv_split ? pl.k_items * 2 * kDkvPart * 4 : 0;
+  pl.part_offset = (2 * pl.stat_floats * 4 + 255) / 256 * 256;
+  pl.part_bytes = qpart > kpart ? qpart : kpart;
+  return pl;
 }
 
 }  // namespace
 
 int64_t attn_bwd_bf16_workspace_size(const AttnBwdArgs& a) {
-  const int64_t s_pad = (a.s + 3) / 4 * 4;
-  return 2 * a.b * a.hp * s_pad * (int64_t)sizeof(float);
+  const BwdPlan pl = plan(a);
+  return pl.part_bytes > 0 ? pl.part_offset + pl.part_bytes : 2 * pl.stat_floats * 4;
 }
 
 hipError_t launch_attn_bwd_bf16(const AttnBwdArgs& a, hipStream_t stream) {
   if (a.d != D) return hipErrorInvalidValue;
-  const int64_t s_pad = (a.s + 3) / 4 * 4;
-  float* delta = static_cast<float*>(a.workspace);
-  float* lse2 = delta + a.b * a.hp * s_pad;
+  const BwdPlan pl = plan(a);
+  float* ndelta = static_cast<float*>(a.workspace);
+  float* nlse = ndelta + pl.stat_floats;
   const int64_t rows = a.s * a.b * a.hp;
   if (rows <= 0) return hipSuccess;
+  if (pl.q_items > 0x3FFFFFFF || pl.k_items > 0x3FFFFFFF) return hipErrorInvalidValue;
   hipLaunchKernelGGL(bwd_prep_kernel, dim3((unsigned)((rows * 16 + 255) / 256)), dim3(256), 0,
-                     stream, (const uint16_t*)a.o, (const uint16_t*)a.dout, a.lse, delta, lse2,
-                     (int)rows, (int)a.s, (int)s_pad, (int)(a.b * a.hp));
+                     stream, (const uint16_t*)a.o, (const uint16_t*)a.dout, a.lse, ndelta, nlse,
+                     (int)rows, (int)a.s, (int)pl.s_pad, (int)(a.b * a.hp),
+                     (float)sqrt((double)D));
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
 
@@ -498,11 +669,14 @@ hipError_t launch_attn_bwd_bf16(const AttnBwdArgs& a, hipStream_t stream) {
   p.k = (const uint16_t*)a.k;
   p.v = (const uint16_t*)a.v;
   p.dout = (const uint16_t*)a.dout;
-  p.delta = delta;
-  p.lse2 = lse2;
+  p.ndelta = ndelta;
+  p.nlse = nlse;
   p.dq = (uint16_t*)a.dq;
   p.dk = (uint16_t*)a.dk;
   p.dv = (uint16_t*)a.dv;
+  p.part = pl.part_bytes > 0
+               ? reinterpret_cast<float*>(static_cast<uint8_t*>(a.workspace) + pl.part_offset)
+               : nullptr;
   p.s = (int)a.s;
   p.b = (int)a.b;
   p.hp = (int)a.hp;
@@ -512,26 +686,32 @@ hipError_t launch_attn_bwd_bf16(const AttnBwdArgs& a, hipStream_t stream) {
   p.kv_tok_bytes = (int)(a.b * a.hkvp * ROW);
   p.q_bytes = (int)(a.s * a.b * a.hp * ROW);
   p.kv_bytes = (int)(a.s * a.b * a.hkvp * ROW);
-  p.s_pad = (int)s_pad;
-  p.stat_bytes = (int)(a.b * a.hp * s_pad * 4);
+  p.s_pad = (int)pl.s_pad;
+  p.stat_bytes = (int)(pl.stat_floats * 4);
   p.c = (float)(1.4426950408889634 / sqrt((double)D));
   p.inv_sd = (float)(1.0 / sqrt((double)D));
-  p.QH = (p.G % 8 == 0) ? 8 : (p.G % 4 == 0) ? 4 : (p.G % 2 == 0) ? 2 : 1;
-  p.QB = 32 * (kQWaves / p.QH);
-  p.n_qblk = (p.s + p.QB - 1) / p.QB;
-  p.nsub = p.G / p.QH;
-  p.n_kblk = (p.s + kKB - 1) / kKB;
-  const int64_t q_items = (int64_t)p.n_qblk * p.b * p.hkvp * p.nsub;
-  const int64_t k_items = (int64_t)p.n_kblk * p.b * p.hkvp;
-  const int64_t slots = bwd_slots();
-  p.slots = (slots > 0 && k_items >= slots && (slots % 2) == 0) ? (int)slots : 0;
+  p.QH = pl.QH;
+  p.QB = pl.QB;
+  p.n_qblk = pl.n_qblk;
+  p.nsub = pl.nsub;
+  p.n_kblk = pl.n_kblk;
+  p.q_split = pl.q_split;
+  p.kv_split = pl.kv_split;
+  const unsigned q_grid = (unsigned)(pl.q_items << pl.q_split);
+  const unsigned k_grid = (unsigned)(pl.k_items << pl.kv_split);
   if (a.causal) {
-    hipLaunchKernelGGL(bwd_dq_kernel<true>, dim3((unsigned)q_items), dim3(kQThreads), 0, stream, p);
-    hipLaunchKernelGGL(bwd_dkv_kernel<true>, dim3((unsigned)k_items), dim3(kKThreads), 0, stream, p);
+    hipLaunchKernelGGL(bwd_dq_kernel<true>, dim3(q_grid), dim3(kThreads), 0, stream, p);
+    if (pl.q_split)
+      hipLaunchKernelGGL(bwd_dq_merge_kernel<true>, dim3((unsigned)pl.q_items), dim3(kThreads), 0,
+                         stream, p);
+    hipLaunchKernelGGL(bwd_dkv_kernel<true>, dim3(k_grid), dim3(kThreads), 0, stream, p);
   } else {
-    hipLaunchKernelGGL(bwd_dq_kernel<false>, dim3((unsigned)q_items), dim3(kQThreads), 0, stream, p);
-    hipLaunchKernelGGL(bwd_dkv_kernel<false>, dim3((unsigned)k_items), dim3(kKThreads), 0, stream, p);
+    hipLaunchKernelGGL(bwd_dq_kernel<false>, dim3(q_grid), dim3(kThreads), 0, stream, p);
+    hipLaunchKernelGGL(bwd_dkv_kernel<false>, dim3(k_grid), dim3(kThreads), 0, stream, p);
   }
+  if (pl.kv_split)
+    hipLaunchKernelGGL(bwd_dkv_merge_kernel, dim3((unsigned)pl.k_items), dim3(kThreads), 0, stream,
+                       p);
   return hipGetLastError();
 }
 
