@@ -10,6 +10,10 @@ Every function follows a passage of the pages cited in ``ulys_oracle.c``:
     ("02 · DeepSpeed-Ulysses", §2 "all-to-all 的转置与重分布");
   * ``seq2head`` / ``head2seq``  -- the whole exchange across P emulated ranks
     (same section; "5. AllToAll（全交换）" of the collectives tutorial);
+  * ``pack_kv`` / ``unpack_kv_sum`` -- K/V send side when there are fewer KV heads
+    than ranks (each head replicated to the ranks whose queries use it) and its
+    backward (the copies' gradients summed) ("Ulysses vs Ring Attention", §三;
+    "长上下文训练中的 SP 与 CP", Ulysses section);
   * ``attn`` / ``attn_rows``     -- softmax(Q K^T / sqrt(d_h)) V per head, dense
     or causal (j <= t), GQA by contiguous groups ("DeepSpeed-Ulysses 深度解析",
     core design step 4), in fp64.
@@ -56,10 +60,13 @@ def load(path: str | None = None) -> ctypes.CDLL:
 
 def _bind(lib: ctypes.CDLL) -> ctypes.CDLL:
     lay = [_vp, _vp, _c_i64, _c_i64, _c_i64, _c_i64, _c_i64, _c_i64]
-    for name in ("orc_pack", "orc_unpack", "orc_seq2head", "orc_head2seq"):
+    for name in ("orc_pack", "orc_unpack", "orc_seq2head", "orc_head2seq", "orc_pack_kv"):
         fn = getattr(lib, name)
         fn.argtypes = lay
         fn.restype = ctypes.c_int
+    lib.orc_unpack_kv_sum.argtypes = [_vp, _vp, _c_i64, _c_i64, _c_i64, _c_i64, _c_i64,
+                                      ctypes.c_int]
+    lib.orc_unpack_kv_sum.restype = ctypes.c_int
     lib.orc_attn.argtypes = [_vp, _vp, _vp, _vp, _vp, _c_i64, _c_i64, _c_i64, _c_i64,
                              _c_i64, _c_i64, ctypes.c_int, ctypes.c_int, ctypes.c_int]
     lib.orc_attn.restype = ctypes.c_int
@@ -138,6 +145,35 @@ def head2seq(y_all: np.ndarray, s: int, b: int, h: int, d: int, P: int, lib=None
     x = np.empty(y_all.size, dtype=y_all.dtype)
     _check(lib.orc_head2seq(_ptr(y_all), _ptr(x), s, b, h, d, P, y_all.itemsize), "head2seq")
     return x.reshape(P, s // P, b, h, d)
+
+
+def kv_heads_per_rank(h_kv: int, P: int) -> int:
+    """KV heads in one rank's share: h_kv/P, or 1 when each head is replicated."""
+    return h_kv // P if h_kv % P == 0 else 1
+
+
+def pack_kv(x: np.ndarray, s: int, b: int, h_kv: int, d: int, P: int, lib=None) -> np.ndarray:
+    """K or V shard [s/P,b,h_kv,d] -> send buffer [P,s/P,b,max(1,h_kv/P),d]; with
+    h_kv < P rank r's block is KV head floor(r*h_kv/P) (replication)."""
+    lib = lib or load()
+    x = _contig(x)
+    hk = kv_heads_per_rank(h_kv, P)
+    y = np.empty(P * (s // P) * b * hk * d, dtype=x.dtype)
+    _check(lib.orc_pack_kv(_ptr(x), _ptr(y), s, b, h_kv, d, P, x.itemsize), "pack_kv")
+    return y.reshape(P, s // P, b, hk, d)
+
+
+def unpack_kv_sum(y: np.ndarray, s: int, b: int, h_kv: int, d: int, P: int,
+                  lib=None) -> np.ndarray:
+    """Gradient blocks [P,s/P,b,max(1,h_kv/P),d] (float32 or bf16 bits) -> [s/P,b,h_kv,d];
+    with h_kv < P the blocks of the ranks sharing a KV head are summed (exactly,
+    rounded once)."""
+    lib = lib or load()
+    y = _contig(y)
+    x = np.empty((s // P) * b * h_kv * d, dtype=y.dtype)
+    _check(lib.orc_unpack_kv_sum(_ptr(y), _ptr(x), s, b, h_kv, d, P, _dtype_code(y)),
+           "unpack_kv_sum")
+    return x.reshape(s // P, b, h_kv, d)
 
 
 # ----------------------------------------------------------------------------- attention

@@ -17,6 +17,8 @@
  *            section "Ulysses：用 All-to-All 把序列分片换成 head 分片".
  *   [COLL]   "【深度长文】大模型分布式训练通信原语及其应用", primitive
  *            "5. AllToAll（全交换）".
+ *   [CMP]    "Ulysses vs Ring Attention：序列并行深度对比", §三 (Q, K and V
+ *            take the same all-to-all; SP is capped by num_kv_heads).
  *
  * Conventions (row-major, last axis fastest):
  *   rank-local shard   x  [s/P, b, h, d]
@@ -153,6 +155,102 @@ int orc_head2seq(const void *Y_all, void *X_all, int64_t s, int64_t b, int64_t h
               int64_t xi = (((j * sl + t) * b + be) * h + (r * hp + k)) * d + e;
               memcpy(dst + xi * elt, src + yi * elt, (size_t)elt);
             }
+  return ORC_OK;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Fewer KV heads than ranks: replication and its backward                  */
+/* ------------------------------------------------------------------------ */
+
+/*
+ * Send side of the seq->head all-to-all for K or V when the model has fewer
+ * KV heads than ranks.  [CMP] §三: Q, K and V take the same all-to-all, so
+ * with one KV head on four ranks three ranks would receive no KV head at all;
+ * [SPCP] (Ulysses section): replicating KV heads lifts the requirement that
+ * P divide the KV head count, at a cost in memory and traffic; [DSU]:
+ * num_kv_heads is passed when the heads do not divide evenly.  Reading
+ * taken: with h_kv < P and h_kv | P, rank r receives KV head
+ * floor(r * h_kv / P) -- the head its query heads [r*h/P, (r+1)*h/P) use
+ * under the contiguous grouping -- so the send buffer holds P blocks of one
+ * head each: y[r] = x[:, :, floor(r*h_kv/P), :].  With P | h_kv it is
+ * orc_pack.
+ *   x [s/P, b, h_kv, d]  ->  y [P, s/P, b, max(1, h_kv/P), d]
+ */
+int orc_pack_kv(const void *x, void *y, int64_t s, int64_t b, int64_t h_kv, int64_t d,
+                int64_t P, int64_t elt) {
+  if (s <= 0 || b <= 0 || h_kv <= 0 || d <= 0 || P <= 0 || elt <= 0) return ORC_EARG;
+  if (h_kv % P == 0) return orc_pack(x, y, s, b, h_kv, d, P, elt);
+  if (P % h_kv != 0 || s % P != 0) return ORC_EARG;
+  const int64_t sl = s / P;
+  const char *src = (const char *)x;
+  char *dst = (char *)y;
+  for (int64_t r = 0; r < P; ++r) {
+    const int64_t g = r * h_kv / P; /* the KV head rank r's queries read */
+    for (int64_t t = 0; t < sl; ++t)
+      for (int64_t be = 0; be < b; ++be)
+        for (int64_t e = 0; e < d; ++e) {
+          int64_t yi = ((r * sl + t) * b + be) * d + e;
+          int64_t xi = ((t * b + be) * h_kv + g) * d + e;
+          memcpy(dst + yi * elt, src + xi * elt, (size_t)elt);
+        }
+  }
+  return ORC_OK;
+}
+
+static double widen(const void *base, int dtype, int64_t i);
+
+/* Nearest-even rounding of a double to bf16 bits, from the format's
+ * definition: 8 significant bits for normal numbers, multiples of 2^-133
+ * below 2^-126, infinity past the largest finite value. */
+static uint16_t round_bf16(double v) {
+  if (isnan(v)) return 0x7FC0;
+  const double a = fabs(v);
+  double q;
+  if (a < ldexp(1.0, -126)) {
+    q = nearbyint(a * ldexp(1.0, 133)) * ldexp(1.0, -133);
+  } else {
+    int e;
+    const double m = frexp(a, &e); /* a = m 2^e, m in [0.5, 1) */
+    q = ldexp(nearbyint(ldexp(m, 8)), e - 8);
+  }
+  float f = (float)q; /* exact: q has at most 8 significant bits, or is out of range */
+  if (q >= ldexp(1.0, 128)) f = INFINITY;
+  uint32_t u;
+  memcpy(&u, &f, sizeof u);
+  return (uint16_t)((u >> 16) | (v < 0 ? 0x8000u : 0u));
+}
+
+/*
+ * Backward of orc_pack_kv, receive side: the gradient blocks sent back by the
+ * P ranks (block r is the gradient of KV head floor(r*h_kv/P) seen by rank
+ * r's queries) are summed per KV head -- the gradient of a replicated value
+ * is the sum of its copies' gradients ([SPCP]: a K/V row used by many queries
+ * receives the sum of their gradients).  The sum is exact in fp64 and rounded
+ * once to the dtype (0 fp32, 1 bf16 bits).  With P | h_kv it is orc_unpack.
+ *   y [P, s/P, b, max(1, h_kv/P), d]  ->  x [s/P, b, h_kv, d]
+ */
+int orc_unpack_kv_sum(const void *y, void *x, int64_t s, int64_t b, int64_t h_kv, int64_t d,
+                      int64_t P, int dtype) {
+  if (dtype != 0 && dtype != 1) return ORC_EARG;
+  const int64_t elt = dtype == 0 ? 4 : 2;
+  if (s <= 0 || b <= 0 || h_kv <= 0 || d <= 0 || P <= 0) return ORC_EARG;
+  if (h_kv % P == 0) return orc_unpack(y, x, s, b, h_kv, d, P, elt);
+  if (P % h_kv != 0 || s % P != 0) return ORC_EARG;
+  const int64_t sl = s / P, R = P / h_kv;
+  for (int64_t t = 0; t < sl; ++t)
+    for (int64_t be = 0; be < b; ++be)
+      for (int64_t g = 0; g < h_kv; ++g)
+        for (int64_t e = 0; e < d; ++e) {
+          double acc = 0.0;
+          for (int64_t r = g * R; r < (g + 1) * R; ++r) /* the ranks holding head g */
+            acc += widen(y, dtype, ((r * sl + t) * b + be) * d + e);
+          const int64_t xi = ((t * b + be) * h_kv + g) * d + e;
+          if (dtype == 0) {
+            ((float *)x)[xi] = (float)acc;
+          } else {
+            ((uint16_t *)x)[xi] = round_bf16(acc);
+          }
+        }
   return ORC_OK;
 }
 

@@ -483,4 +483,152 @@ ATTN_PINS = [pin_attn_vs_torch, pin_attn_large_scores, pin_attn_closed_forms,
              pin_rows_match_full]
 BWD_PINS = [pin_bwd_finite_differences, pin_bwd_vs_torch, pin_bwd_closed_forms,
             pin_bwd_rows_match_full, pin_bwd_sharded_chain]
-ALL_PINS = LAYOUT_PINS + ATTN_PINS + BWD_PINS
+# ---------------------------------------------------------------------------- KV replication pins
+def _route(blocks_per_rank, P):
+    """The exchange's routing: rank r receives block r of every sender j, in
+    source order, concatenated along the sequence."""
+    return [np.concatenate([blocks_per_rank[j][r] for j in range(P)], axis=0) for r in range(P)]
+
+
+def pin_kv_replication_example(lib):
+    """One KV head on four ranks: the plain head split leaves ranks 1-3 with no
+    KV head; with replication every rank holds the head's whole sequence."""
+    rows = _read_golden("kv_replication_1head_4rank.txt")
+    P, s, b, h_kv, d = 4, 4, 1, 1, 1
+    heads = [int(t) for t in rows[0].split(":")[1].split()]
+    # the plain split of the head axis into P parts (the first parts take the
+    # remainder) -- what the page shows -- and the basic method rejects it
+    assert heads == [len(part) for part in np.array_split(np.arange(h_kv), P)]
+    with np.testing.assert_raises(ValueError):
+        oracle.pack(np.zeros(1, np.uint16), s, b, h_kv, d, P, lib=lib)
+    code = {f"K{j}": 0x100 + j for j in range(P)}
+    shards, expect = {}, {}
+    for r in rows[1:]:
+        rank, rest = r.split(":")
+        lhs, rhs = rest.split("->")
+        shards[int(rank)] = np.array([code[t] for t in lhs.split()], dtype=np.uint16)
+        expect[int(rank)] = [code[t] for t in rhs.split()]
+    sent = [oracle.pack_kv(shards[j].reshape(1, 1, 1, 1), s, b, h_kv, d, P, lib=lib)
+            for j in range(P)]
+    got = _route(sent, P)
+    for r in range(P):
+        assert got[r].reshape(-1).tolist() == expect[r], (r, got[r].reshape(-1))
+
+
+def pin_pack_kv_brute_force(lib):
+    """Every tiny shape with h_kv < P, P | h_kv * k, values equal to their flat
+    index: rank r's block is KV head r*h_kv//P (numpy indexing); with P | h_kv
+    the replicated pack is the plain one."""
+    for P in (2, 3, 4, 6, 8):
+        for h_kv in range(1, 2 * P + 1):
+            if not (h_kv % P == 0 or P % h_kv == 0):
+                continue
+            for b in (1, 2):
+                s, d = 2 * P, 3
+                x = np.arange((s // P) * b * h_kv * d, dtype=np.int32).reshape(s // P, b, h_kv, d)
+                y = oracle.pack_kv(x, s, b, h_kv, d, P, lib=lib)
+                if h_kv % P == 0:
+                    ref = np_pack(x, s, b, h_kv, d, P)
+                else:
+                    ref = np.stack([x[:, :, r * h_kv // P][:, :, None] for r in range(P)])
+                assert y.shape == ref.shape and np.array_equal(y, ref), (P, h_kv, b)
+
+
+def _bf16_rne_bits(f32):
+    """float32 -> bf16 bits, nearest-even, by the usual integer trick."""
+    u = np.ascontiguousarray(f32, dtype=np.float32).view(np.uint32).astype(np.uint64)
+    return ((u + 0x7FFF + ((u >> 16) & 1)) >> 16).astype(np.uint16)
+
+
+def pin_unpack_kv_sum(lib):
+    """Backward of the replication.  Replicate-then-sum multiplies by R = P/h_kv
+    exactly (R a power of two); with P | h_kv it is the plain unpack; and a sum
+    of R = 2 bf16 blocks (exact in float32 when the exponents are close) rounds
+    like the independent integer nearest-even conversion."""
+    for P, h_kv in ((4, 1), (8, 2), (8, 4), (16, 4)):
+        s, b, d = 2 * P, 2, 8
+        R = P // h_kv
+        for dt in ("f32", "bf16"):
+            x = synth.tensor(1700 + P + h_kv, (s // P, b, h_kv, d), dt)
+            y = oracle.pack_kv(x, s, b, h_kv, d, P, lib=lib)
+            z = oracle.unpack_kv_sum(y, s, b, h_kv, d, P, lib=lib)
+            assert np.array_equal(widen(z), R * widen(x)), (P, h_kv, dt)
+    s, b, d, P, h_kv = 8, 1, 4, 4, 4
+    x = synth.tensor(1710, (s // P, b, h_kv, d), "bf16")
+    y = oracle.pack_kv(x, s, b, h_kv, d, P, lib=lib)
+    assert np.array_equal(oracle.unpack_kv_sum(y, s, b, h_kv, d, P, lib=lib), x)
+    # rounding: blocks with magnitudes in [1, 2) so that pair sums are exact in float32
+    P, h_kv, s, b, d = 4, 2, 4, 1, 64
+    mags = 1.0 + synth.uniform01(1720, P * d).astype(np.float32)
+    signs = np.where(synth.uniform01(1721, P * d) < 0.5, -1.0, 1.0).astype(np.float32)
+    y = _bf16_rne_bits(mags * signs).reshape(P, 1, b, 1, d)
+    got = oracle.unpack_kv_sum(y, s, b, h_kv, d, P, lib=lib)
+    yf = widen(y).astype(np.float32).reshape(P, d)
+    for g in range(h_kv):
+        ref = _bf16_rne_bits(yf[2 * g] + yf[2 * g + 1])
+        assert np.array_equal(got[0, 0, g], ref), g
+
+
+def _gqa_case(seed, s, b, h, h_kv, d, dt):
+    q = synth.tensor(seed, (s, b, h, d), dt)
+    k = synth.tensor(seed + 1, (s, b, h_kv, d), dt)
+    v = synth.tensor(seed + 2, (s, b, h_kv, d), dt)
+    return q, k, v
+
+
+def pin_kv_replication_head_independence(lib):
+    """Unsharded GQA attention with fewer KV heads than ranks, sliced to rank
+    r's query heads, equals rank r's attention on its exchanged share, whose
+    single KV head arrived by replication (bit for bit in the oracle)."""
+    for (s, b, h, h_kv, P, causal) in ((16, 1, 8, 2, 4, True), (12, 2, 8, 1, 4, False),
+                                       (16, 1, 16, 2, 8, True)):
+        d = 8
+        q, k, v = _gqa_case(1730 + h_kv, s, b, h, h_kv, d, "bf16")
+        o_full, lse_full = oracle.attn(q, k, v, s, b, h, h_kv, d, 1, causal, lib=lib)
+        sl, hp = s // P, h // P
+        qs = _route([oracle.pack(q[j * sl:(j + 1) * sl], s, b, h, d, P, lib=lib)
+                     for j in range(P)], P)
+        ks = _route([oracle.pack_kv(k[j * sl:(j + 1) * sl], s, b, h_kv, d, P, lib=lib)
+                     for j in range(P)], P)
+        vs = _route([oracle.pack_kv(v[j * sl:(j + 1) * sl], s, b, h_kv, d, P, lib=lib)
+                     for j in range(P)], P)
+        for r in range(P):
+            # one KV head per share: the attention of the share has h_kv_eff = P
+            o, lse = oracle.attn(qs[r], ks[r], vs[r], s, b, h, P, d, P, causal, lib=lib)
+            assert np.array_equal(o, o_full[:, :, r * hp:(r + 1) * hp]), (r, s, h_kv)
+            assert np.array_equal(lse, lse_full[:, r * hp:(r + 1) * hp]), (r, s, h_kv)
+
+
+def pin_kv_replication_backward_chain(lib):
+    """The backward with replicated KV heads: each rank's dK, dV (fp64, rounded
+    to float32) go back through the head->seq exchange and the copies of a KV
+    head are summed (unpack_kv_sum); the result equals the unsharded
+    gradients to float32 rounding."""
+    s, b, h, h_kv, P, d = 16, 1, 8, 2, 4, 8
+    sl = s // P
+    for causal in (False, True):
+        q, k, v = _gqa_case(1740, s, b, h, h_kv, d, "f32")
+        dout = synth.tensor(1743, (s, b, h, d), "f32")
+        _, dk_f, dv_f = oracle.attn_bwd(q, k, v, dout, s, b, h, h_kv, d, 1, causal, lib=lib)
+        share = lambda t, kv: _route([(oracle.pack_kv if kv else oracle.pack)(  # noqa: E731
+            t[j * sl:(j + 1) * sl], s, b, h_kv if kv else h, d, P, lib=lib) for j in range(P)], P)
+        qs, ks, vs, gs = share(q, False), share(k, True), share(v, True), share(dout, False)
+        dks, dvs = [], []
+        for r in range(P):
+            _, dk, dv = oracle.attn_bwd(qs[r], ks[r], vs[r], gs[r], s, b, h, P, d, P, causal,
+                                        lib=lib)
+            dks.append(dk.astype(np.float32))
+            dvs.append(dv.astype(np.float32))
+        for grads, full in ((dks, dk_f), (dvs, dv_f)):
+            for j in range(P):  # rank j gets sequence segment j of every rank's gradient
+                recv = np.stack([grads[r][j * sl:(j + 1) * sl] for r in range(P)])
+                got = oracle.unpack_kv_sum(recv, s, b, h_kv, d, P, lib=lib).astype(np.float64)
+                ref = full[j * sl:(j + 1) * sl]
+                assert np.max(np.abs(got - ref)) <= 4e-7 * max(1.0, np.max(np.abs(ref))), \
+                    (causal, j)
+
+
+KV_PINS = [pin_kv_replication_example, pin_pack_kv_brute_force, pin_unpack_kv_sum,
+           pin_kv_replication_head_independence, pin_kv_replication_backward_chain]
+
+ALL_PINS = LAYOUT_PINS + ATTN_PINS + BWD_PINS + KV_PINS

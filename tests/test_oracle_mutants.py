@@ -52,6 +52,13 @@ MUTANTS = [
      "for (int64_t t = J->causal ? j + 1 : 0; t < s; ++t) {"),
     ("bwd_dk_uses_dout", "dqrow[e] += ds * krow[e] * scale;\n            dkrow[e] += ds * qrow[e] * scale;",
      "dqrow[e] += ds * krow[e] * scale;\n            dkrow[e] += ds * drow[e] * scale;"),
+    # KV replication and its backward
+    ("pack_kv_strided_heads", "const int64_t g = r * h_kv / P; /* the KV head",
+     "const int64_t g = r % h_kv; /* the KV head"),
+    ("unpack_kv_sum_drops_a_copy", "for (int64_t r = g * R; r < (g + 1) * R; ++r) /* the ranks",
+     "for (int64_t r = g * R; r < (g + 1) * R - 1; ++r) /* the ranks"),
+    ("round_bf16_truncates", "q = ldexp(nearbyint(ldexp(m, 8)), e - 8);",
+     "q = ldexp(floor(ldexp(m, 8)), e - 8);"),
 ]
 
 
