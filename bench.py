@@ -173,9 +173,12 @@ def bench_backward(args, w, binding, torch, np, q, k, v, code, stream):
                                    int(w.causal), code, ws.data_ptr(), nbytes, sh), "attn bwd")
         if record:
             e[2].record(stream)
-        for src, dst, hh in ((dq, xdq, w.h), (dk, xdk, w.h_kv), (dv, xdv, w.h_kv)):
-            call(binding.ulys_unpack_head2seq(src.data_ptr(), dst.data_ptr(), w.s, w.b, hh, w.d,
-                                              w.P, code, sh), "unpack grad")
+        call(binding.ulys_unpack_head2seq(dq.data_ptr(), xdq.data_ptr(), w.s, w.b, w.h, w.d,
+                                          w.P, code, sh), "unpack dq")
+        # dK, dV: with replicated KV heads the copies' gradients are summed
+        for src, dst in ((dk, xdk), (dv, xdv)):
+            call(binding.ulys_unpack_head2seq_kv(src.data_ptr(), dst.data_ptr(), w.s, w.b,
+                                                 w.h_kv, w.d, w.P, code, sh), "unpack dkv")
         if record:
             e.append(torch.cuda.Event(enable_timing=True))
             e[3].record(stream)
@@ -192,7 +195,7 @@ def bench_backward(args, w, binding, torch, np, q, k, v, code, stream):
     attn_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in marks]))
     layout_ms = float(np.mean([e[0].elapsed_time(e[1]) + e[2].elapsed_time(e[3]) for e in marks]))
     flops = w.attn_bwd_flops()
-    layout_bytes = 2 * (2 * w.shard_bytes() + 2 * w.shard_bytes(kv=True))
+    layout_bytes = w.layout_bytes()  # pack dO + unpack dQ: as pack Q + unpack O; dK, dV as K, V
     return {
         "steps": args.bwd_steps, "ms_per_step": round(ms_step, 4),
         "tflops_step": round(flops / (ms_step * 1e-3) / 1e12, 2),
@@ -272,10 +275,12 @@ def main():
             e[0].record(stream)
         call(binding.ulys_pack_seq2head(xq.data_ptr(), yq.data_ptr(), w.s, w.b, w.h, w.d, w.P,
                                         code, sh), "pack q")
-        call(binding.ulys_pack_seq2head(xk.data_ptr(), yk.data_ptr(), w.s, w.b, w.h_kv, w.d,
-                                        w.P, code, sh), "pack k")
-        call(binding.ulys_pack_seq2head(xv.data_ptr(), yv.data_ptr(), w.s, w.b, w.h_kv, w.d,
-                                        w.P, code, sh), "pack v")
+        # K and V: the plain pack, or with fewer KV heads than ranks the
+        # replicating one (the same kernel when P | h_kv)
+        call(binding.ulys_pack_seq2head_kv(xk.data_ptr(), yk.data_ptr(), w.s, w.b, w.h_kv, w.d,
+                                           w.P, code, sh), "pack k")
+        call(binding.ulys_pack_seq2head_kv(xv.data_ptr(), yv.data_ptr(), w.s, w.b, w.h_kv, w.d,
+                                           w.P, code, sh), "pack v")
         if record:
             e[1].record(stream)
         # the send buffers stand in for the receive buffers: [P, s/P, b, hp, d] == [s, b, hp, d]
@@ -310,7 +315,7 @@ def main():
     flops = w.attn_flops()
     attn_tflops = flops / (attn_ms * 1e-3) / 1e12
     peak = PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_F32_TFLOPS
-    pack_bytes = 2 * (w.shard_bytes() + 2 * w.shard_bytes(kv=True))
+    pack_bytes = 2 * w.shard_bytes() + 2 * (w.shard_bytes(kv=True) + w.kv_blocks_bytes())
     unpack_bytes = 2 * w.shard_bytes()
     pack_gbps = pack_bytes / (pack_ms * 1e-3) / 1e9
     unpack_gbps = unpack_bytes / (unpack_ms * 1e-3) / 1e9

@@ -10,6 +10,8 @@
  *   [DSU]   "DeepSpeed-Ulysses 深度解析：用 All-to-All 序列并行撑起百万 Token
  *           超长序列训练", core design steps 1-5 and the DistributedAttention
  *           signature (scatter_idx, gather_idx, sp_stream, num_kv_heads).
+ *   [CMP]   "Ulysses vs Ring Attention：序列并行深度对比", §三 (Q, K and V take
+ *           the same all-to-all; Ulysses' degree is capped by num_kv_heads).
  *   [SPCP]  "长上下文训练中的 SP 与 CP：从 Megatron 到分布式 Attention",
  *           the Ulysses section (P must divide the KV head count under GQA)
  *           and the Ring section (online softmax, scale 1/sqrt(d_h)).
@@ -21,7 +23,8 @@
  *     calls, so all entry points are thread-safe.
  *   - s, h and h_kv are GLOBAL sizes (whole sequence, all heads); P is the
  *     number of ranks of the sequence-parallel group.  Shapes below use
- *     sl = s/P, hp = h/P, hkvp = h_kv/P.
+ *     sl = s/P, hp = h/P, and hkvp = h_kv/P, or hkvp = 1 when h_kv < P and
+ *     h_kv | P (KV heads replicated, see ulys_pack_seq2head_kv).
  *   - stream is a hipStream_t passed as void* (NULL = the null stream).  Each
  *     entry only enqueues kernels on it and never synchronizes.
  *   - Arguments are validated on the host first; on any error the entry
@@ -48,7 +51,8 @@ enum {
   ULYS_OK = 0,
   ULYS_ERR_NULL = -1,         /* a required pointer is NULL                      */
   ULYS_ERR_DIM = -2,          /* a size is <= 0 or too large                      */
-  ULYS_ERR_DIVISIBILITY = -3, /* P does not divide s, h or h_kv, or h_kv !| h     */
+  ULYS_ERR_DIVISIBILITY = -3, /* P !| s, P !| h, h_kv !| h, or neither of P and  */
+                              /* h_kv divides the other                          */
   ULYS_ERR_UNSUPPORTED = -4,  /* dtype or head size not supported by the kernel   */
   ULYS_ERR_ALIGNMENT = -5,    /* a pointer is not 16-byte aligned                 */
   ULYS_ERR_ALIAS = -6,        /* an output overlaps an input or another output    */
@@ -74,6 +78,44 @@ int ulys_pack_seq2head(const void* x, void* y, int64_t s, int64_t b, int64_t h,
                        int64_t d_h, int32_t P, int32_t dtype, void* stream);
 
 /*
+ * Seq->head send side for K or V when the model may have fewer KV heads than
+ * ranks.  [CMP] §三: Q, K and V take the same all-to-all, so a plain split of
+ * h_kv < P heads leaves some ranks with no KV head (one head on four ranks:
+ * [1, 0, 0, 0]); [SPCP] (Ulysses section): replicating KV heads lifts the
+ * requirement that P divide h_kv, at a cost in memory and traffic; [DSU]:
+ * num_kv_heads is given when heads do not divide evenly.
+ *
+ *   x : input  [sl, b, h_kv, d_h]                 the rank's K or V shard
+ *   y : output [P, sl, b, max(1, h_kv/P), d_h]    send buffer, block r for rank r
+ * With P | h_kv this is ulys_pack_seq2head.  With h_kv < P and h_kv | P,
+ * block r is KV head floor(r*h_kv/P) -- the head that rank r's query heads
+ * [r*hp, (r+1)*hp) use under the contiguous GQA grouping -- so after the
+ * exchange every rank holds one KV head for the whole sequence, and
+ * ulys_attn_fwd / ulys_attn_bwd take the model's h_kv unchanged.  Bit-exact.
+ * Errors: as ulys_pack_seq2head, with ULYS_ERR_DIVISIBILITY unless P | s and
+ * (P | h_kv or h_kv | P); ULYS_ERR_DIM for more than 2^31 elements with
+ * replication.
+ */
+int ulys_pack_seq2head_kv(const void* x, void* y, int64_t s, int64_t b, int64_t h_kv,
+                          int64_t d_h, int32_t P, int32_t dtype, void* stream);
+
+/*
+ * Backward of ulys_pack_seq2head_kv, receive side: the gradients of K or V
+ * sent back by the P ranks (block r from rank r) into the rank's
+ * [sl, b, h_kv, d_h] shard.  With P | h_kv this is ulys_unpack_head2seq.  With
+ * replication the gradient of a KV head is the sum of its copies' gradients
+ * ([SPCP]: a K/V row used by many queries receives the sum of their
+ * gradients): x[:, :, g, :] = sum over j < P/h_kv of y[g*P/h_kv + j],
+ * accumulated in fp32 in ascending j and rounded once (nearest-even) to the
+ * dtype.
+ *   y : input  [P, sl, b, max(1, h_kv/P), d_h]
+ *   x : output [sl, b, h_kv, d_h]
+ * Errors: as ulys_pack_seq2head_kv.
+ */
+int ulys_unpack_head2seq_kv(const void* y, void* x, int64_t s, int64_t b, int64_t h_kv,
+                            int64_t d_h, int32_t P, int32_t dtype, void* stream);
+
+/*
  * Head->seq all-to-all, receive side (unpack), one rank.
  * [ATLAS] §2: the second all-to-all inverts the first: the P blocks received
  * (block r holds head group r of this rank's sequence segment) are
@@ -94,7 +136,9 @@ int ulys_unpack_head2seq(const void* y, void* x, int64_t s, int64_t b, int64_t h
  * fixed at 1/sqrt(d_h) ([SPCP], Ring section).  causal != 0 lets query t see
  * keys j <= t (global positions; the received blocks are in sequence order).
  * GQA: query head i of the share reads KV head i / (h/h_kv), i.e. contiguous
- * groups ([DSU] num_kv_heads; [SPCP] requires P | h_kv).
+ * groups ([DSU] num_kv_heads; [SPCP] requires P | h_kv).  With h_kv < P
+ * (h_kv | P) the share holds the one replicated KV head that all its query
+ * heads read (ulys_pack_seq2head_kv).
  *
  *   q   : [s, b, hp, d_h]      o : [s, b, hp, d_h]   (same dtype as q)
  *   k,v : [s, b, hkvp, d_h]
@@ -103,8 +147,8 @@ int ulys_unpack_head2seq(const void* y, void* x, int64_t s, int64_t b, int64_t h
  * O is accumulated in fp32 and rounded once (nearest-even) to the dtype.
  * Supported: ULYS_BF16 with d_h in {64, 128} (MFMA kernel); ULYS_F32 with
  * d_h in {64, 128} (fp32 kernel).  s may be any positive multiple of P.
- * Errors: as above, plus h_kv !| h, P !| h_kv, unsupported d_h/dtype, and
- * o or lse overlapping q, k, v or each other.
+ * Errors: as above, plus h_kv !| h, neither of P and h_kv dividing the other,
+ * unsupported d_h/dtype, and o or lse overlapping q, k, v or each other.
  */
 int ulys_attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
                   int64_t s, int64_t b, int64_t h, int64_t h_kv, int64_t d_h, int32_t P,
@@ -195,7 +239,7 @@ const char* ulys_status_string(int status);
 /* ABI version of this header: (major << 16) | minor. */
 int ulys_abi_version(void);
 
-#define ULYS_ABI_VERSION ((1 << 16) | 2)
+#define ULYS_ABI_VERSION ((1 << 16) | 3)
 
 #ifdef __cplusplus
 }

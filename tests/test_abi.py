@@ -36,7 +36,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_version(lib):
-    assert B.ulys_abi_version() == (1 << 16) | 2
+    assert B.ulys_abi_version() == (1 << 16) | 3
 
 
 def test_status_strings(lib):
@@ -80,7 +80,7 @@ Q, K, V, O, L = (0x7F0000000000 + i * (1 << 32) for i in range(5))
     ((Q, K, V, O, L, 0, 1, 8, 8, 128, 4, 1, B.ULYS_BF16), B.ULYS_ERR_DIM),
     ((Q, K, V, O, L, 64, 1, 8, 0, 128, 4, 1, B.ULYS_BF16), B.ULYS_ERR_DIM),
     ((Q, K, V, O, L, 66, 1, 8, 8, 128, 4, 1, B.ULYS_BF16), B.ULYS_ERR_DIVISIBILITY),
-    ((Q, K, V, O, L, 64, 1, 8, 2, 128, 4, 1, B.ULYS_BF16), B.ULYS_ERR_DIVISIBILITY),  # P !| h_kv
+    ((Q, K, V, O, L, 64, 1, 12, 6, 128, 4, 1, B.ULYS_BF16), B.ULYS_ERR_DIVISIBILITY),  # P, h_kv
     ((Q, K, V, O, L, 64, 1, 12, 8, 128, 4, 1, B.ULYS_BF16), B.ULYS_ERR_DIVISIBILITY),
     ((Q, K, V, O, L, 64, 1, 8, 8, 96, 4, 1, B.ULYS_BF16), B.ULYS_ERR_UNSUPPORTED),
     ((Q, K, V, O, L, 64, 1, 8, 8, 128, 4, 1, 3), B.ULYS_ERR_UNSUPPORTED),
@@ -160,7 +160,8 @@ def bwd_args(**kw):
     (dict(ws=None), B.ULYS_ERR_NULL),
     (dict(s=0), B.ULYS_ERR_DIM),
     (dict(s=66), B.ULYS_ERR_DIVISIBILITY),
-    (dict(h_kv=2), B.ULYS_ERR_DIVISIBILITY),
+    (dict(h=12, h_kv=6), B.ULYS_ERR_DIVISIBILITY),
+    (dict(h_kv=3), B.ULYS_ERR_DIVISIBILITY),
     (dict(d=64), B.ULYS_ERR_UNSUPPORTED),
     (dict(dtype=B.ULYS_F32), B.ULYS_ERR_UNSUPPORTED),
     (dict(nbytes=16), B.ULYS_ERR_DIM),
@@ -181,3 +182,35 @@ def test_attn_bwd_workspace_size(lib):
     assert B.ulys_attn_bwd_workspace_size(64, 1, 8, 8, 64, 4, 1, B.ULYS_BF16) == B.ULYS_ERR_UNSUPPORTED
     assert B.ulys_attn_bwd_workspace_size(64, 1, 8, 8, 128, 4, 1, B.ULYS_F32) == B.ULYS_ERR_UNSUPPORTED
     assert B.ulys_attn_bwd_workspace_size(0, 1, 8, 8, 128, 4, 1, B.ULYS_BF16) == B.ULYS_ERR_DIM
+
+
+# ---------------------------------------------------------------------- fewer KV heads than ranks
+@pytest.mark.parametrize("fn", [B.ulys_pack_seq2head_kv, B.ulys_unpack_head2seq_kv])
+@pytest.mark.parametrize("args,expect", [
+    ((None, Y, 16, 1, 2, 64, 4, B.ULYS_BF16), B.ULYS_ERR_NULL),
+    ((X, None, 16, 1, 2, 64, 4, B.ULYS_BF16), B.ULYS_ERR_NULL),
+    ((X, Y, 0, 1, 2, 64, 4, B.ULYS_BF16), B.ULYS_ERR_DIM),
+    ((X, Y, 16, 1, 0, 64, 4, B.ULYS_BF16), B.ULYS_ERR_DIM),
+    ((X, Y, 18, 1, 2, 64, 4, B.ULYS_BF16), B.ULYS_ERR_DIVISIBILITY),
+    ((X, Y, 16, 1, 3, 64, 4, B.ULYS_BF16), B.ULYS_ERR_DIVISIBILITY),   # neither divides
+    ((X, Y, 16, 1, 6, 64, 4, B.ULYS_BF16), B.ULYS_ERR_DIVISIBILITY),
+    ((X, Y, 16, 1, 2, 64, 4, 5), B.ULYS_ERR_UNSUPPORTED),
+    ((X + 8, Y, 16, 1, 2, 64, 4, B.ULYS_F32), B.ULYS_ERR_ALIGNMENT),
+    ((X, Y + 4, 16, 1, 2, 64, 4, B.ULYS_F32), B.ULYS_ERR_ALIGNMENT),
+    # replicated: shard 4*1*2*64*4 = 2 KiB, blocks 4*4*1*1*64*4 = 4 KiB
+    ((X, X + 1024, 16, 1, 2, 64, 4, B.ULYS_F32), B.ULYS_ERR_ALIAS),
+    ((X + 1024, X, 16, 1, 2, 64, 4, B.ULYS_F32), B.ULYS_ERR_ALIAS),
+])
+def test_layout_kv_rejects(lib, fn, args, expect):
+    assert fn(*args) == expect
+
+
+def test_attention_accepts_fewer_kv_heads_than_ranks(lib):
+    """h_kv < P with h_kv | P is a valid share (one replicated KV head); neither
+    dividing the other is not."""
+    assert B.ulys_attn_fwd_workspace_size(64, 1, 8, 2, 128, 4, 1, B.ULYS_BF16) >= 0
+    assert B.ulys_attn_fwd_workspace_size(64, 1, 8, 1, 128, 8, 0, B.ULYS_BF16) >= 0
+    assert B.ulys_attn_fwd_workspace_size(64, 1, 12, 6, 128, 4, 1, B.ULYS_BF16) == \
+        B.ULYS_ERR_DIVISIBILITY
+    # the backward's statistics are per query head: b * hp * s_pad * 2 floats
+    assert B.ulys_attn_bwd_workspace_size(64, 1, 8, 2, 128, 4, 1, B.ULYS_BF16) == 2 * 2 * 64 * 4

@@ -20,7 +20,8 @@ ULYS_ERR_NULL, ULYS_ERR_DIM, ULYS_ERR_DIVISIBILITY = -1, -2, -3
 ULYS_ERR_UNSUPPORTED, ULYS_ERR_ALIGNMENT, ULYS_ERR_ALIAS, ULYS_ERR_HIP = -4, -5, -6, -7
 
 # every symbol include/ulysses.h declares
-EXPORTED = ("ulys_pack_seq2head", "ulys_unpack_head2seq", "ulys_attn_fwd", "ulys_attn_fwd_ws",
+EXPORTED = ("ulys_pack_seq2head", "ulys_unpack_head2seq", "ulys_pack_seq2head_kv",
+            "ulys_unpack_head2seq_kv", "ulys_attn_fwd", "ulys_attn_fwd_ws",
             "ulys_attn_fwd_workspace_size", "ulys_attn_bwd", "ulys_attn_bwd_workspace_size",
             "ulys_status_string", "ulys_abi_version")
 
@@ -48,6 +49,10 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.ulys_pack_seq2head.restype = ctypes.c_int
     lib.ulys_unpack_head2seq.argtypes = lay
     lib.ulys_unpack_head2seq.restype = ctypes.c_int
+    lib.ulys_pack_seq2head_kv.argtypes = lay
+    lib.ulys_pack_seq2head_kv.restype = ctypes.c_int
+    lib.ulys_unpack_head2seq_kv.argtypes = lay
+    lib.ulys_unpack_head2seq_kv.restype = ctypes.c_int
     lib.ulys_attn_fwd.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i32, i32, i32, vp]
     lib.ulys_attn_fwd.restype = ctypes.c_int
     lib.ulys_attn_fwd_ws.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i32, i32, i32,
@@ -74,6 +79,14 @@ def ulys_pack_seq2head(x, y, s, b, h, d_h, P, dtype, stream=None) -> int:
 
 def ulys_unpack_head2seq(y, x, s, b, h, d_h, P, dtype, stream=None) -> int:
     return load().ulys_unpack_head2seq(y, x, s, b, h, d_h, P, dtype, stream)
+
+
+def ulys_pack_seq2head_kv(x, y, s, b, h_kv, d_h, P, dtype, stream=None) -> int:
+    return load().ulys_pack_seq2head_kv(x, y, s, b, h_kv, d_h, P, dtype, stream)
+
+
+def ulys_unpack_head2seq_kv(y, x, s, b, h_kv, d_h, P, dtype, stream=None) -> int:
+    return load().ulys_unpack_head2seq_kv(y, x, s, b, h_kv, d_h, P, dtype, stream)
 
 
 def ulys_attn_fwd(q, k, v, o, lse, s, b, h, h_kv, d_h, P, causal, dtype, stream=None) -> int:
@@ -153,6 +166,34 @@ def unpack_head2seq(y, out=None, stream=None):
         out = _torch().empty((sl, b, hp * P, d), dtype=y.dtype, device=y.device)
     _check(ulys_unpack_head2seq(y.data_ptr(), out.data_ptr(), sl * P, b, hp * P, d, P,
                                 dtype_code(y), _stream(stream)), "ulys_unpack_head2seq")
+    return out
+
+
+def kv_heads_per_rank(h_kv: int, P: int) -> int:
+    """KV heads of one rank's share: h_kv/P, or 1 when h_kv < P (replicated)."""
+    return h_kv // P if h_kv % P == 0 else 1
+
+
+def pack_seq2head_kv(x, P: int, out=None, stream=None):
+    """K or V shard x [s/P, b, h_kv, d] -> send buffer [P, s/P, b, max(1, h_kv/P), d];
+    with h_kv < P block r is KV head floor(r*h_kv/P)."""
+    sl, b, h_kv, d = x.shape
+    if out is None:
+        out = _torch().empty((P, sl, b, kv_heads_per_rank(h_kv, P), d), dtype=x.dtype,
+                             device=x.device)
+    _check(ulys_pack_seq2head_kv(x.data_ptr(), out.data_ptr(), sl * P, b, h_kv, d, P,
+                                 dtype_code(x), _stream(stream)), "ulys_pack_seq2head_kv")
+    return out
+
+
+def unpack_head2seq_kv(y, h_kv: int, out=None, stream=None):
+    """Received K/V gradient blocks y [P, s/P, b, max(1, h_kv/P), d] -> [s/P, b, h_kv, d];
+    with h_kv < P the copies of each KV head are summed."""
+    P, sl, b, _, d = y.shape
+    if out is None:
+        out = _torch().empty((sl, b, h_kv, d), dtype=y.dtype, device=y.device)
+    _check(ulys_unpack_head2seq_kv(y.data_ptr(), out.data_ptr(), sl * P, b, h_kv, d, P,
+                                   dtype_code(y), _stream(stream)), "ulys_unpack_head2seq_kv")
     return out
 
 

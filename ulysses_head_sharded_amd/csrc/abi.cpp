@@ -39,6 +39,11 @@ int64_t checked_product(std::initializer_list<int64_t> xs) {
   return r;
 }
 
+// KV heads in one rank's share: h_kv/P, or 1 when there are fewer KV heads
+// than ranks and each is replicated to the ranks whose query heads use it
+// (then rank r's query heads all map to KV head floor(r*h_kv/P)).
+int64_t kv_per_rank(int64_t h_kv, int64_t P) { return h_kv % P == 0 ? h_kv / P : 1; }
+
 // Shared validation of the two layout entry points.
 int check_layout(const void* in, const void* out, int64_t s, int64_t b, int64_t h, int64_t d_h,
                  int32_t P, int32_t dtype, int64_t* bytes) {
@@ -94,11 +99,12 @@ int check_attn_shape(int64_t s, int64_t b, int64_t h, int64_t h_kv, int64_t d_h,
   if (s <= 0 || b <= 0 || h <= 0 || h_kv <= 0 || d_h <= 0 || P <= 0) return ULYS_ERR_DIM;
   if (s > kMaxDim || b > kMaxDim || h > kMaxDim || h_kv > kMaxDim || d_h > kMaxDim)
     return ULYS_ERR_DIM;
-  if (s % P != 0 || h % P != 0 || h_kv % P != 0 || h % h_kv != 0) return ULYS_ERR_DIVISIBILITY;
+  if (s % P != 0 || h % P != 0 || h % h_kv != 0) return ULYS_ERR_DIVISIBILITY;
+  if (h_kv % P != 0 && P % h_kv != 0) return ULYS_ERR_DIVISIBILITY;
   const int elt = elt_size(dtype);
   if (elt == 0) return ULYS_ERR_UNSUPPORTED;
   if (d_h != 64 && d_h != 128) return ULYS_ERR_UNSUPPORTED;
-  const int64_t hp = h / P, hkvp = h_kv / P;
+  const int64_t hp = h / P, hkvp = kv_per_rank(h_kv, P);
   *nq = checked_product({s, b, hp, d_h, (int64_t)elt});
   *nkv = checked_product({s, b, hkvp, d_h, (int64_t)elt});
   *nl = checked_product({b, hp, s, (int64_t)sizeof(float)});
@@ -126,7 +132,7 @@ ulys::AttnArgs make_args(const void* q, const void* k, const void* v, void* o, f
   a.s = s;
   a.b = b;
   a.hp = h / P;
-  a.hkvp = h_kv / P;
+  a.hkvp = kv_per_rank(h_kv, P);
   a.d = d_h;
   a.causal = causal != 0;
   a.workspace = nullptr;
@@ -200,7 +206,7 @@ int64_t ulys_attn_bwd_workspace_size(int64_t s, int64_t b, int64_t h, int64_t h_
   a.s = s;
   a.b = b;
   a.hp = h / P;
-  a.hkvp = h_kv / P;
+  a.hkvp = kv_per_rank(h_kv, P);
   a.d = d_h;
   a.causal = causal != 0;
   const int64_t need = ulys::attn_bwd_bf16_workspace_size(a);
@@ -248,12 +254,61 @@ int ulys_attn_bwd(const void* q, const void* k, const void* v, const void* o, co
   a.s = s;
   a.b = b;
   a.hp = h / P;
-  a.hkvp = h_kv / P;
+  a.hkvp = kv_per_rank(h_kv, P);
   a.d = d_h;
   a.causal = causal != 0;
   a.workspace = workspace;
   a.workspace_bytes = workspace_bytes;
   const hipError_t e = ulys::launch_attn_bwd_bf16(a, (hipStream_t)stream);
+  return e == hipSuccess ? ULYS_OK : ULYS_ERR_HIP;
+}
+
+// Shared validation of the two KV layout entry points; *rep is set when the
+// heads are replicated (h_kv < P), else the plain layout applies.
+static int check_layout_kv(const void* in, const void* out, int64_t s, int64_t b, int64_t h_kv,
+                           int64_t d_h, int32_t P, int32_t dtype, int* rep, int64_t* shard,
+                           int64_t* blocks) {
+  if (!in || !out) return ULYS_ERR_NULL;
+  if (s <= 0 || b <= 0 || h_kv <= 0 || d_h <= 0 || P <= 0) return ULYS_ERR_DIM;
+  if (s > kMaxDim || b > kMaxDim || h_kv > kMaxDim || d_h > kMaxDim) return ULYS_ERR_DIM;
+  if (s % P != 0 || (h_kv % P != 0 && P % h_kv != 0)) return ULYS_ERR_DIVISIBILITY;
+  const int elt = elt_size(dtype);
+  if (elt == 0) return ULYS_ERR_UNSUPPORTED;
+  *rep = h_kv % P != 0;
+  *shard = checked_product({s / P, b, h_kv, d_h, (int64_t)elt});
+  *blocks = checked_product({(int64_t)P, s / P, b, kv_per_rank(h_kv, P), d_h, (int64_t)elt});
+  if (*shard < 0 || *blocks < 0) return ULYS_ERR_DIM;
+  // the replication kernels index with 32-bit integers
+  if (*rep && *blocks / elt >= (int64_t(1) << 31)) return ULYS_ERR_DIM;
+  if (!aligned16(in) || !aligned16(out)) return ULYS_ERR_ALIGNMENT;
+  return ULYS_OK;
+}
+
+int ulys_pack_seq2head_kv(const void* x, void* y, int64_t s, int64_t b, int64_t h_kv,
+                          int64_t d_h, int32_t P, int32_t dtype, void* stream) {
+  int rep = 0;
+  int64_t shard = 0, blocks = 0;
+  const int rc = check_layout_kv(x, y, s, b, h_kv, d_h, P, dtype, &rep, &shard, &blocks);
+  if (rc != ULYS_OK) return rc;
+  if (overlaps(x, shard, y, blocks)) return ULYS_ERR_ALIAS;
+  if (!rep) return ulys_pack_seq2head(x, y, s, b, h_kv, d_h, P, dtype, stream);
+  const hipError_t e = ulys::launch_replicate_runs(
+      x, y, (uint32_t)((s / P) * b), (uint32_t)h_kv, (uint32_t)P,
+      (uint32_t)(d_h * elt_size(dtype)), (hipStream_t)stream);
+  return e == hipSuccess ? ULYS_OK : ULYS_ERR_HIP;
+}
+
+int ulys_unpack_head2seq_kv(const void* y, void* x, int64_t s, int64_t b, int64_t h_kv,
+                            int64_t d_h, int32_t P, int32_t dtype, void* stream) {
+  int rep = 0;
+  int64_t shard = 0, blocks = 0;
+  const int rc = check_layout_kv(y, x, s, b, h_kv, d_h, P, dtype, &rep, &shard, &blocks);
+  if (rc != ULYS_OK) return rc;
+  if (overlaps(y, blocks, x, shard)) return ULYS_ERR_ALIAS;
+  if (!rep) return ulys_unpack_head2seq(y, x, s, b, h_kv, d_h, P, dtype, stream);
+  const hipError_t e = ulys::launch_sum_runs(y, x, (uint32_t)((s / P) * b), (uint32_t)h_kv,
+                                             (uint32_t)P, (uint32_t)(d_h * elt_size(dtype)),
+                                             elt_size(dtype), (hipStream_t)stream);
   return e == hipSuccess ? ULYS_OK : ULYS_ERR_HIP;
 }
 
@@ -263,7 +318,7 @@ const char* ulys_status_string(int status) {
     case ULYS_ERR_NULL: return "a required pointer is NULL";
     case ULYS_ERR_DIM: return "a size is non-positive or too large";
     case ULYS_ERR_DIVISIBILITY:
-      return "P must divide s, h and h_kv, and h_kv must divide h";
+      return "P must divide s and h, P and h_kv must divide one another, and h_kv must divide h";
     case ULYS_ERR_UNSUPPORTED: return "unsupported dtype or head size";
     case ULYS_ERR_ALIGNMENT: return "a pointer is not 16-byte aligned";
     case ULYS_ERR_ALIAS: return "an output overlaps an input or another output";

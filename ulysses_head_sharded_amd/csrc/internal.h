@@ -36,6 +36,16 @@ __device__ __forceinline__ uint32_t fast_div(uint32_t n, FastDiv f) {
 hipError_t launch_transpose_runs(const void* in, void* out, uint64_t A, uint64_t B,
                                  uint64_t run_bytes, hipStream_t stream);
 
+// KV replication (fewer KV heads C than ranks P, C | P), runs of one head:
+//   replicate: out[r][a] = in[a][r*C/P]            in [A][C], out [P][A]
+//   sum:       out[a][g] = sum_{j<P/C} in[g*P/C+j][a] in [P][A], out [A][C]
+// The sum accumulates in fp32 in ascending j and rounds once to the element
+// type (elt 4: fp32, 2: bf16).  Grids must stay below 2^32 vectors.
+hipError_t launch_replicate_runs(const void* in, void* out, uint32_t A, uint32_t C, uint32_t P,
+                                 uint32_t run_bytes, hipStream_t stream);
+hipError_t launch_sum_runs(const void* in, void* out, uint32_t A, uint32_t C, uint32_t P,
+                           uint32_t run_bytes, int elt, hipStream_t stream);
+
 struct AttnArgs {
   const void* q;
   const void* k;

@@ -22,6 +22,8 @@ namespace {
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 
 constexpr int kThreads = 256;
 constexpr int kUnroll = 1;
@@ -83,7 +85,148 @@ hipError_t launch_vec(const void* in, void* out, uint64_t A, uint64_t B, uint64_
   return hipGetLastError();
 }
 
+// ---- fewer KV heads than ranks ("Ulysses vs Ring Attention" §三: Q, K and V
+// take the same all-to-all, so with h_kv < P some ranks would get no KV head;
+// the SP/CP page's Ulysses section: replicating KV heads lifts P | h_kv).
+// Rank r's block is KV head r*C/P, the head its query heads use; the backward
+// sums the gradient copies of each head.  Both walk the output in order, one
+// vector per thread, like the transpose.
+template <typename Vec>
+__global__ __launch_bounds__(kThreads) void replicate_runs(
+    const Vec* __restrict__ in, Vec* __restrict__ out, uint32_t total, FastDiv vpr,
+    FastDiv rows_a, uint32_t C, FastDiv ranks) {
+  const uint32_t g = blockIdx.x * kThreads + threadIdx.x;
+  if (g >= total) return;
+  const uint32_t run = fast_div(g, vpr);  // r*A + a
+  const uint32_t c = g - run * vpr.div;
+  const uint32_t r = fast_div(run, rows_a);
+  const uint32_t a = run - r * rows_a.div;
+  const uint32_t head = fast_div(r * C, ranks);
+  __builtin_nontemporal_store(__builtin_nontemporal_load(&in[(a * C + head) * vpr.div + c]),
+                              &out[g]);
+}
+
+// One thread per 16-byte output vector (8 bf16 or 4 fp32 elements).
+template <bool BF16>
+__global__ __launch_bounds__(kThreads) void sum_runs16(
+    const u32x4* __restrict__ in, u32x4* __restrict__ out, uint32_t total, FastDiv vpr,
+    FastDiv heads_c, uint32_t A, uint32_t R) {
+  const uint32_t g = blockIdx.x * kThreads + threadIdx.x;
+  if (g >= total) return;
+  const uint32_t run = fast_div(g, vpr);  // a*C + head
+  const uint32_t c = g - run * vpr.div;
+  const uint32_t a = fast_div(run, heads_c);
+  const uint32_t head = run - a * heads_c.div;
+  constexpr int N = BF16 ? 8 : 4;
+  float acc[N];
+#pragma unroll
+  for (int e = 0; e < N; ++e) acc[e] = 0.f;
+  for (uint32_t j = 0; j < R; ++j) {
+    const u32x4 v = __builtin_nontemporal_load(&in[((head * R + j) * A + a) * vpr.div + c]);
+    // whole-vector casts (a bit_cast of a single vector element is miscompiled)
+    if (BF16) {
+      const f32x4 lo = __builtin_bit_cast(f32x4, v << 16);          // even elements
+      const f32x4 hi = __builtin_bit_cast(f32x4, v & 0xFFFF0000u);  // odd elements
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        acc[2 * w] += lo[w];
+        acc[2 * w + 1] += hi[w];
+      }
+    } else {
+      const f32x4 f = __builtin_bit_cast(f32x4, v);
+#pragma unroll
+      for (int w = 0; w < 4; ++w) acc[w] += f[w];
+    }
+  }
+  u32x4 o;
+  if (BF16) {
+    bf16x8 r;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) r[e] = (__bf16)acc[e];  // nearest-even
+    o = __builtin_bit_cast(u32x4, r);
+  } else {
+    const f32x4 f = {acc[0], acc[1], acc[2], acc[3]};
+    o = __builtin_bit_cast(u32x4, f);
+  }
+  __builtin_nontemporal_store(o, &out[g]);
+}
+
+// One thread per element, for runs that are not a whole number of vectors.
+template <typename T>
+__global__ __launch_bounds__(kThreads) void sum_runs1(const T* __restrict__ in,
+                                                      T* __restrict__ out, uint32_t total,
+                                                      FastDiv epr, FastDiv heads_c, uint32_t A,
+                                                      uint32_t R) {
+  const uint32_t g = blockIdx.x * kThreads + threadIdx.x;
+  if (g >= total) return;
+  const uint32_t run = fast_div(g, epr);
+  const uint32_t c = g - run * epr.div;
+  const uint32_t a = fast_div(run, heads_c);
+  const uint32_t head = run - a * heads_c.div;
+  float acc = 0.f;
+  for (uint32_t j = 0; j < R; ++j) acc += (float)in[((head * R + j) * A + a) * epr.div + c];
+  out[g] = (T)acc;
+}
+
+template <typename Vec>
+hipError_t launch_replicate_vec(const void* in, void* out, uint32_t A, uint32_t C, uint32_t P,
+                                uint32_t run_bytes, hipStream_t stream) {
+  const uint32_t vpr = run_bytes / sizeof(Vec);
+  const uint64_t total = (uint64_t)P * A * vpr;
+  if (total == 0) return hipSuccess;
+  if (total >= (1ull << 32) - kThreads) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(replicate_runs<Vec>, dim3((uint32_t)((total + kThreads - 1) / kThreads)),
+                     dim3(kThreads), 0, stream, static_cast<const Vec*>(in),
+                     static_cast<Vec*>(out), (uint32_t)total, make_fastdiv(vpr),
+                     make_fastdiv(A), C, make_fastdiv(P));
+  return hipGetLastError();
+}
+
 }  // namespace
+
+hipError_t launch_replicate_runs(const void* in, void* out, uint32_t A, uint32_t C, uint32_t P,
+                                 uint32_t run_bytes, hipStream_t stream) {
+  if (run_bytes % 16 == 0) return launch_replicate_vec<u32x4>(in, out, A, C, P, run_bytes, stream);
+  if (run_bytes % 8 == 0) return launch_replicate_vec<u32x2>(in, out, A, C, P, run_bytes, stream);
+  if (run_bytes % 4 == 0) return launch_replicate_vec<uint32_t>(in, out, A, C, P, run_bytes, stream);
+  return launch_replicate_vec<uint16_t>(in, out, A, C, P, run_bytes, stream);
+}
+
+hipError_t launch_sum_runs(const void* in, void* out, uint32_t A, uint32_t C, uint32_t P,
+                           uint32_t run_bytes, int elt, hipStream_t stream) {
+  if (C == 0 || P % C != 0 || (elt != 2 && elt != 4)) return hipErrorInvalidValue;
+  const uint32_t R = P / C;
+  if (run_bytes % 16 == 0) {
+    const uint32_t vpr = run_bytes / 16;
+    const uint64_t total = (uint64_t)A * C * vpr;
+    if (total == 0) return hipSuccess;
+    if (total >= (1ull << 32) - kThreads) return hipErrorInvalidValue;
+    const dim3 grid((uint32_t)((total + kThreads - 1) / kThreads));
+    if (elt == 2)
+      hipLaunchKernelGGL(sum_runs16<true>, grid, dim3(kThreads), 0, stream,
+                         static_cast<const u32x4*>(in), static_cast<u32x4*>(out), (uint32_t)total,
+                         make_fastdiv(vpr), make_fastdiv(C), A, R);
+    else
+      hipLaunchKernelGGL(sum_runs16<false>, grid, dim3(kThreads), 0, stream,
+                         static_cast<const u32x4*>(in), static_cast<u32x4*>(out), (uint32_t)total,
+                         make_fastdiv(vpr), make_fastdiv(C), A, R);
+    return hipGetLastError();
+  }
+  const uint32_t epr = run_bytes / elt;
+  const uint64_t total = (uint64_t)A * C * epr;
+  if (total == 0) return hipSuccess;
+  if (total >= (1ull << 32) - kThreads) return hipErrorInvalidValue;
+  const dim3 grid((uint32_t)((total + kThreads - 1) / kThreads));
+  if (elt == 2)
+    hipLaunchKernelGGL(sum_runs1<__bf16>, grid, dim3(kThreads), 0, stream,
+                       static_cast<const __bf16*>(in), static_cast<__bf16*>(out), (uint32_t)total,
+                       make_fastdiv(epr), make_fastdiv(C), A, R);
+  else
+    hipLaunchKernelGGL(sum_runs1<float>, grid, dim3(kThreads), 0, stream,
+                       static_cast<const float*>(in), static_cast<float*>(out), (uint32_t)total,
+                       make_fastdiv(epr), make_fastdiv(C), A, R);
+  return hipGetLastError();
+}
 
 hipError_t launch_transpose_runs(const void* in, void* out, uint64_t A, uint64_t B,
                                  uint64_t run_bytes, hipStream_t stream) {

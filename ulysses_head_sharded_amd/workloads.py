@@ -30,7 +30,8 @@ class Workload:
 
     @property
     def hkvp(self) -> int:
-        return self.h_kv // self.P
+        """KV heads of the share: h_kv/P, or 1 when h_kv < P (each KV head replicated)."""
+        return self.h_kv // self.P if self.h_kv % self.P == 0 else 1
 
     @property
     def elt(self) -> int:
@@ -54,9 +55,14 @@ class Workload:
         heads = self.h_kv if kv else self.h
         return (self.s // self.P) * self.b * heads * self.d * self.elt
 
+    def kv_blocks_bytes(self) -> int:
+        """Bytes of one K or V send buffer [P, s/P, b, hkvp, d] (larger than the
+        shard when heads are replicated)."""
+        return self.s * self.b * self.hkvp * self.d * self.elt
+
     def layout_bytes(self) -> int:
         """Algorithmic HBM bytes of pack(Q), pack(K), pack(V), unpack(O): read + write."""
-        return 2 * (2 * self.shard_bytes() + 2 * self.shard_bytes(kv=True))
+        return 4 * self.shard_bytes() + 2 * (self.shard_bytes(kv=True) + self.kv_blocks_bytes())
 
 
 WORKLOADS = {
@@ -68,6 +74,11 @@ WORKLOADS = {
                          "MHA long share: 32 heads, s=131072, P=8, causal"),
     "gqa-64k": Workload("gqa-64k", 4, 8, 65536, 2, 32, 8, 128, "bf16", True,
                         "GQA share: 32 Q / 8 KV heads, s=65536, b=2, P=8, causal"),
+    # not in the task's list: the GQA share at twice the ranks it has KV heads
+    # for, possible only with KV-head replication (each rank gets one KV head)
+    "gqa-64k-p16": Workload("gqa-64k-p16", 6, 16, 65536, 2, 32, 8, 128, "bf16", True,
+                            "GQA share with fewer KV heads than ranks: 32 Q / 8 KV heads, "
+                            "s=65536, b=2, P=16 (KV heads replicated), causal"),
     "mtok-1m": Workload("mtok-1m", 5, 64, 1048576, 1, 64, 64, 128, "bf16", True,
                         "million-token share: 64 heads, s=1048576, P=64, causal"),
     "dit-256k": Workload("dit-256k", 5, 8, 262144, 1, 32, 32, 128, "bf16", False,
