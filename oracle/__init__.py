@@ -14,6 +14,9 @@ Every function follows a passage of the pages cited in ``ulys_oracle.c``:
     than ranks (each head replicated to the ranks whose queries use it) and its
     backward (the copies' gradients summed) ("Ulysses vs Ring Attention", §三;
     "长上下文训练中的 SP 与 CP", Ulysses section);
+  * ``attn_merge``               -- two partial attention results over disjoint
+    key sets combined through their log-sum-exp ("长上下文训练中的 SP 与 CP",
+    Ring section's online-softmax state; the USP and hierarchical schemes);
   * ``attn`` / ``attn_rows``     -- softmax(Q K^T / sqrt(d_h)) V per head, dense
     or causal (j <= t), GQA by contiguous groups ("DeepSpeed-Ulysses 深度解析",
     core design step 4), in fp64.
@@ -66,6 +69,9 @@ def _bind(lib: ctypes.CDLL) -> ctypes.CDLL:
         fn.restype = ctypes.c_int
     lib.orc_unpack_kv_sum.argtypes = [_vp, _vp, _c_i64, _c_i64, _c_i64, _c_i64, _c_i64,
                                       ctypes.c_int]
+    lib.orc_attn_merge.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _c_i64, _c_i64, _c_i64,
+                                   _c_i64]
+    lib.orc_attn_merge.restype = ctypes.c_int
     lib.orc_unpack_kv_sum.restype = ctypes.c_int
     lib.orc_attn.argtypes = [_vp, _vp, _vp, _vp, _vp, _c_i64, _c_i64, _c_i64, _c_i64,
                              _c_i64, _c_i64, ctypes.c_int, ctypes.c_int, ctypes.c_int]
@@ -212,6 +218,22 @@ def attn_rows(q, k, v, rows, s, b, h, h_kv, d, P, causal, nthreads=None, lib=Non
     _check(rc, "attn_rows")
     return o, lse
 
+
+
+def attn_merge(o_a, lse_a, o_b, lse_b, lib=None):
+    """Merge two partial attention results of one share over disjoint key sets
+    (float64): o_* [s, b, hp, d], lse_* [b, hp, s] (the attention's layouts).
+    Returns (o, lse) float64."""
+    lib = lib or load()
+    o_a, o_b = (np.ascontiguousarray(x, dtype=np.float64) for x in (o_a, o_b))
+    lse_a, lse_b = (np.ascontiguousarray(x, dtype=np.float64) for x in (lse_a, lse_b))
+    s, b, hp, d = o_a.shape
+    assert o_b.shape == o_a.shape and lse_a.shape == (b, hp, s) and lse_b.shape == (b, hp, s)
+    o = np.empty_like(o_a)
+    lse = np.empty_like(lse_a)
+    _check(lib.orc_attn_merge(_ptr(o_a), _ptr(lse_a), _ptr(o_b), _ptr(lse_b), _ptr(o),
+                              _ptr(lse), s, b, hp, d), "attn_merge")
+    return o, lse
 
 
 # ----------------------------------------------------------------------------- backward

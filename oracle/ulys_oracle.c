@@ -552,6 +552,49 @@ static void *bwd_worker(void *arg) {
 }
 
 /*
+ * Merge of two partial attention results over disjoint key sets, one query
+ * row at a time.  [SPCP] (Ring section): each query row keeps the running
+ * max m of its scores, the sum l of exp(score - m) and the weighted sum A of
+ * the values at that scale; a block arriving from another key range is
+ * brought to the common max and added, and O = A / l once every block is in.
+ * A finished partial result over a key range J carries the same state as
+ * lse_J = m + ln l (natural log) and O_J = A / l, so two of them combine as
+ *   lse = ln(exp(lse_a) + exp(lse_b)),
+ *   O   = exp(lse_a - lse) O_a + exp(lse_b - lse) O_b,
+ * written here with the larger lse factored out.  A partial over no key
+ * (lse = -inf) contributes nothing; if both are empty, O = 0 and lse = -inf
+ * (as for a fully masked row).  The hierarchical scheme ([ATLAS] §4: all-to-all
+ * inside a node, a ring across nodes) and USP ([SPCP]: Ulysses groups whose
+ * same-head ranks exchange KV around a ring) merge partial results this way.
+ * Layouts are those the attention produces for one share:
+ *   o_a, o_b, o [s, b, hp, d]; lse_a, lse_b, lse [b, hp, s]; fp64 throughout
+ */
+int orc_attn_merge(const double *o_a, const double *lse_a, const double *o_b,
+                   const double *lse_b, double *o, double *lse, int64_t s, int64_t b,
+                   int64_t hp, int64_t d) {
+  if (s <= 0 || b <= 0 || hp <= 0 || d <= 0) return ORC_EARG;
+  if (!o_a || !lse_a || !o_b || !lse_b || !o || !lse) return ORC_EARG;
+  for (int64_t t = 0; t < s; ++t)
+    for (int64_t be = 0; be < b; ++be)
+      for (int64_t i = 0; i < hp; ++i) {
+        const int64_t li = (be * hp + i) * s + t;  /* this row's lse */
+        const int64_t oi = ((t * b + be) * hp + i) * d; /* and its output row */
+        const double la = lse_a[li], lb = lse_b[li];
+        const double m = la > lb ? la : lb;
+        if (m == -INFINITY) {
+          for (int64_t e = 0; e < d; ++e) o[oi + e] = 0.0;
+          lse[li] = -INFINITY;
+          continue;
+        }
+        const double ea = exp(la - m), eb = exp(lb - m); /* exp(-inf) = 0 */
+        const double l = ea + eb;
+        for (int64_t e = 0; e < d; ++e) o[oi + e] = (ea * o_a[oi + e] + eb * o_b[oi + e]) / l;
+        lse[li] = m + log(l);
+      }
+  return ORC_OK;
+}
+
+/*
  * Backward of the head-sharded attention on one rank's share.
  *   q, dout [s, b, h/P, d]; k, v [s, b, h_kv/P, d] (dtype 0 fp32, 1 bf16 bits)
  *   dq [s, b, h/P, d], dk, dv [s, b, h_kv/P, d] fp64

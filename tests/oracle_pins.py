@@ -628,7 +628,123 @@ def pin_kv_replication_backward_chain(lib):
                     (causal, j)
 
 
+# ---------------------------------------------------------------------------- merge pins
+def _chunk_attn(q, k, v, i, j, c, b, nq, nkv, d, causal, lib):
+    """Attention of query chunk i against key chunk j (c tokens each): with a
+    causal mask, causal inside the diagonal block and dense for an earlier key
+    chunk; without one, dense."""
+    qi, kj, vj = q[i * c:(i + 1) * c], k[j * c:(j + 1) * c], v[j * c:(j + 1) * c]
+    return oracle.attn(qi, kj, vj, c, b, nq, nkv, d, 1, causal and i == j, lib=lib)
+
+
+def _merge_all(parts, lib):
+    o, lse = parts[0]
+    for o2, lse2 in parts[1:]:
+        o, lse = oracle.attn_merge(o, lse, o2, lse2, lib=lib)
+    return o, lse
+
+
+def pin_merge_recovers_full_attention(lib):
+    """Attention over all keys equals the merge of attention over disjoint key
+    chunks: dense over two chunks, and causal over four chunks merged in the
+    order a four-rank ring delivers them to rank 3 (KV_3, KV_2, KV_1, KV_0),
+    to 1e-12."""
+    for dt, (c, b, nq, nkv, d) in (("f32", (6, 2, 4, 2, 8)), ("bf16", (5, 1, 2, 1, 16))):
+        for causal, n in ((False, 2), (True, 4)):
+            s = n * c
+            q = synth.tensor(1800 + s, (s, b, nq, d), dt)
+            k = synth.tensor(1801 + s, (s, b, nkv, d), dt)
+            v = synth.tensor(1802 + s, (s, b, nkv, d), dt)
+            o_full, lse_full = oracle.attn(q, k, v, s, b, nq, nkv, d, 1, causal, lib=lib)
+            for i in range(n):
+                keys = range(i, -1, -1) if causal else range(n)  # later chunks are skipped
+                o, lse = _merge_all([_chunk_attn(q, k, v, i, j, c, b, nq, nkv, d, causal, lib)
+                                     for j in keys], lib)
+                ref_o = o_full[i * c:(i + 1) * c]
+                ref_l = lse_full[:, :, i * c:(i + 1) * c]
+                assert np.max(np.abs(o - ref_o)) < 1e-12, (dt, causal, i)
+                assert np.max(np.abs(lse - ref_l)) < 1e-12, (dt, causal, i)
+
+
+def pin_merge_special_cases(lib):
+    """An empty partial (lse = -inf) leaves the other exactly; two empties give
+    O = 0 and lse = -inf; the merge is symmetric bit for bit; merging a result
+    with itself keeps O and adds ln 2 to lse."""
+    s, b, hp, d = 7, 2, 3, 5
+    rows = s * b * hp
+    o_a = synth.normal_f32(1810, rows * d).astype(np.float64).reshape(s, b, hp, d)
+    o_b = synth.normal_f32(1811, rows * d).astype(np.float64).reshape(s, b, hp, d)
+    l_a = 3.0 * synth.normal_f32(1812, rows).astype(np.float64).reshape(b, hp, s)
+    l_b = 3.0 * synth.normal_f32(1813, rows).astype(np.float64).reshape(b, hp, s)
+    empty = np.full((b, hp, s), -np.inf)
+    o, lse = oracle.attn_merge(o_a, l_a, o_b, empty, lib=lib)
+    assert np.array_equal(o, o_a) and np.array_equal(lse, l_a)
+    o, lse = oracle.attn_merge(o_a, empty, o_b, empty, lib=lib)
+    assert np.array_equal(o, np.zeros_like(o)) and np.all(lse == -np.inf)
+    o1, l1 = oracle.attn_merge(o_a, l_a, o_b, l_b, lib=lib)
+    o2, l2 = oracle.attn_merge(o_b, l_b, o_a, l_a, lib=lib)
+    assert np.array_equal(o1, o2) and np.array_equal(l1, l2)
+    o, lse = oracle.attn_merge(o_a, l_a, o_a, l_a, lib=lib)
+    assert np.max(np.abs(o - o_a)) < 1e-15 * (1 + np.max(np.abs(o_a)))
+    assert np.max(np.abs(lse - (l_a + math.log(2.0)))) < 1e-14 * (1 + np.max(np.abs(l_a)))
+    # weights by hand: lse_a = ln 3, lse_b = ln 1 -> O = (3 O_a + O_b) / 4, lse = ln 4
+    o, lse = oracle.attn_merge(o_a, np.full((b, hp, s), math.log(3.0)), o_b,
+                               np.zeros((b, hp, s)), lib=lib)
+    assert np.max(np.abs(o - (3 * o_a + o_b) / 4)) < 4e-15 * (1 + np.max(np.abs(o_a)))
+    assert np.max(np.abs(lse - math.log(4.0))) < 1e-15
+    # the row map: lse [b, hp, s] pairs with o [s, b, hp, :] -- one row at a time
+    la, lb = l_a.copy(), l_b.copy()
+    la[1, 2, 4], lb[1, 2, 4] = 0.0, -np.inf
+    o, lse = oracle.attn_merge(o_a, la, o_b, lb, lib=lib)
+    assert np.array_equal(o[4, 1, 2], o_a[4, 1, 2]) and lse[1, 2, 4] == 0.0
+
+
+def pin_usp_four_by_two(lib):
+    """The USP arrangement of the SP/CP page at small scale: eight cards, a
+    Ulysses degree of 4 and a ring degree of 2.  Each card starts with s/8
+    tokens; inside each group of four the Ulysses exchange gives every card
+    its group's s/2 tokens for h/4 heads; the two cards holding the same heads
+    in the two groups then exchange K and V, and each merges attention over
+    its own half (causal) with attention over the other group's half (dense
+    when that half comes first, skipped when it comes after).  The head->seq
+    exchange inside each group then returns outputs equal to unsharded causal
+    attention, to 1e-12."""
+    U, Rg = 4, 2
+    s, b, h, h_kv, d = 16, 1, 8, 4, 4
+    half, hp, hkvp = s // Rg, h // U, h_kv // U
+    q = synth.tensor(1820, (s, b, h, d), "bf16")
+    k = synth.tensor(1821, (s, b, h_kv, d), "bf16")
+    v = synth.tensor(1822, (s, b, h_kv, d), "bf16")
+    o_full, _ = oracle.attn(q, k, v, s, b, h, h_kv, d, 1, True, lib=lib)
+    # group g holds tokens [g*half, (g+1)*half); card u of group g holds s/8 of them
+    shares = {}
+    for g in range(Rg):
+        grp = slice(g * half, (g + 1) * half)
+        xq = q[grp].reshape(U, half // U, b, h, d)  # the four cards' shards, in order
+        xk = k[grp].reshape(U, half // U, b, h_kv, d)
+        xv = v[grp].reshape(U, half // U, b, h_kv, d)
+        sq = oracle.seq2head(xq, half, b, h, d, U, lib=lib)      # [U, half, b, hp, d]
+        sk = oracle.seq2head(xk, half, b, h_kv, d, U, lib=lib)
+        sv = oracle.seq2head(xv, half, b, h_kv, d, U, lib=lib)
+        for u in range(U):
+            shares[g, u] = (sq[u], sk[u], sv[u])
+    for g in range(Rg):
+        outs = []
+        for u in range(U):
+            qs, ks, vs = shares[g, u]
+            parts = [oracle.attn(qs, ks, vs, half, b, hp, hkvp, d, 1, True, lib=lib)]
+            for g2 in range(g):  # the other group's K/V, received around the ring
+                _, k2, v2 = shares[g2, u]
+                parts.append(oracle.attn(qs, k2, v2, half, b, hp, hkvp, d, 1, False, lib=lib))
+            outs.append(_merge_all(parts, lib)[0])
+        back = oracle.head2seq(np.stack(outs), half, b, h, d, U, lib=lib)  # [U, half/U, b, h, d]
+        got = back.reshape(half, b, h, d)
+        assert np.max(np.abs(got - o_full[g * half:(g + 1) * half])) < 1e-12, g
+
+
+MERGE_PINS = [pin_merge_recovers_full_attention, pin_merge_special_cases, pin_usp_four_by_two]
+
 KV_PINS = [pin_kv_replication_example, pin_pack_kv_brute_force, pin_unpack_kv_sum,
            pin_kv_replication_head_independence, pin_kv_replication_backward_chain]
 
-ALL_PINS = LAYOUT_PINS + ATTN_PINS + BWD_PINS + KV_PINS
+ALL_PINS = LAYOUT_PINS + ATTN_PINS + BWD_PINS + KV_PINS + MERGE_PINS

@@ -40,9 +40,9 @@ MUTANTS = [
     ("bwd_drop_D", "const double ds = p[j] * (dp[j] - D);\n          const double *krow = J->k",
      "const double ds = p[j] * dp[j];\n          const double *krow = J->k"),
     ("bwd_dv_uses_ds", "dvrow[e] += p[j] * drow[e];\n          }\n        }\n      }\n    }\n  }\n"
-     "  free(p); free(dp);\n  J->status = ORC_OK;\n  return NULL;\n}\n\n/*\n * Backward of",
+     "  free(p); free(dp);\n  J->status = ORC_OK;\n  return NULL;\n}\n\n/*\n * Merge of",
      "dvrow[e] += ds * drow[e];\n          }\n        }\n      }\n    }\n  }\n"
-     "  free(p); free(dp);\n  J->status = ORC_OK;\n  return NULL;\n}\n\n/*\n * Backward of"),
+     "  free(p); free(dp);\n  J->status = ORC_OK;\n  return NULL;\n}\n\n/*\n * Merge of"),
     ("bwd_gqa_first_head_only",
      "for (int64_t i = g * G; i < (g + 1) * G; ++i) {\n      for (int64_t t = 0; t < s; ++t) {",
      "for (int64_t i = g * G; i < g * G + 1; ++i) {\n      for (int64_t t = 0; t < s; ++t) {"),
@@ -59,6 +59,14 @@ MUTANTS = [
      "for (int64_t r = g * R; r < (g + 1) * R - 1; ++r) /* the ranks"),
     ("round_bf16_truncates", "q = ldexp(nearbyint(ldexp(m, 8)), e - 8);",
      "q = ldexp(floor(ldexp(m, 8)), e - 8);"),
+    # merge of partial attention results
+    ("merge_drops_max_in_lse", "lse[li] = m + log(l);", "lse[li] = log(l);"),
+    ("merge_swaps_weights", "o[oi + e] = (ea * o_a[oi + e] + eb * o_b[oi + e]) / l;",
+     "o[oi + e] = (eb * o_a[oi + e] + ea * o_b[oi + e]) / l;"),
+    ("merge_skips_normalisation", "o[oi + e] = (ea * o_a[oi + e] + eb * o_b[oi + e]) / l;",
+     "o[oi + e] = (ea * o_a[oi + e] + eb * o_b[oi + e]);"),
+    ("merge_lse_row_transposed", "const int64_t li = (be * hp + i) * s + t;",
+     "const int64_t li = (t * b + be) * hp + i;"),
 ]
 
 
