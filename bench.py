@@ -41,6 +41,9 @@ def parse_args():
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="wall-time budget of the oracle's cpu_baseline sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--merge-steps", type=int, default=50,
+                    help="timed ulys_attn_merge calls on the share (one ring step's merge of "
+                         "two partial results), reported under 'merge'; 0 skips them")
     ap.add_argument("--bwd-steps", type=int, default=100,
                     help="timed backward steps (pack dO, attention backward, unpack dQ, dK, "
                          "dV) reported under 'backward'; 0 skips them")
@@ -124,6 +127,40 @@ def cpu_baseline(w, q, k, v, budget_s: float):
         "sample": f"{rows_done} uniformly drawn query rows of the {w.name} share "
                   f"(fp64 oracle, {t_used:.1f} s wall, algorithmic flops of the sample)",
     }
+
+
+def bench_merge(args, w, binding, torch, np, o, code, stream):
+    """ulys_attn_merge of two partial results of the share (O [s, b, hp, d] in the
+    workload's dtype, lse [b, hp, s] fp32), accumulating in place as a ring step
+    does.  HBM-bound: 3 O tensors and 3 lse tensors move per call."""
+    s, b, hp, d = w.s, w.b, w.hp, w.d
+    o_a = o.clone()
+    o_b = o.flip(0).contiguous()
+    lse_a = torch.zeros((b, hp, s), dtype=torch.float32, device=o.device)
+    lse_b = torch.full((b, hp, s), -0.5, dtype=torch.float32, device=o.device)
+    sh = stream.cuda_stream
+
+    def call():
+        rc = binding.ulys_attn_merge(o_a.data_ptr(), lse_a.data_ptr(), o_b.data_ptr(),
+                                     lse_b.data_ptr(), o_a.data_ptr(), lse_a.data_ptr(), s, b,
+                                     hp, d, code, sh)
+        if rc != 0:
+            raise RuntimeError(f"merge: {binding.ulys_status_string(rc)}")
+
+    for _ in range(5):
+        call()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for _ in range(args.merge_steps):
+        call()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / args.merge_steps
+    nbytes = 3 * (s * b * hp * d * w.elt + s * b * hp * 4)
+    return {"calls": args.merge_steps, "us": round(us, 2), "bytes": nbytes,
+            "gbps": round(nbytes / (us * 1e-6) / 1e9, 1),
+            "frac_hbm_peak": round(nbytes / (us * 1e-6) / 1e9 / PEAK_HBM_GBPS, 4)}
 
 
 def bench_backward(args, w, binding, torch, np, q, k, v, code, stream):
@@ -351,6 +388,8 @@ def main():
                      "unit": "TFLOP/s", "frac": round(attn_tflops / peak, 4),
                      "traffic": counter_traffic(kernel_src, w.name)},
     }
+    if args.merge_steps > 0:
+        rec["merge"] = bench_merge(args, w, binding, torch, np, o, code, stream)
     if args.bwd_steps > 0 and w.dtype == "bf16":
         rec["backward"] = bench_backward(args, w, binding, torch, np, yq, yk, yv, code, stream)
     if not args.no_cpu_baseline:

@@ -14,7 +14,7 @@
  *           the same all-to-all; Ulysses' degree is capped by num_kv_heads).
  *   [SPCP]  "长上下文训练中的 SP 与 CP：从 Megatron 到分布式 Attention",
  *           the Ulysses section (P must divide the KV head count under GQA)
- *           and the Ring section (online softmax, scale 1/sqrt(d_h)).
+ *           and the Ring section (online softmax, scale 1/sqrt(d_h)), USP.
  *
  * General conventions
  *   - Every tensor pointer is a DEVICE pointer to a contiguous row-major
@@ -233,13 +233,40 @@ int ulys_attn_bwd(const void* q, const void* k, const void* v, const void* o, co
 int64_t ulys_attn_bwd_workspace_size(int64_t s, int64_t b, int64_t h, int64_t h_kv, int64_t d_h,
                                      int32_t P, int32_t causal, int32_t dtype);
 
+/*
+ * Merge of two partial attention results of one share over disjoint key sets.
+ * [SPCP] (Ring section): each query row's online-softmax state -- running
+ * max, scaled sum, scaled weighted sum of values -- is brought to a common max
+ * and added when a block from another key range arrives; a finished partial
+ * result carries that state as its log-sum-exp and normalised output, so
+ *   lse = ln(e^lse_a + e^lse_b),  O = e^(lse_a - lse) O_a + e^(lse_b - lse) O_b
+ * per query row.  This combines a rank's Ulysses share with key blocks that
+ * arrive around a ring: [ATLAS] §4 (all-to-all inside a node, ring across
+ * nodes) and [SPCP] (USP: Ulysses groups whose same-head ranks exchange K/V).
+ * Partials come from ulys_attn_fwd with lse (dense for a key block wholly
+ * before the queries, causal for the block that holds them).
+ *
+ *   o_a, o_b, o       : [s, b, hp, d_h]  (dtype; hp = query heads of the share)
+ *   lse_a, lse_b, lse : [b, hp, s] fp32, natural log; -inf marks an empty
+ *                       partial, which contributes nothing (both empty: O = 0,
+ *                       lse = -inf)
+ * o may be o_a and lse may be lse_a (in-place accumulation); every other
+ * overlap is ULYS_ERR_ALIAS.  Arithmetic in fp32, O rounded once
+ * (nearest-even).  Supported: F32 and BF16 with d_h in {64, 128}.
+ * Errors: NULL pointers, sizes <= 0, unsupported dtype or d_h, misaligned
+ * buffers, overlaps other than the in-place pair.
+ */
+int ulys_attn_merge(const void* o_a, const float* lse_a, const void* o_b, const float* lse_b,
+                    void* o, float* lse, int64_t s, int64_t b, int64_t hp, int64_t d_h,
+                    int32_t dtype, void* stream);
+
 /* Static, human-readable text for a status code (never NULL). */
 const char* ulys_status_string(int status);
 
 /* ABI version of this header: (major << 16) | minor. */
 int ulys_abi_version(void);
 
-#define ULYS_ABI_VERSION ((1 << 16) | 3)
+#define ULYS_ABI_VERSION ((1 << 16) | 4)
 
 #ifdef __cplusplus
 }

@@ -36,7 +36,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_version(lib):
-    assert B.ulys_abi_version() == (1 << 16) | 3
+    assert B.ulys_abi_version() == (1 << 16) | 4
 
 
 def test_status_strings(lib):
@@ -214,3 +214,34 @@ def test_attention_accepts_fewer_kv_heads_than_ranks(lib):
         B.ULYS_ERR_DIVISIBILITY
     # the backward's statistics are per query head: b * hp * s_pad * 2 floats
     assert B.ulys_attn_bwd_workspace_size(64, 1, 8, 2, 128, 4, 1, B.ULYS_BF16) == 2 * 2 * 64 * 4
+
+
+# ---------------------------------------------------------------------- merge of partial results
+OA, LA, OB, LB, OO, LO = (0x7F0000000000 + i * (1 << 32) for i in range(11, 17))
+MERGE_OK = (OA, LA, OB, LB, OO, LO, 64, 1, 2, 128, B.ULYS_BF16)
+
+
+def merge_args(**kw):
+    names = ("o_a", "lse_a", "o_b", "lse_b", "o", "lse", "s", "b", "hp", "d", "dtype")
+    a = dict(zip(names, MERGE_OK))
+    a.update(kw)
+    return tuple(a[n] for n in names)
+
+
+@pytest.mark.parametrize("kw,expect", [
+    (dict(o_a=None), B.ULYS_ERR_NULL),
+    (dict(lse=None), B.ULYS_ERR_NULL),
+    (dict(s=0), B.ULYS_ERR_DIM),
+    (dict(hp=-1), B.ULYS_ERR_DIM),
+    (dict(d=96), B.ULYS_ERR_UNSUPPORTED),
+    (dict(dtype=7), B.ULYS_ERR_UNSUPPORTED),
+    (dict(o_b=OB + 8), B.ULYS_ERR_ALIGNMENT),
+    (dict(lse=LO + 4), B.ULYS_ERR_ALIGNMENT),
+    (dict(o=OB), B.ULYS_ERR_ALIAS),              # output on the second input
+    (dict(o=OA + 256), B.ULYS_ERR_ALIAS),        # partial overlap with the first
+    (dict(lse=LB), B.ULYS_ERR_ALIAS),
+    (dict(lse=OO + 512), B.ULYS_ERR_ALIAS),      # lse inside o
+    (dict(o=LA), B.ULYS_ERR_ALIAS),              # o over lse_a
+])
+def test_attn_merge_rejects(lib, kw, expect):
+    assert B.ulys_attn_merge(*merge_args(**kw)) == expect

@@ -23,6 +23,7 @@ ULYS_ERR_UNSUPPORTED, ULYS_ERR_ALIGNMENT, ULYS_ERR_ALIAS, ULYS_ERR_HIP = -4, -5,
 EXPORTED = ("ulys_pack_seq2head", "ulys_unpack_head2seq", "ulys_pack_seq2head_kv",
             "ulys_unpack_head2seq_kv", "ulys_attn_fwd", "ulys_attn_fwd_ws",
             "ulys_attn_fwd_workspace_size", "ulys_attn_bwd", "ulys_attn_bwd_workspace_size",
+            "ulys_attn_merge",
             "ulys_status_string", "ulys_abi_version")
 
 _lib = None
@@ -64,6 +65,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.ulys_attn_bwd.restype = ctypes.c_int
     lib.ulys_attn_bwd_workspace_size.argtypes = [i64, i64, i64, i64, i64, i32, i32, i32]
     lib.ulys_attn_bwd_workspace_size.restype = ctypes.c_int64
+    lib.ulys_attn_merge.argtypes = [vp] * 6 + [i64] * 4 + [i32, vp]
+    lib.ulys_attn_merge.restype = ctypes.c_int
     lib.ulys_status_string.argtypes = [ctypes.c_int]
     lib.ulys_status_string.restype = ctypes.c_char_p
     lib.ulys_abi_version.argtypes = []
@@ -111,6 +114,10 @@ def ulys_attn_bwd(q, k, v, o, dout, lse, dq, dk, dv, s, b, h, h_kv, d_h, P, caus
 
 def ulys_attn_bwd_workspace_size(s, b, h, h_kv, d_h, P, causal, dtype) -> int:
     return load().ulys_attn_bwd_workspace_size(s, b, h, h_kv, d_h, P, causal, dtype)
+
+
+def ulys_attn_merge(o_a, lse_a, o_b, lse_b, o, lse, s, b, hp, d_h, dtype, stream=None) -> int:
+    return load().ulys_attn_merge(o_a, lse_a, o_b, lse_b, o, lse, s, b, hp, d_h, dtype, stream)
 
 
 def ulys_status_string(status: int) -> str:
@@ -244,3 +251,19 @@ def attn_bwd(q, k, v, o, dout, lse, P: int = 1, causal: bool = False, stream=Non
                        d, P, int(bool(causal)), code, ws.data_ptr(), ws_bytes, _stream(stream))
     _check(rc, "ulys_attn_bwd")
     return dq, dk, dv
+
+
+def attn_merge(o_a, lse_a, o_b, lse_b, out=None, lse_out=None, stream=None):
+    """Merge two partial attention results of one share: o_* [s, b, hp, d],
+    lse_* [b, hp, s] float32.  out/lse_out may be o_a/lse_a (in place); by
+    default new tensors.  Returns (o, lse)."""
+    torch = _torch()
+    s, b, hp, d = o_a.shape
+    if out is None:
+        out = torch.empty_like(o_a)
+    if lse_out is None:
+        lse_out = torch.empty_like(lse_a)
+    _check(ulys_attn_merge(o_a.data_ptr(), lse_a.data_ptr(), o_b.data_ptr(), lse_b.data_ptr(),
+                           out.data_ptr(), lse_out.data_ptr(), s, b, hp, d, dtype_code(o_a),
+                           _stream(stream)), "ulys_attn_merge")
+    return out, lse_out

@@ -17,7 +17,8 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD_DIR = os.path.join(ROOT, "_build")
 LIB_PATH = os.path.join(PKG, "libulysses.so")
-SOURCES = ["abi.cpp", "layout.hip", "attn_bf16.hip", "attn_bwd_bf16.hip", "attn_f32.hip"]
+SOURCES = ["abi.cpp", "layout.hip", "attn_bf16.hip", "attn_bwd_bf16.hip", "attn_f32.hip",
+           "merge.hip"]
 ARCH = "gfx950"
 
 

@@ -312,6 +312,41 @@ int ulys_unpack_head2seq_kv(const void* y, void* x, int64_t s, int64_t b, int64_
   return e == hipSuccess ? ULYS_OK : ULYS_ERR_HIP;
 }
 
+int ulys_attn_merge(const void* o_a, const float* lse_a, const void* o_b, const float* lse_b,
+                    void* o, float* lse, int64_t s, int64_t b, int64_t hp, int64_t d_h,
+                    int32_t dtype, void* stream) {
+  if (!o_a || !lse_a || !o_b || !lse_b || !o || !lse) return ULYS_ERR_NULL;
+  if (s <= 0 || b <= 0 || hp <= 0 || d_h <= 0) return ULYS_ERR_DIM;
+  if (s > kMaxDim || b > kMaxDim || hp > kMaxDim || d_h > kMaxDim) return ULYS_ERR_DIM;
+  const int elt = elt_size(dtype);
+  if (elt == 0 || (d_h != 64 && d_h != 128)) return ULYS_ERR_UNSUPPORTED;
+  const int64_t no = checked_product({s, b, hp, d_h, (int64_t)elt});
+  const int64_t nl = checked_product({s, b, hp, (int64_t)sizeof(float)});
+  if (no < 0 || nl < 0) return ULYS_ERR_DIM;
+  // one 16-byte vector per thread, 32-bit indices
+  if (no / 16 >= (int64_t(1) << 31)) return ULYS_ERR_DIM;
+  const void* ptrs[] = {o_a, lse_a, o_b, lse_b, o, lse};
+  for (const void* p : ptrs)
+    if (!aligned16(p)) return ULYS_ERR_ALIGNMENT;
+  // o may be exactly o_a and lse exactly lse_a (in-place accumulation);
+  // any other overlap between an output and an input or the other output is
+  // rejected
+  const void* ins[] = {o_a, lse_a, o_b, lse_b};
+  const int64_t in_bytes[] = {no, nl, no, nl};
+  const void* outs[] = {o, lse};
+  const int64_t out_bytes[] = {no, nl};
+  const void* same[] = {o_a, lse_a};
+  for (int i = 0; i < 2; ++i)
+    for (int j = 0; j < 4; ++j)
+      if (!(j == i && outs[i] == same[i]) && overlaps(outs[i], out_bytes[i], ins[j], in_bytes[j]))
+        return ULYS_ERR_ALIAS;
+  if (overlaps(o, no, lse, nl)) return ULYS_ERR_ALIAS;
+  const hipError_t e = ulys::launch_attn_merge(o_a, lse_a, o_b, lse_b, o, lse, (uint32_t)s,
+                                               (uint32_t)b, (uint32_t)hp,
+                                               (uint32_t)(d_h * elt), elt, (hipStream_t)stream);
+  return e == hipSuccess ? ULYS_OK : ULYS_ERR_HIP;
+}
+
 const char* ulys_status_string(int status) {
   switch (status) {
     case ULYS_OK: return "ok";

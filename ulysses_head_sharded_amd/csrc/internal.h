@@ -46,6 +46,13 @@ hipError_t launch_replicate_runs(const void* in, void* out, uint32_t A, uint32_t
 hipError_t launch_sum_runs(const void* in, void* out, uint32_t A, uint32_t C, uint32_t P,
                            uint32_t run_bytes, int elt, hipStream_t stream);
 
+// Merge of two partial attention results of one share (O [s, b, hp, d],
+// lse [b, hp, s] fp32); o/lse may be o_a/lse_a.  row_bytes = d * elt, a
+// multiple of 16 up to 1 KiB.
+hipError_t launch_attn_merge(const void* o_a, const float* lse_a, const void* o_b,
+                             const float* lse_b, void* o, float* lse, uint32_t s, uint32_t b,
+                             uint32_t hp, uint32_t row_bytes, int elt, hipStream_t stream);
+
 struct AttnArgs {
   const void* q;
   const void* k;
