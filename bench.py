@@ -310,14 +310,10 @@ def main():
         if record:
             e = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
             e[0].record(stream)
-        call(binding.ulys_pack_seq2head(xq.data_ptr(), yq.data_ptr(), w.s, w.b, w.h, w.d, w.P,
-                                        code, sh), "pack q")
-        # K and V: the plain pack, or with fewer KV heads than ranks the
-        # replicating one (the same kernel when P | h_kv)
-        call(binding.ulys_pack_seq2head_kv(xk.data_ptr(), yk.data_ptr(), w.s, w.b, w.h_kv, w.d,
-                                           w.P, code, sh), "pack k")
-        call(binding.ulys_pack_seq2head_kv(xv.data_ptr(), yv.data_ptr(), w.s, w.b, w.h_kv, w.d,
-                                           w.P, code, sh), "pack v")
+        # Q, K and V packed by one call (K and V replicated when h_kv < P)
+        call(binding.ulys_pack_seq2head_qkv(xq.data_ptr(), xk.data_ptr(), xv.data_ptr(),
+                                            yq.data_ptr(), yk.data_ptr(), yv.data_ptr(), w.s,
+                                            w.b, w.h, w.h_kv, w.d, w.P, code, sh), "pack qkv")
         if record:
             e[1].record(stream)
         # the send buffers stand in for the receive buffers: [P, s/P, b, hp, d] == [s, b, hp, d]

@@ -100,6 +100,20 @@ int ulys_pack_seq2head_kv(const void* x, void* y, int64_t s, int64_t b, int64_t 
                           int64_t d_h, int32_t P, int32_t dtype, void* stream);
 
 /*
+ * The send sides of Q, K and V in one call: the same results as
+ * ulys_pack_seq2head(xq -> yq, h) followed by ulys_pack_seq2head_kv(xk -> yk,
+ * h_kv) and ulys_pack_seq2head_kv(xv -> yv, h_kv) ([DSU] step 3: Q, K and V
+ * each go through the seq->head exchange; [CMP] §三: all three take the same
+ * path), done by a single kernel launch when every run is a whole number of
+ * 16-byte vectors (else the three packs in turn).  Shapes, validation and
+ * errors as the single packs; no output may overlap any input or another
+ * output.
+ */
+int ulys_pack_seq2head_qkv(const void* xq, const void* xk, const void* xv, void* yq, void* yk,
+                           void* yv, int64_t s, int64_t b, int64_t h, int64_t h_kv, int64_t d_h,
+                           int32_t P, int32_t dtype, void* stream);
+
+/*
  * Backward of ulys_pack_seq2head_kv, receive side: the gradients of K or V
  * sent back by the P ranks (block r from rank r) into the rank's
  * [sl, b, h_kv, d_h] shard.  With P | h_kv this is ulys_unpack_head2seq.  With
@@ -266,7 +280,7 @@ const char* ulys_status_string(int status);
 /* ABI version of this header: (major << 16) | minor. */
 int ulys_abi_version(void);
 
-#define ULYS_ABI_VERSION ((1 << 16) | 4)
+#define ULYS_ABI_VERSION ((1 << 16) | 5)
 
 #ifdef __cplusplus
 }

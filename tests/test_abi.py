@@ -36,7 +36,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_version(lib):
-    assert B.ulys_abi_version() == (1 << 16) | 4
+    assert B.ulys_abi_version() == (1 << 16) | 5
 
 
 def test_status_strings(lib):
@@ -245,3 +245,32 @@ def merge_args(**kw):
 ])
 def test_attn_merge_rejects(lib, kw, expect):
     assert B.ulys_attn_merge(*merge_args(**kw)) == expect
+
+
+# ---------------------------------------------------------------------- fused Q/K/V pack
+XQ, XK, XV, YQ, YK, YV = (0x7F0000000000 + i * (1 << 32) for i in range(20, 26))
+QKV_OK = (XQ, XK, XV, YQ, YK, YV, 64, 1, 8, 2, 128, 4, B.ULYS_BF16)
+
+
+def qkv_args(**kw):
+    names = ("xq", "xk", "xv", "yq", "yk", "yv", "s", "b", "h", "h_kv", "d", "P", "dtype")
+    a = dict(zip(names, QKV_OK))
+    a.update(kw)
+    return tuple(a[n] for n in names)
+
+
+@pytest.mark.parametrize("kw,expect", [
+    (dict(xv=None), B.ULYS_ERR_NULL),
+    (dict(yk=None), B.ULYS_ERR_NULL),
+    (dict(s=0), B.ULYS_ERR_DIM),
+    (dict(s=66), B.ULYS_ERR_DIVISIBILITY),
+    (dict(h=6), B.ULYS_ERR_DIVISIBILITY),
+    (dict(h_kv=3), B.ULYS_ERR_DIVISIBILITY),
+    (dict(dtype=9), B.ULYS_ERR_UNSUPPORTED),
+    (dict(yv=YV + 8), B.ULYS_ERR_ALIGNMENT),
+    (dict(yq=XK), B.ULYS_ERR_ALIAS),            # an output over another tensor's input
+    (dict(yv=YK + 1024), B.ULYS_ERR_ALIAS),     # two outputs overlapping
+    (dict(yk=XK + 16), B.ULYS_ERR_ALIAS),
+])
+def test_pack_qkv_rejects(lib, kw, expect):
+    assert B.ulys_pack_seq2head_qkv(*qkv_args(**kw)) == expect

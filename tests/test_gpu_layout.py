@@ -119,3 +119,37 @@ def test_deterministic_and_stream_ordered():
         y2 = binding.pack_seq2head(x, P)
     st.synchronize()
     assert torch.equal(y1.view(torch.int16), y2.view(torch.int16))
+
+
+def run_pack_qkv(xq, xk, xv, s, b, h, h_kv, d, P, elt):
+    """ulys_pack_seq2head_qkv into guarded buffers."""
+    dev()
+    hk = h_kv // P if h_kv % P == 0 else 1
+    ins = [to_dev(x) for x in (xq, xk, xv)]
+    outs = [Guarded((P, s // P, b, hh, d), TORCH_DT[elt]) for hh in (h // P, hk, hk)]
+    rc = binding.ulys_pack_seq2head_qkv(*(t.data_ptr() for t in ins),
+                                        *(g.tensor.data_ptr() for g in outs), s, b, h, h_kv, d, P,
+                                        CODE[elt], torch.cuda.current_stream().cuda_stream)
+    assert rc == 0, binding.ulys_status_string(rc)
+    torch.cuda.synchronize()
+    assert all(g.guards_intact() for g in outs)
+    return [from_dev(g.tensor) for g in outs]
+
+
+QKV_CASES = [(w.s, w.b, w.h, w.h_kv, w.d, w.P, w.elt, n) for n, w in WORKLOADS.items()] + [
+    (40, 2, 8, 2, 64, 8, 2, "replicated"), (24, 1, 12, 3, 128, 6, 4, "replicated-f32"),
+    (12, 2, 8, 8, 3, 4, 2, "vectorless"), (16, 1, 4, 1, 8, 4, 4, "mqa")]
+
+
+@pytest.mark.parametrize("s,b,h,h_kv,d,P,elt,name", QKV_CASES, ids=[c[-1] for c in QKV_CASES])
+def test_pack_qkv_bit_exact(s, b, h, h_kv, d, P, elt, name):
+    """One call packs Q (plain) and K, V (plain, or replicated when h_kv < P)
+    exactly as the oracle's three separate packs."""
+    print(f"case pack_qkv {name} s={s} b={b} h={h} h_kv={h_kv} d={d} P={P} elt={elt}", flush=True)
+    xq = bits(3000 + s, (s // P, b, h, d), elt)
+    xk = bits(3001 + s, (s // P, b, h_kv, d), elt)
+    xv = bits(3002 + s, (s // P, b, h_kv, d), elt)
+    yq, yk, yv = run_pack_qkv(xq, xk, xv, s, b, h, h_kv, d, P, elt)
+    assert same_bits(yq, oracle.pack(xq, s, b, h, d, P))
+    assert same_bits(yk, oracle.pack_kv(xk, s, b, h_kv, d, P))
+    assert same_bits(yv, oracle.pack_kv(xv, s, b, h_kv, d, P))

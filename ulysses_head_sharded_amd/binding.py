@@ -21,7 +21,7 @@ ULYS_ERR_UNSUPPORTED, ULYS_ERR_ALIGNMENT, ULYS_ERR_ALIAS, ULYS_ERR_HIP = -4, -5,
 
 # every symbol include/ulysses.h declares
 EXPORTED = ("ulys_pack_seq2head", "ulys_unpack_head2seq", "ulys_pack_seq2head_kv",
-            "ulys_unpack_head2seq_kv", "ulys_attn_fwd", "ulys_attn_fwd_ws",
+            "ulys_unpack_head2seq_kv", "ulys_pack_seq2head_qkv", "ulys_attn_fwd", "ulys_attn_fwd_ws",
             "ulys_attn_fwd_workspace_size", "ulys_attn_bwd", "ulys_attn_bwd_workspace_size",
             "ulys_attn_merge",
             "ulys_status_string", "ulys_abi_version")
@@ -54,6 +54,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.ulys_pack_seq2head_kv.restype = ctypes.c_int
     lib.ulys_unpack_head2seq_kv.argtypes = lay
     lib.ulys_unpack_head2seq_kv.restype = ctypes.c_int
+    lib.ulys_pack_seq2head_qkv.argtypes = [vp] * 6 + [i64] * 5 + [i32, i32, vp]
+    lib.ulys_pack_seq2head_qkv.restype = ctypes.c_int
     lib.ulys_attn_fwd.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i32, i32, i32, vp]
     lib.ulys_attn_fwd.restype = ctypes.c_int
     lib.ulys_attn_fwd_ws.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i32, i32, i32,
@@ -90,6 +92,12 @@ def ulys_pack_seq2head_kv(x, y, s, b, h_kv, d_h, P, dtype, stream=None) -> int:
 
 def ulys_unpack_head2seq_kv(y, x, s, b, h_kv, d_h, P, dtype, stream=None) -> int:
     return load().ulys_unpack_head2seq_kv(y, x, s, b, h_kv, d_h, P, dtype, stream)
+
+
+def ulys_pack_seq2head_qkv(xq, xk, xv, yq, yk, yv, s, b, h, h_kv, d_h, P, dtype,
+                           stream=None) -> int:
+    return load().ulys_pack_seq2head_qkv(xq, xk, xv, yq, yk, yv, s, b, h, h_kv, d_h, P, dtype,
+                                         stream)
 
 
 def ulys_attn_fwd(q, k, v, o, lse, s, b, h, h_kv, d_h, P, causal, dtype, stream=None) -> int:

@@ -312,6 +312,49 @@ int ulys_unpack_head2seq_kv(const void* y, void* x, int64_t s, int64_t b, int64_
   return e == hipSuccess ? ULYS_OK : ULYS_ERR_HIP;
 }
 
+int ulys_pack_seq2head_qkv(const void* xq, const void* xk, const void* xv, void* yq, void* yk,
+                           void* yv, int64_t s, int64_t b, int64_t h, int64_t h_kv, int64_t d_h,
+                           int32_t P, int32_t dtype, void* stream) {
+  int64_t nq = 0;
+  int rc = check_layout(xq, yq, s, b, h, d_h, P, dtype, &nq);
+  if (rc != ULYS_OK) return rc;
+  int rep = 0;
+  int64_t shard_kv = 0, blocks_kv = 0;
+  rc = check_layout_kv(xk, yk, s, b, h_kv, d_h, P, dtype, &rep, &shard_kv, &blocks_kv);
+  if (rc != ULYS_OK) return rc;
+  rc = check_layout_kv(xv, yv, s, b, h_kv, d_h, P, dtype, &rep, &shard_kv, &blocks_kv);
+  if (rc != ULYS_OK) return rc;
+  const void* ins[] = {xq, xk, xv};
+  const int64_t in_bytes[] = {nq, shard_kv, shard_kv};
+  void* outs[] = {yq, yk, yv};
+  const int64_t out_bytes[] = {nq, blocks_kv, blocks_kv};
+  for (int i = 0; i < 3; ++i) {
+    for (int j = 0; j < 3; ++j)
+      if (overlaps(outs[i], out_bytes[i], ins[j], in_bytes[j])) return ULYS_ERR_ALIAS;
+    for (int j = 0; j < i; ++j)
+      if (overlaps(outs[i], out_bytes[i], outs[j], out_bytes[j])) return ULYS_ERR_ALIAS;
+  }
+  const int elt = elt_size(dtype);
+  const int64_t hkv_runs = rep ? h_kv : P;  // input runs per token-batch row
+  const int64_t run_q = (h / P) * d_h * elt, run_kv = kv_per_rank(h_kv, P) * d_h * elt;
+  const int64_t vecs = (nq + 2 * blocks_kv) / 16;
+  if (run_q % 16 != 0 || run_kv % 16 != 0 || vecs >= (int64_t(1) << 31)) {
+    // not a whole number of 16-byte vectors per run, or too large for one
+    // launch's 32-bit indices: the three packs one after another
+    rc = ulys_pack_seq2head(xq, yq, s, b, h, d_h, P, dtype, stream);
+    if (rc == ULYS_OK) rc = ulys_pack_seq2head_kv(xk, yk, s, b, h_kv, d_h, P, dtype, stream);
+    if (rc == ULYS_OK) rc = ulys_pack_seq2head_kv(xv, yv, s, b, h_kv, d_h, P, dtype, stream);
+    return rc;
+  }
+  const void* in3[3] = {xq, xk, xv};
+  void* out3[3] = {yq, yk, yv};
+  const uint32_t cols[3] = {(uint32_t)P, (uint32_t)hkv_runs, (uint32_t)hkv_runs};
+  const uint32_t runs[3] = {(uint32_t)run_q, (uint32_t)run_kv, (uint32_t)run_kv};
+  const hipError_t e = ulys::launch_pack_qkv(in3, out3, (uint32_t)((s / P) * b), (uint32_t)P, cols,
+                                             runs, (hipStream_t)stream);
+  return e == hipSuccess ? ULYS_OK : ULYS_ERR_HIP;
+}
+
 int ulys_attn_merge(const void* o_a, const float* lse_a, const void* o_b, const float* lse_b,
                     void* o, float* lse, int64_t s, int64_t b, int64_t hp, int64_t d_h,
                     int32_t dtype, void* stream) {

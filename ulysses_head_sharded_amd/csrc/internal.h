@@ -43,6 +43,13 @@ hipError_t launch_transpose_runs(const void* in, void* out, uint64_t A, uint64_t
 // type (elt 4: fp32, 2: bf16).  Grids must stay below 2^32 vectors.
 hipError_t launch_replicate_runs(const void* in, void* out, uint32_t A, uint32_t C, uint32_t P,
                                  uint32_t run_bytes, hipStream_t stream);
+// Q, K and V packs in one launch: segment k maps input [A][cols[k]] runs to
+// output [P][A] runs with run r*A + a <- a*cols[k] + r*cols[k]/P (cols = P:
+// the plain pack; cols = h_kv < P: the replicating one).  Every run_bytes
+// a multiple of 16 and fewer than 2^32 vectors in all.
+hipError_t launch_pack_qkv(const void* const in[3], void* const out[3], uint32_t A, uint32_t P,
+                           const uint32_t cols[3], const uint32_t run_bytes[3],
+                           hipStream_t stream);
 hipError_t launch_sum_runs(const void* in, void* out, uint32_t A, uint32_t C, uint32_t P,
                            uint32_t run_bytes, int elt, hipStream_t stream);
 

@@ -182,7 +182,66 @@ hipError_t launch_replicate_vec(const void* in, void* out, uint32_t A, uint32_t 
   return hipGetLastError();
 }
 
+// ---- Q, K and V packed by one launch.  Each segment is a pack whose output
+// run r*A + a (rank r, token-batch row a) comes from input run
+// a*C + r*C/P: C = P is the plain pack (run = the rank's head group), C = h_kv
+// < P the replicating one (run = one KV head).  Thread g finds its segment
+// from the segments' starting vectors, then walks that output in order.
+struct PackSeg {
+  const u32x4* in;
+  u32x4* out;
+  uint32_t start;    // first global vector index of this segment
+  FastDiv vpr;       // vectors per run
+  FastDiv rows_a;    // A = s/P * b
+  uint32_t cols_c;   // input runs per token-batch row
+};
+struct PackSegs {
+  PackSeg seg[3];
+  FastDiv ranks;     // P
+  uint32_t total;
+};
+
+__global__ __launch_bounds__(kThreads) void pack_segments(PackSegs ps) {
+  const uint32_t g = blockIdx.x * kThreads + threadIdx.x;
+  if (g >= ps.total) return;
+  const int k = (g >= ps.seg[2].start) ? 2 : (g >= ps.seg[1].start) ? 1 : 0;
+  const PackSeg sg = ps.seg[k];
+  const uint32_t gl = g - sg.start;
+  const uint32_t run = fast_div(gl, sg.vpr);  // r*A + a
+  const uint32_t c = gl - run * sg.vpr.div;
+  const uint32_t r = fast_div(run, sg.rows_a);
+  const uint32_t a = run - r * sg.rows_a.div;
+  const uint32_t col = fast_div(r * sg.cols_c, ps.ranks);
+  __builtin_nontemporal_store(
+      __builtin_nontemporal_load(&sg.in[(a * sg.cols_c + col) * sg.vpr.div + c]), &sg.out[gl]);
+}
+
 }  // namespace
+
+hipError_t launch_pack_qkv(const void* const in[3], void* const out[3], uint32_t A, uint32_t P,
+                           const uint32_t cols[3], const uint32_t run_bytes[3],
+                           hipStream_t stream) {
+  PackSegs ps;
+  uint64_t start = 0;
+  for (int k = 0; k < 3; ++k) {
+    if (run_bytes[k] % 16 != 0 || cols[k] == 0) return hipErrorInvalidValue;
+    const uint32_t vpr = run_bytes[k] / 16;
+    ps.seg[k].in = static_cast<const u32x4*>(in[k]);
+    ps.seg[k].out = static_cast<u32x4*>(out[k]);
+    ps.seg[k].start = (uint32_t)start;
+    ps.seg[k].vpr = make_fastdiv(vpr);
+    ps.seg[k].rows_a = make_fastdiv(A);
+    ps.seg[k].cols_c = cols[k];
+    start += (uint64_t)P * A * vpr;
+    if (start >= (1ull << 32) - kThreads) return hipErrorInvalidValue;
+  }
+  ps.ranks = make_fastdiv(P);
+  ps.total = (uint32_t)start;
+  if (ps.total == 0) return hipSuccess;
+  hipLaunchKernelGGL(pack_segments, dim3((ps.total + kThreads - 1) / kThreads), dim3(kThreads), 0,
+                     stream, ps);
+  return hipGetLastError();
+}
 
 hipError_t launch_replicate_runs(const void* in, void* out, uint32_t A, uint32_t C, uint32_t P,
                                  uint32_t run_bytes, hipStream_t stream) {
