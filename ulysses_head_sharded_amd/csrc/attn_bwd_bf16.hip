@@ -110,7 +110,23 @@ struct BwdParams {
   // dkv kernel: items = n_kblk * b * hkvp
   int n_kblk;
   int kv_split;  // 1: every dkv item runs as two halves of its query steps
+  int kv_units;  // dkv work units: items << kv_split
+  int kv_xcd;    // 1: dkv units dispatched in the XCD-aware order (see xcd_unit)
 };
+
+// XCD-aware order of the dkv units.  The dispatcher sends workgroup b to XCD
+// b % 8 (each XCD has its own L2) and each XCD starts its workgroups in order
+// of b.  Causal dkv units are ranked longest first and neighbouring units read
+// nearly the same query tiles at nearly the same time, but the round-robin
+// spreads neighbours over all eight L2s.  Here the ranked list is cut into 16
+// equal chunks and XCD x runs chunk x, then chunk 15 - x: the units it runs
+// together are neighbours (their Q / dout tiles are shared in its L2), and a
+// long chunk paired with the mirrored short one gives every XCD the same
+// amount of work under the linear causal profile.  Needs N % 16 == 0.
+__device__ __forceinline__ int xcd_unit(int b, int n) {
+  const int c = n >> 4, x = b & 7, j = b >> 3;
+  return j < c ? x * c + j : (15 - x) * c + (j - c);
+}
 
 // Transposed 32 x 32 accumulator (rows = features, column = lane % 32) scaled
 // and rounded once to bf16, stored at row `col` of a [tokens, heads, d] tensor
@@ -409,7 +425,8 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkv_kernel(BwdParams p) {
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
   const int l32 = lane & 31, hh = lane >> 5;
-  int rank = blockIdx.x, half = 0;
+  const int unit = p.kv_xcd ? xcd_unit(blockIdx.x, p.kv_units) : (int)blockIdx.x;
+  int rank = unit, half = 0;
   if (p.kv_split) {
     half = rank & 1;
     rank >>= 1;
@@ -574,7 +591,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkv_kernel(BwdParams p) {
     __syncthreads();
   }
   if (p.kv_split) {
-    float* base = p.part + (int64_t)blockIdx.x * kDkvPart;
+    float* base = p.part + (int64_t)unit * kDkvPart;
     store_part<D / 32>(base, dka, wave, lane);
     store_part<D / 32>(base + kDkvPart / 2, dva, wave, lane);
     return;
@@ -697,6 +714,8 @@ hipError_t launch_attn_bwd_bf16(const AttnBwdArgs& a, hipStream_t stream) {
   p.n_kblk = pl.n_kblk;
   p.q_split = pl.q_split;
   p.kv_split = pl.kv_split;
+  p.kv_units = (int)(pl.k_items << pl.kv_split);
+  p.kv_xcd = (a.causal && p.kv_units % 16 == 0) ? 1 : 0;
   const unsigned q_grid = (unsigned)(pl.q_items << pl.q_split);
   const unsigned k_grid = (unsigned)(pl.k_items << pl.kv_split);
   if (a.causal) {
