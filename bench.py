@@ -44,6 +44,9 @@ def parse_args():
     ap.add_argument("--merge-steps", type=int, default=50,
                     help="timed ulys_attn_merge calls on the share (one ring step's merge of "
                          "two partial results), reported under 'merge'; 0 skips them")
+    ap.add_argument("--push-steps", type=int, default=20,
+                    help="timed pushes of the Q shard into P share buffers on this GPU "
+                         "(ulys_seq2head_push), reported under 'exchange_push'; 0 skips them")
     ap.add_argument("--bwd-steps", type=int, default=100,
                     help="timed backward steps (pack dO, attention backward, unpack dQ, dK, "
                          "dV) reported under 'backward'; 0 skips them")
@@ -159,6 +162,36 @@ def bench_merge(args, w, binding, torch, np, o, code, stream):
     us = e0.elapsed_time(e1) * 1e3 / args.merge_steps
     nbytes = 3 * (s * b * hp * d * w.elt + s * b * hp * 4)
     return {"calls": args.merge_steps, "us": round(us, 2), "bytes": nbytes,
+            "gbps": round(nbytes / (us * 1e-6) / 1e9, 1),
+            "frac_hbm_peak": round(nbytes / (us * 1e-6) / 1e9 / PEAK_HBM_GBPS, 4)}
+
+
+def bench_push(args, w, binding, torch, np, xq, tdt, code, stream):
+    """One rank's seq->head push of its Q shard into the P ranks' share buffers,
+    all on this GPU (on a node the destinations are peers' buffers and the
+    writes cross xGMI).  Moves the shard's bytes once: read + write."""
+    shares = [torch.empty((w.s, w.b, w.hp, w.d), dtype=tdt, device=xq.device)
+              for _ in range(w.P)]
+    ptrs = [t.data_ptr() for t in shares]
+    sh = stream.cuda_stream
+
+    def call():
+        rc = binding.ulys_seq2head_push(xq.data_ptr(), ptrs, 0, w.s, w.b, w.h, w.d, w.P, code, sh)
+        if rc != 0:
+            raise RuntimeError(f"push: {binding.ulys_status_string(rc)}")
+
+    for _ in range(3):
+        call()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for _ in range(args.push_steps):
+        call()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / args.push_steps
+    nbytes = 2 * w.shard_bytes()
+    return {"calls": args.push_steps, "us": round(us, 2), "bytes": nbytes,
             "gbps": round(nbytes / (us * 1e-6) / 1e9, 1),
             "frac_hbm_peak": round(nbytes / (us * 1e-6) / 1e9 / PEAK_HBM_GBPS, 4)}
 
@@ -386,6 +419,8 @@ def main():
     }
     if args.merge_steps > 0:
         rec["merge"] = bench_merge(args, w, binding, torch, np, o, code, stream)
+    if args.push_steps > 0:
+        rec["exchange_push"] = bench_push(args, w, binding, torch, np, xq, tdt, code, stream)
     if args.bwd_steps > 0 and w.dtype == "bf16":
         rec["backward"] = bench_backward(args, w, binding, torch, np, yq, yk, yv, code, stream)
     if not args.no_cpu_baseline:

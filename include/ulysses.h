@@ -247,6 +247,45 @@ int ulys_attn_bwd(const void* q, const void* k, const void* v, const void* o, co
 int64_t ulys_attn_bwd_workspace_size(int64_t s, int64_t b, int64_t h, int64_t h_kv, int64_t d_h,
                                      int32_t P, int32_t causal, int32_t dtype);
 
+/* Largest P the push entry points take (the destination table size). */
+#define ULYS_MAX_RANKS 64
+
+/*
+ * Seq->head exchange as pushes, the send side of one rank writing straight
+ * into every rank's receive buffer.  [ATLAS] §2: rank `rank` splits its
+ * [sl, b, h, d_h] shard along heads and sends group r to rank r, which
+ * concatenates what it receives along the sequence in source order; here the
+ * sender places its block at rows [rank*sl, (rank+1)*sl) of rank r's share,
+ * so neither the send buffer of ulys_pack_seq2head nor a receive-side step
+ * exists.  On a node the P destinations are the ranks' share buffers mapped
+ * into this process (hipIpcOpenMemHandle); on one GPU any P buffers.
+ *
+ *   x       : [sl, b, h, d_h]        this rank's shard (device)
+ *   y_ranks : HOST array of P device pointers; y_ranks[r] is rank r's share
+ *             [s, b, hp, d_h]; this call writes its rows [rank*sl, (rank+1)*sl)
+ *   rank    : this rank, 0 <= rank < P <= ULYS_MAX_RANKS
+ * After every rank's call (and the streams' ordering across ranks), share r
+ * equals what ulys_pack_seq2head + an all-to-all + the source-ordered receive
+ * gives.  Bit-exact.  Errors: as ulys_pack_seq2head, plus ULYS_ERR_DIM for P
+ * or rank out of range, ULYS_ERR_NULL / ULYS_ERR_ALIGNMENT for any
+ * destination, ULYS_ERR_ALIAS when a written range overlaps x or another
+ * destination's.
+ */
+int ulys_seq2head_push(const void* x, void* const* y_ranks, int32_t rank, int64_t s, int64_t b,
+                       int64_t h, int64_t d_h, int32_t P, int32_t dtype, void* stream);
+
+/*
+ * Head->seq exchange as pushes, from rank `rank` holding head group `rank`
+ * ([ATLAS] §2: the reverse exchange splits along the sequence and the
+ * receiver concatenates along heads): rank j's shard x_ranks[j]
+ * [sl, b, h, d_h] receives rows [j*sl, (j+1)*sl) of this rank's output o
+ * [s, b, hp, d_h] at heads [rank*hp, (rank+1)*hp).  Replaces the send of O's
+ * blocks and ulys_unpack_head2seq.  Bit-exact.  Errors: as
+ * ulys_seq2head_push.
+ */
+int ulys_head2seq_push(const void* o, void* const* x_ranks, int32_t rank, int64_t s, int64_t b,
+                       int64_t h, int64_t d_h, int32_t P, int32_t dtype, void* stream);
+
 /*
  * Merge of two partial attention results of one share over disjoint key sets.
  * [SPCP] (Ring section): each query row's online-softmax state -- running
@@ -280,7 +319,7 @@ const char* ulys_status_string(int status);
 /* ABI version of this header: (major << 16) | minor. */
 int ulys_abi_version(void);
 
-#define ULYS_ABI_VERSION ((1 << 16) | 5)
+#define ULYS_ABI_VERSION ((1 << 16) | 6)
 
 #ifdef __cplusplus
 }

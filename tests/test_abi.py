@@ -36,7 +36,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_version(lib):
-    assert B.ulys_abi_version() == (1 << 16) | 5
+    assert B.ulys_abi_version() == (1 << 16) | 6
 
 
 def test_status_strings(lib):
@@ -274,3 +274,30 @@ def qkv_args(**kw):
 ])
 def test_pack_qkv_rejects(lib, kw, expect):
     assert B.ulys_pack_seq2head_qkv(*qkv_args(**kw)) == expect
+
+
+# ---------------------------------------------------------------------- exchange as pushes
+PX = 0x7F0000000000 + 30 * (1 << 32)
+PY = [0x7F0000000000 + (31 + r) * (1 << 32) for r in range(4)]
+
+
+@pytest.mark.parametrize("fn", [B.ulys_seq2head_push, B.ulys_head2seq_push])
+@pytest.mark.parametrize("kw,expect", [
+    (dict(x=None), B.ULYS_ERR_NULL),
+    (dict(dst=[PY[0], None, PY[2], PY[3]]), B.ULYS_ERR_NULL),
+    (dict(rank=4), B.ULYS_ERR_DIM),
+    (dict(rank=-1), B.ULYS_ERR_DIM),
+    (dict(P=65, dst=PY * 17, s=65 * 16, h=65), B.ULYS_ERR_DIM),
+    (dict(s=18), B.ULYS_ERR_DIVISIBILITY),
+    (dict(h=6), B.ULYS_ERR_DIVISIBILITY),
+    (dict(dtype=3), B.ULYS_ERR_UNSUPPORTED),
+    (dict(x=PX + 8), B.ULYS_ERR_ALIGNMENT),
+    (dict(dst=[PY[0], PY[1] + 4, PY[2], PY[3]]), B.ULYS_ERR_ALIGNMENT),
+    (dict(dst=[PY[0], PY[0], PY[2], PY[3]]), B.ULYS_ERR_ALIAS),      # two ranks, one buffer
+    (dict(dst=[PX, PY[1], PY[2], PY[3]]), B.ULYS_ERR_ALIAS),         # over the local tensor
+])
+def test_push_rejects(lib, fn, kw, expect):
+    a = dict(x=PX, dst=PY, rank=1, s=16, b=1, h=8, d=64, P=4, dtype=B.ULYS_BF16)
+    a.update(kw)
+    assert fn(a["x"], a["dst"], a["rank"], a["s"], a["b"], a["h"], a["d"], a["P"],
+              a["dtype"]) == expect

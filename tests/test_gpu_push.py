@@ -1,0 +1,112 @@
+"""GPU parity of the exchange as pushes (ulys_seq2head_push, ulys_head2seq_push):
+every emulated rank pushes its blocks straight into the P destination
+buffers (here P regions of one GPU's memory, as peer-mapped receive buffers
+would be on a node), and the P destinations together equal the oracle's
+whole exchange (orc_seq2head, orc_head2seq) bit for bit; and a whole layer
+built on pushes -- Q, K, V in, attention on each share, O back -- equals the
+oracle's unsharded attention within the attention tolerance."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from gpu_util import Guarded, as_f64, dev, from_dev, to_dev
+from ulysses_head_sharded_amd import binding, synth
+
+pytestmark = pytest.mark.gpu
+
+TORCH_DT = {2: torch.bfloat16, 4: torch.float32}
+NP_DT = {2: np.uint16, 4: np.float32}
+CODE = {2: binding.ULYS_BF16, 4: binding.ULYS_F32}
+
+
+def stream():
+    return torch.cuda.current_stream().cuda_stream
+
+
+def bits(seed, shape, elt):
+    raw = synth.random_bits(seed, int(np.prod(shape)) * elt)
+    return raw.view(NP_DT[elt]).reshape(shape)
+
+
+# (s, b, h, d, P, elt): runs of 16-byte vectors, of 4-byte words (d = 2,
+# fp32 hp = 1) and of 2-byte elements (d = 3 bf16), up to P = 16
+CASES = [(16, 1, 8, 64, 4, 2), (24, 2, 8, 128, 8, 2), (12, 2, 6, 3, 3, 2), (40, 1, 16, 2, 8, 4),
+         (64, 2, 32, 128, 16, 2), (8, 1, 4, 64, 2, 4)]
+
+
+@pytest.mark.parametrize("s,b,h,d,P,elt", CASES)
+def test_seq2head_push_equals_exchange(s, b, h, d, P, elt):
+    print(f"case seq2head_push s={s} b={b} h={h} d={d} P={P} elt={elt}", flush=True)
+    sl, hp = s // P, h // P
+    x_all = bits(4000 + s + d, (P, sl, b, h, d), elt)
+    dev()
+    shares = [Guarded((s, b, hp, d), TORCH_DT[elt]) for _ in range(P)]
+    ptrs = [g.tensor.data_ptr() for g in shares]
+    for j in range(P):
+        xj = to_dev(np.ascontiguousarray(x_all[j]))
+        rc = binding.ulys_seq2head_push(xj.data_ptr(), ptrs, j, s, b, h, d, P, CODE[elt], stream())
+        assert rc == 0, binding.ulys_status_string(rc)
+    torch.cuda.synchronize()
+    assert all(g.guards_intact() for g in shares)
+    ref = oracle.seq2head(x_all, s, b, h, d, P)
+    for r in range(P):
+        got = from_dev(shares[r].tensor)
+        assert np.array_equal(got.view(np.uint8), ref[r].view(np.uint8)), r
+
+
+@pytest.mark.parametrize("s,b,h,d,P,elt", CASES)
+def test_head2seq_push_equals_exchange(s, b, h, d, P, elt):
+    print(f"case head2seq_push s={s} b={b} h={h} d={d} P={P} elt={elt}", flush=True)
+    sl, hp = s // P, h // P
+    y_all = bits(4100 + s + d, (P, s, b, hp, d), elt)
+    dev()
+    shards = [Guarded((sl, b, h, d), TORCH_DT[elt]) for _ in range(P)]
+    ptrs = [g.tensor.data_ptr() for g in shards]
+    for r in range(P):
+        yr = to_dev(np.ascontiguousarray(y_all[r]))
+        rc = binding.ulys_head2seq_push(yr.data_ptr(), ptrs, r, s, b, h, d, P, CODE[elt], stream())
+        assert rc == 0, binding.ulys_status_string(rc)
+    torch.cuda.synchronize()
+    assert all(g.guards_intact() for g in shards)
+    ref = oracle.head2seq(y_all, s, b, h, d, P)
+    for j in range(P):
+        got = from_dev(shards[j].tensor)
+        assert np.array_equal(got.view(np.uint8), ref[j].view(np.uint8)), j
+
+
+@pytest.mark.parametrize("causal", [True, False])
+def test_layer_on_pushes(causal):
+    """Q, K, V pushed from every rank's shard into every rank's share, attention
+    on each share, O pushed back into every rank's shard: equals the oracle's
+    unsharded attention over all heads."""
+    s, b, h, h_kv, d, P = 256, 2, 8, 4, 128, 4
+    sl = s // P
+    qg, kg, vg = (synth.tensor(4200 + n, (s, b, hh, d), "bf16")
+                  for n, hh in enumerate((h, h_kv, h_kv)))
+    dev()
+
+    def push_in(t, hh):
+        shares = [torch.empty((s, b, hh // P, d), dtype=torch.bfloat16, device="cuda")
+                  for _ in range(P)]
+        ptrs = [x.data_ptr() for x in shares]
+        for j in range(P):
+            xj = to_dev(np.ascontiguousarray(t[j * sl:(j + 1) * sl]))
+            assert binding.ulys_seq2head_push(xj.data_ptr(), ptrs, j, s, b, hh, d, P,
+                                              binding.ULYS_BF16, stream()) == 0
+            torch.cuda.synchronize()  # xj is freed after this iteration
+        return shares
+
+    qs, ks, vs = push_in(qg, h), push_in(kg, h_kv), push_in(vg, h_kv)
+    outs = [torch.empty((sl, b, h, d), dtype=torch.bfloat16, device="cuda") for _ in range(P)]
+    optrs = [x.data_ptr() for x in outs]
+    for r in range(P):
+        o, _ = binding.attn_fwd(qs[r], ks[r], vs[r], P=P, causal=causal)
+        assert binding.ulys_head2seq_push(o.data_ptr(), optrs, r, s, b, h, d, P,
+                                          binding.ULYS_BF16, stream()) == 0
+        torch.cuda.synchronize()
+    got = np.concatenate([from_dev(x) for x in outs], axis=0)
+    ref, _ = oracle.attn(qg, kg, vg, s, b, h, h_kv, d, 1, causal)
+    err = np.max(np.abs(as_f64(got) - ref))
+    print(f"  o: max err {err:.3e}", flush=True)
+    assert err <= 2e-2

@@ -23,7 +23,7 @@ ULYS_ERR_UNSUPPORTED, ULYS_ERR_ALIGNMENT, ULYS_ERR_ALIAS, ULYS_ERR_HIP = -4, -5,
 EXPORTED = ("ulys_pack_seq2head", "ulys_unpack_head2seq", "ulys_pack_seq2head_kv",
             "ulys_unpack_head2seq_kv", "ulys_pack_seq2head_qkv", "ulys_attn_fwd", "ulys_attn_fwd_ws",
             "ulys_attn_fwd_workspace_size", "ulys_attn_bwd", "ulys_attn_bwd_workspace_size",
-            "ulys_attn_merge",
+            "ulys_attn_merge", "ulys_seq2head_push", "ulys_head2seq_push",
             "ulys_status_string", "ulys_abi_version")
 
 _lib = None
@@ -67,6 +67,11 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.ulys_attn_bwd.restype = ctypes.c_int
     lib.ulys_attn_bwd_workspace_size.argtypes = [i64, i64, i64, i64, i64, i32, i32, i32]
     lib.ulys_attn_bwd_workspace_size.restype = ctypes.c_int64
+    push = [vp, ctypes.POINTER(vp), i32, i64, i64, i64, i64, i32, i32, vp]
+    lib.ulys_seq2head_push.argtypes = push
+    lib.ulys_seq2head_push.restype = ctypes.c_int
+    lib.ulys_head2seq_push.argtypes = push
+    lib.ulys_head2seq_push.restype = ctypes.c_int
     lib.ulys_attn_merge.argtypes = [vp] * 6 + [i64] * 4 + [i32, vp]
     lib.ulys_attn_merge.restype = ctypes.c_int
     lib.ulys_status_string.argtypes = [ctypes.c_int]
@@ -126,6 +131,21 @@ def ulys_attn_bwd_workspace_size(s, b, h, h_kv, d_h, P, causal, dtype) -> int:
 
 def ulys_attn_merge(o_a, lse_a, o_b, lse_b, o, lse, s, b, hp, d_h, dtype, stream=None) -> int:
     return load().ulys_attn_merge(o_a, lse_a, o_b, lse_b, o, lse, s, b, hp, d_h, dtype, stream)
+
+
+def _ptr_table(ptrs):
+    vp = ctypes.c_void_p
+    return (vp * len(ptrs))(*[vp(p) if p else None for p in ptrs])
+
+
+def ulys_seq2head_push(x, y_ranks, rank, s, b, h, d_h, P, dtype, stream=None) -> int:
+    """y_ranks: sequence of P device addresses (ints)."""
+    return load().ulys_seq2head_push(x, _ptr_table(y_ranks), rank, s, b, h, d_h, P, dtype, stream)
+
+
+def ulys_head2seq_push(o, x_ranks, rank, s, b, h, d_h, P, dtype, stream=None) -> int:
+    """x_ranks: sequence of P device addresses (ints)."""
+    return load().ulys_head2seq_push(o, _ptr_table(x_ranks), rank, s, b, h, d_h, P, dtype, stream)
 
 
 def ulys_status_string(status: int) -> str:

@@ -355,6 +355,73 @@ int ulys_pack_seq2head_qkv(const void* xq, const void* xk, const void* xv, void*
   return e == hipSuccess ? ULYS_OK : ULYS_ERR_HIP;
 }
 
+// Shared validation of the two push entry points: `local` is the rank's own
+// tensor (x [sl,b,h,d] or o [s,b,hp,d]), `remote` the P destination pointers;
+// the bytes each destination receives are checked against `local` and
+// against every other destination's.
+static int check_push(const void* local, void* const* remote, int32_t rank, int64_t s, int64_t b,
+                      int64_t h, int64_t d_h, int32_t P, int32_t dtype, bool seq2head) {
+  if (!local || !remote) return ULYS_ERR_NULL;
+  if (s <= 0 || b <= 0 || h <= 0 || d_h <= 0 || P <= 0) return ULYS_ERR_DIM;
+  if (s > kMaxDim || b > kMaxDim || h > kMaxDim || d_h > kMaxDim) return ULYS_ERR_DIM;
+  if (P > ULYS_MAX_RANKS || rank < 0 || rank >= P) return ULYS_ERR_DIM;
+  if (s % P != 0 || h % P != 0) return ULYS_ERR_DIVISIBILITY;
+  const int elt = elt_size(dtype);
+  if (elt == 0) return ULYS_ERR_UNSUPPORTED;
+  const int64_t n = checked_product({s / P, b, h, d_h, (int64_t)elt});  // shard = share bytes
+  if (n < 0 || n / elt >= (int64_t(1) << 31)) return ULYS_ERR_DIM;
+  if (!aligned16(local)) return ULYS_ERR_ALIGNMENT;
+  for (int32_t r = 0; r < P; ++r) {
+    if (!remote[r]) return ULYS_ERR_NULL;
+    if (!aligned16(remote[r])) return ULYS_ERR_ALIGNMENT;
+  }
+  // the byte range this call writes in destination r
+  const int64_t blk = n / P;
+  auto written = [&](int32_t r, const char** lo, int64_t* len) {
+    if (seq2head) {  // rows [rank*sl, (rank+1)*sl) of share r
+      *lo = static_cast<const char*>(remote[r]) + (int64_t)rank * blk;
+      *len = blk;
+    } else {  // head group `rank` of every row of shard r: the span from its first to last run
+      const int64_t run = (h / P) * d_h * elt;
+      *lo = static_cast<const char*>(remote[r]) + (int64_t)rank * run;
+      *len = n - (int64_t)(P - 1) * run;
+    }
+  };
+  for (int32_t r = 0; r < P; ++r) {
+    const char* lo = nullptr;
+    int64_t len = 0;
+    written(r, &lo, &len);
+    if (overlaps(lo, len, local, n)) return ULYS_ERR_ALIAS;
+    for (int32_t q = 0; q < r; ++q) {
+      const char* lo2 = nullptr;
+      int64_t len2 = 0;
+      written(q, &lo2, &len2);
+      if (overlaps(lo, len, lo2, len2)) return ULYS_ERR_ALIAS;
+    }
+  }
+  return ULYS_OK;
+}
+
+int ulys_seq2head_push(const void* x, void* const* y_ranks, int32_t rank, int64_t s, int64_t b,
+                       int64_t h, int64_t d_h, int32_t P, int32_t dtype, void* stream) {
+  const int rc = check_push(x, y_ranks, rank, s, b, h, d_h, P, dtype, true);
+  if (rc != ULYS_OK) return rc;
+  const hipError_t e = ulys::launch_push(x, y_ranks, (uint32_t)((s / P) * b), (uint32_t)P,
+                                         (uint32_t)rank, (uint32_t)((h / P) * d_h * elt_size(dtype)),
+                                         true, (hipStream_t)stream);
+  return e == hipSuccess ? ULYS_OK : ULYS_ERR_HIP;
+}
+
+int ulys_head2seq_push(const void* o, void* const* x_ranks, int32_t rank, int64_t s, int64_t b,
+                       int64_t h, int64_t d_h, int32_t P, int32_t dtype, void* stream) {
+  const int rc = check_push(o, x_ranks, rank, s, b, h, d_h, P, dtype, false);
+  if (rc != ULYS_OK) return rc;
+  const hipError_t e = ulys::launch_push(o, x_ranks, (uint32_t)((s / P) * b), (uint32_t)P,
+                                         (uint32_t)rank, (uint32_t)((h / P) * d_h * elt_size(dtype)),
+                                         false, (hipStream_t)stream);
+  return e == hipSuccess ? ULYS_OK : ULYS_ERR_HIP;
+}
+
 int ulys_attn_merge(const void* o_a, const float* lse_a, const void* o_b, const float* lse_b,
                     void* o, float* lse, int64_t s, int64_t b, int64_t hp, int64_t d_h,
                     int32_t dtype, void* stream) {

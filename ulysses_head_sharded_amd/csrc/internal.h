@@ -50,6 +50,13 @@ hipError_t launch_replicate_runs(const void* in, void* out, uint32_t A, uint32_t
 hipError_t launch_pack_qkv(const void* const in[3], void* const out[3], uint32_t A, uint32_t P,
                            const uint32_t cols[3], const uint32_t run_bytes[3],
                            hipStream_t stream);
+// The exchange as pushes from one rank `src` to P destination pointers (runs
+// of run_bytes = hp*d*elt, A = s/P*b rows):
+//   seq2head: dst[r][src*A + a] = in[a*P + r]      (in: the rank's shard)
+//   head2seq: dst[j][a*P + src] = in[j*A + a]      (in: the rank's output share)
+// P <= 64.
+hipError_t launch_push(const void* in, void* const* dst, uint32_t A, uint32_t P, uint32_t src,
+                       uint32_t run_bytes, bool seq2head, hipStream_t stream);
 hipError_t launch_sum_runs(const void* in, void* out, uint32_t A, uint32_t C, uint32_t P,
                            uint32_t run_bytes, int elt, hipStream_t stream);
 

@@ -216,7 +216,77 @@ __global__ __launch_bounds__(kThreads) void pack_segments(PackSegs ps) {
       __builtin_nontemporal_load(&sg.in[(a * sg.cols_c + col) * sg.vpr.div + c]), &sg.out[gl]);
 }
 
+// ---- the exchange as pushes: the sender writes each block straight into its
+// destination's final layout ("02 · DeepSpeed-Ulysses" §2: send by head
+// group, the receiver concatenates along the sequence; the reverse exchange
+// sends by sequence segment and the receiver concatenates along heads), so
+// neither a local send buffer nor an unpack is needed.  The destinations are
+// P device pointers -- on a node, the ranks' receive buffers mapped into this
+// process; on one GPU, P regions of its own memory.  Output order walk, one
+// vector per thread; the pointer table travels in the kernel arguments.
+constexpr int kMaxRanks = 64;
+template <typename Vec>
+struct RankPtrs {
+  Vec* p[kMaxRanks];
+};
+
+// seq->head, from rank `src`: y_ranks[r][(src*A + a)*V + c] = x[(a*P + r)*V + c]
+// (A = s/P * b token-batch rows, V = vectors per run of hp*d elements)
+// head->seq, from rank `src`: x_ranks[j][(a*P + src)*V + c] = o[(j*A + a)*V + c]
+template <typename Vec, bool SEQ2HEAD>
+__global__ __launch_bounds__(kThreads) void push_runs(const Vec* __restrict__ in,
+                                                      RankPtrs<Vec> dst, uint32_t total,
+                                                      FastDiv vpr, FastDiv rows_a, uint32_t P,
+                                                      uint32_t src) {
+  const uint32_t g = blockIdx.x * kThreads + threadIdx.x;
+  if (g >= total) return;
+  const uint32_t run = fast_div(g, vpr);  // m*A + a: destination rank m, row a
+  const uint32_t c = g - run * vpr.div;
+  const uint32_t m = fast_div(run, rows_a);
+  const uint32_t a = run - m * rows_a.div;
+  const uint32_t V = vpr.div, A = rows_a.div;
+  if (SEQ2HEAD) {
+    __builtin_nontemporal_store(__builtin_nontemporal_load(&in[(a * P + m) * V + c]),
+                                &dst.p[m][(src * A + a) * V + c]);
+  } else {
+    __builtin_nontemporal_store(__builtin_nontemporal_load(&in[(m * A + a) * V + c]),
+                                &dst.p[m][(a * P + src) * V + c]);
+  }
+}
+
+template <typename Vec>
+hipError_t launch_push_vec(const void* in, void* const* dst, uint32_t A, uint32_t P, uint32_t src,
+                           uint32_t run_bytes, bool seq2head, hipStream_t stream) {
+  RankPtrs<Vec> ptrs;
+  for (uint32_t r = 0; r < P; ++r) ptrs.p[r] = static_cast<Vec*>(dst[r]);
+  for (uint32_t r = P; r < (uint32_t)kMaxRanks; ++r) ptrs.p[r] = nullptr;
+  const uint32_t vpr = run_bytes / sizeof(Vec);
+  const uint64_t total = (uint64_t)P * A * vpr;
+  if (total == 0) return hipSuccess;
+  if (total >= (1ull << 32) - kThreads) return hipErrorInvalidValue;
+  const dim3 grid((uint32_t)((total + kThreads - 1) / kThreads));
+  if (seq2head)
+    hipLaunchKernelGGL((push_runs<Vec, true>), grid, dim3(kThreads), 0, stream,
+                       static_cast<const Vec*>(in), ptrs, (uint32_t)total, make_fastdiv(vpr),
+                       make_fastdiv(A), P, src);
+  else
+    hipLaunchKernelGGL((push_runs<Vec, false>), grid, dim3(kThreads), 0, stream,
+                       static_cast<const Vec*>(in), ptrs, (uint32_t)total, make_fastdiv(vpr),
+                       make_fastdiv(A), P, src);
+  return hipGetLastError();
+}
+
 }  // namespace
+
+hipError_t launch_push(const void* in, void* const* dst, uint32_t A, uint32_t P, uint32_t src,
+                       uint32_t run_bytes, bool seq2head, hipStream_t stream) {
+  if (P == 0 || P > (uint32_t)kMaxRanks || src >= P) return hipErrorInvalidValue;
+  if (run_bytes % 16 == 0)
+    return launch_push_vec<u32x4>(in, dst, A, P, src, run_bytes, seq2head, stream);
+  if (run_bytes % 4 == 0)
+    return launch_push_vec<uint32_t>(in, dst, A, P, src, run_bytes, seq2head, stream);
+  return launch_push_vec<uint16_t>(in, dst, A, P, src, run_bytes, seq2head, stream);
+}
 
 hipError_t launch_pack_qkv(const void* const in[3], void* const out[3], uint32_t A, uint32_t P,
                            const uint32_t cols[3], const uint32_t run_bytes[3],
