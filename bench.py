@@ -92,7 +92,10 @@ def counter_traffic(kernel_src: str, workload: str):
         for line in f:
             if ":" in line and not line.startswith("#"):
                 key, val = line.split(":", 1)
-                fields[key.strip()] = val.strip()
+                key = key.strip()
+                if key == "kernel" and "kernel" in fields:
+                    break  # only the first section describes the attention call
+                fields[key] = val.strip()
     if fields.get("source_sha256") != source_digest(kernel_src):
         return None
     try:
