@@ -155,6 +155,40 @@ def test_large_scores_stay_finite():
         assert np.max(np.abs(as_f64(o) - o_ref)) <= TOL["bf16"]
 
 
+def rising_scores_inputs(seed, s, b, h, d, log2_jump_per_tile):
+    """Q near a common direction u and keys along u with a magnitude that grows
+    with the key index, so a row's scores rise from tile to tile by about
+    `log2_jump_per_tile` (log2 units, i.e. scaled by log2(e)/sqrt(d)): every
+    64-key tile passes the row's earlier max by that much."""
+    q, k, v = share_inputs(seed, s, b, h, h, d, "f32")
+    u = np.ones(d)
+    raw_per_key = log2_jump_per_tile * np.sqrt(d) / np.log2(np.e) / 64.0
+    a = raw_per_key / d * np.arange(s)  # score of key j against u: d * a_j
+    qd = u[None, None, None, :] + 0.05 * q
+    kd = a[:, None, None, None] * u[None, None, None, :] + 0.05 * k
+    return (synth.f32_to_bf16_bits(qd.astype(np.float32)),
+            synth.f32_to_bf16_bits(kd.astype(np.float32)), synth.f32_to_bf16_bits(v))
+
+
+@pytest.mark.parametrize("ws", [False, True], ids=["plain", "ws"])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("jump", [15.0, 100.0], ids=["rescale", "overflow-retry"])
+def test_rising_scores(jump, causal, ws):
+    """Scores that keep rising along the keys.  A jump of 15 log2 units per
+    tile makes the fast steps' probability sums pass 2^8, so the reference
+    max moves after the PV product; 100 per tile would overflow them, so the
+    unit is redone with the row max on every tile.  Both must match the
+    oracle."""
+    s, b, h, d = 1024, 1, 2, 128
+    q, k, v = rising_scores_inputs(15, s, b, h, d, jump)
+    o, lse = gpu_attn(q, k, v, s, b, h, h, d, 1, causal, "bf16", ws=ws)
+    o_ref, lse_ref = oracle.attn(q, k, v, s, b, h, h, d, 1, causal)
+    assert np.all(np.isfinite(as_f64(o))) and np.all(np.isfinite(lse))
+    assert np.max(np.abs(as_f64(o) - o_ref)) <= TOL["bf16"]
+    # lse is in the thousands here; bf16 inputs make fp32 scores exact to ~1e-7 relative
+    assert np.max(np.abs(lse - lse_ref) / np.maximum(1.0, np.abs(lse_ref))) <= 1e-5
+
+
 def test_deterministic():
     s, b, h, h_kv, d = 2048, 2, 8, 2, 128
     q, k, v = share_inputs(14, s, b, h, h_kv, d, "bf16")

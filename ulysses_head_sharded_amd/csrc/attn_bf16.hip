@@ -32,9 +32,16 @@
 //    and the ragged tail needs no branch.  Tile rows are unpadded with
 //    XOR-swizzled 16-byte chunks chosen so the MFMA K reads and the
 //    transposing V reads are free of bank conflicts.
-//  * exp2 with log2(e)/sqrt(d_h) folded into one FMA per score; the online
-//    rescale runs only when some row's max grew; causal tiles above a wave's
-//    diagonal are skipped and only diagonal / tail tiles are masked.
+//  * exp2 with log2(e)/sqrt(d_h) folded into one FMA per score; causal tiles
+//    above a wave's diagonal are skipped and only diagonal / tail tiles are
+//    masked.
+//  * The row max is taken only on a unit's first tile and on masked tiles.
+//    Every other tile's probabilities are taken against the row's current
+//    reference max, and only their sum is checked afterwards: a row whose
+//    sum passed 2^8 moves its reference up by log2 of that sum (an upper
+//    bound of the tile's max) and rescales.  Scores that jump so far within
+//    one tile that the sum passes 2^64 flag the wave, which then redoes its
+//    rows with the row max on every tile, reading K and V from global memory.
 //  * Work items are ordered longest-first (causal), which the dispatcher turns
 //    into a longest-processing-time-first schedule; with a workspace, causal
 //    shares with few items split every item's keys in two halves that a
@@ -231,12 +238,9 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bf16_kernel(Params p) {
     v_src[i] = row * p.kv_tok_bytes + kv_head_off + ((pc ^ v_swz<D>(row)) << 4);
   }
   f32x16 oacc[D / 32];
-#pragma unroll
-  for (int db = 0; db < D / 32; ++db)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) oacc[db][r] = 0.f;
-  float m_run = -INFINITY;  // running max of raw scores (q.k)
-  float l_run = 0.f;        // this lane's share of the running sum
+  float m_run;  // reference max of raw scores (q.k) the exponents subtract
+  float l_run;  // this lane's share of the running sum
+  bool overflow = false;  // a fast step's probabilities got too large
 
   // K tile t goes to K buffer (t - t_lo) % 2 and V tile t to V buffer
   // (t - t_lo) % 2.  Past the unit's last tile the source is clamped to it
@@ -304,6 +308,36 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bf16_kernel(Params p) {
         oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[ks], oacc[db], 0, 0, 0);
       }
   };
+  // S^T blocks of tile t read straight from global memory (rows past the
+  // sequence read as zero, as in the LDS loads)
+  auto qk_global = [&](int t, f32x16* sc) {
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) sc[kb][r] = 0.f;
+      const int off = (t * kBN + kb * 32 + l32) * p.kv_tok_bytes + kv_head_off + hh * 16;
+#pragma unroll
+      for (int dk = 0; dk < D / 16; ++dk) {
+        const bf16x8 a = as_bf16x8(__builtin_amdgcn_raw_buffer_load_b128(rk, off + dk * 32, 0, 0));
+        sc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[dk], sc[kb], 0, 0, 0);
+      }
+    }
+  };
+  // scores of tile t past the sequence end or above the causal diagonal -> -inf
+  auto needs_mask = [&](int t) {
+    const int k0 = t * kBN;
+    return (k0 + kBN > p.s) || (CAUSAL && k0 + kBN - 1 > q0);
+  };
+  auto mask = [&](int t, f32x16* sc) {
+    const int k0 = t * kBN;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int key = k0 + kb * 32 + 8 * (r >> 2) + 4 * hh + (r & 3);
+        if (key >= p.s || (CAUSAL && key > my_q)) sc[kb][r] = -INFINITY;
+      }
+  };
   // online-softmax step on the scores of one tile.  The reference max m_run
   // that the exponents subtract moves only when a row's tile max exceeds it
   // by more than p.lazy (8 in log2 units): any m_run at least the true max
@@ -331,10 +365,10 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bf16_kernel(Params p) {
     }
     return (m_run == -INFINITY) ? 0.f : m_run * p.c;
   };
-  // probabilities exp2(s c - m c) of one tile, summed in fp32 into l_run and
-  // packed to bf16 as the P^T operands: 16-key step ks uses registers
-  // 8 (ks%2) .. +7 of block ks/2
-  auto probs = [&](f32x16* sc, float base, bf16x8* pb) {
+  // probabilities exp2(s c - m c) of one tile, packed to bf16 as the P^T
+  // operands (16-key step ks uses registers 8 (ks%2) .. +7 of block ks/2);
+  // returns their fp32 sum over this lane's 32 keys
+  auto probs = [&](f32x16* sc, float base, bf16x8* pb) -> float {
     float ps = 0.f;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
@@ -344,11 +378,72 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bf16_kernel(Params p) {
         sc[kb][r] = e;
         ps += e;
       }
-    l_run += ps;
 #pragma unroll
     for (int ks = 0; ks < kBN / 16; ++ks)
 #pragma unroll
       for (int e = 0; e < 8; ++e) pb[ks][e] = (__bf16)sc[ks >> 1][(ks & 1) * 8 + e];
+    return ps;
+  };
+  // After a fast step (probabilities against the current reference, no row
+  // max): a row whose tile sum -- over both partner lanes -- passed 2^8 had
+  // a score more than 8 (log2 units) above the reference, or many near it.
+  // Its reference moves up by log2 of that sum, which bounds the tile's max
+  // from above (the sum is at least its largest term), and the running sum
+  // and accumulator are scaled by its inverse -- the same rescale a max
+  // would give, with another valid reference.  A sum beyond 2^64 (or not a
+  // number) flags the unit: its accumulator may have lost range, and it is
+  // redone with the row max on every tile.
+  auto settle = [&](float ps) {
+    const float pair = xsum32(ps);
+    overflow |= !(pair <= 0x1p64f);
+    if (pair > 256.f && pair <= 0x1p64f) {
+      const float alpha = __builtin_amdgcn_rcpf(pair);
+      m_run += __builtin_amdgcn_logf(pair) * (p.lazy * 0.125f);  // log2(pair) / c
+      l_run *= alpha;
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
+    }
+  };
+
+  // O^T += V^T P^T for tile t with V^T read from global memory: the A operand
+  // slot e of lane (feature f, half hh) is key 16 ks + 8 (e/4) + 4 hh + e%4,
+  // the key the P^T slot e of the same half holds (rows past the sequence
+  // read as zero).
+  auto pv_global = [&](int t, const bf16x8* pb) {
+#pragma unroll
+    for (int ks = 0; ks < kBN / 16; ++ks)
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db) {
+        bf16x8 a;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const int key = t * kBN + 16 * ks + 8 * (e >> 2) + 4 * hh + (e & 3);
+          const int off = key * p.kv_tok_bytes + kv_head_off + (db * 32 + l32) * 2;
+          a[e] = __builtin_bit_cast(__bf16, (uint16_t)__builtin_amdgcn_raw_buffer_load_b16(rv, off, 0, 0));
+        }
+        oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[ks], oacc[db], 0, 0, 0);
+      }
+  };
+  auto redo_from_global = [&]() {
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) oacc[db][r] = 0.f;
+    m_run = -INFINITY;
+    l_run = 0.f;
+    const int t_end = min(wave_tiles, n_tiles);
+#pragma unroll 1
+    for (int t = t_lo; t < t_end; ++t) {
+      f32x16 sc[2];
+      qk_global(t, sc);
+      if (needs_mask(t)) mask(t, sc);
+      const float base = update_max(sc);
+      bf16x8 pb[kBN / 16];
+      l_run += probs(sc, base, pb);
+      pv_global(t, pb);
+    }
   };
 
   // ---- software pipeline over the unit's key tiles [t_lo, n_tiles).  On
@@ -365,31 +460,27 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bf16_kernel(Params p) {
   auto step = [&](int t, f32x16* cur, f32x16* nxt) {
     const int k0 = t * kBN;
     const bool need_mask = (k0 + kBN > p.s) || (CAUSAL && k0 + kBN - 1 > q0);
-    if (t < wave_tiles && !need_mask && t + 1 < wave_tiles) {
-      // steady state: one basic block after the rescale test
-      const float base = update_max(cur);
+    if (t > t_lo && t < wave_tiles && !need_mask && t + 1 < wave_tiles) {
+      // steady state, fast: no row max.  The probabilities of S_t are taken
+      // against the reference max as it stands (every row has seen visible
+      // keys in tile t_lo, so it is finite), and the rule that bounds them
+      // is applied afterwards (settle).  One basic block up to that test.
       qk(t + 1, nxt);
       bf16x8 pb[kBN / 16];
-      probs(cur, base, pb);
+      const float ps = probs(cur, m_run * p.c, pb);
       load_k(t + 2);
       load_v(t + 1);
       pv(t, pb);
+      l_run += ps;
+      if (__ballot(ps > 256.f) != 0) settle(ps);
     } else {
       load_k(t + 2);
       load_v(t + 1);
       if (t < wave_tiles) {
-        if (need_mask) {
-#pragma unroll
-          for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-              const int key = k0 + kb * 32 + 8 * (r >> 2) + 4 * hh + (r & 3);
-              if (key >= p.s || (CAUSAL && key > my_q)) cur[kb][r] = -INFINITY;
-            }
-        }
+        if (need_mask) mask(t, cur);
         const float base = update_max(cur);
         bf16x8 pb[kBN / 16];
-        probs(cur, base, pb);
+        l_run += probs(cur, base, pb);
         if (t + 1 < wave_tiles) qk(t + 1, nxt);
         pv(t, pb);
       }
@@ -399,6 +490,12 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bf16_kernel(Params p) {
     __syncthreads();
   };
 
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) oacc[db][r] = 0.f;
+  m_run = -INFINITY;
+  l_run = 0.f;
   f32x16 sa[2], sb[2];
   if (t_lo < n_tiles) {
     load_k(t_lo);
@@ -416,6 +513,12 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bf16_kernel(Params p) {
     step(t, sa, sb);
     if (t + 1 < n_tiles) step(t + 1, sb, sa);
   }
+  // Only if a fast step flagged an overflow (scores that jump by more than
+  // ~64 log2 units past a row's reference within one tile, so that the
+  // accumulator may have lost range): this wave's rows again, every tile with
+  // the row max, K and V read from global memory (the other waves have
+  // moved on, so the LDS tiles and barriers are not available).
+  if (__ballot(overflow) != 0) redo_from_global();
 
   if (p.nsplit == 2) {
     // partial state of this half, lanes contiguous: [wave][slot][lane]
