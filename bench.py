@@ -47,6 +47,9 @@ def parse_args():
     ap.add_argument("--push-steps", type=int, default=20,
                     help="timed pushes of the Q shard into P share buffers on this GPU "
                          "(ulys_seq2head_push), reported under 'exchange_push'; 0 skips them")
+    ap.add_argument("--layout-calls", type=int, default=64,
+                    help="pack and unpack calls over rotating buffer sets of >= 2 GiB, "
+                         "reported under 'layout_hbm'; 0 skips them")
     ap.add_argument("--bwd-steps", type=int, default=100,
                     help="timed backward steps (pack dO, attention backward, unpack dQ, dK, "
                          "dV) reported under 'backward'; 0 skips them")
@@ -197,6 +200,70 @@ def bench_push(args, w, binding, torch, np, xq, tdt, code, stream):
     return {"calls": args.push_steps, "us": round(us, 2), "bytes": nbytes,
             "gbps": round(nbytes / (us * 1e-6) / 1e9, 1),
             "frac_hbm_peak": round(nbytes / (us * 1e-6) / 1e9 / PEAK_HBM_GBPS, 4)}
+
+
+def bench_layout_hbm(args, w, binding, torch, tdt, code, stream):
+    """The step's layout kernels streaming from HBM: the fused Q/K/V pack and
+    the O unpack, called back to back over rotating buffer sets whose total is
+    at least 2 GiB (8x the 256 MiB last-level cache), so no call finds its
+    inputs cached; one event pair around each run of calls."""
+    sl, hp, hkvp = w.s // w.P, w.hp, w.hkvp
+    dev = stream.device
+
+    def new_set():
+        return {"xq": torch.empty((sl, w.b, w.h, w.d), dtype=tdt, device=dev),
+                "xk": torch.empty((sl, w.b, w.h_kv, w.d), dtype=tdt, device=dev),
+                "xv": torch.empty((sl, w.b, w.h_kv, w.d), dtype=tdt, device=dev),
+                "yq": torch.empty((w.P, sl, w.b, hp, w.d), dtype=tdt, device=dev),
+                "yk": torch.empty((w.P, sl, w.b, hkvp, w.d), dtype=tdt, device=dev),
+                "yv": torch.empty((w.P, sl, w.b, hkvp, w.d), dtype=tdt, device=dev),
+                "o": torch.empty((w.s, w.b, hp, w.d), dtype=tdt, device=dev),
+                "xo": torch.empty((sl, w.b, w.h, w.d), dtype=tdt, device=dev)}
+
+    pack_bytes = 2 * w.shard_bytes() + 2 * (w.shard_bytes(kv=True) + w.kv_blocks_bytes())
+    unpack_bytes = 2 * w.shard_bytes()
+    n_sets = max(2, -(-(2 << 30) // (pack_bytes + unpack_bytes)))
+    sets = [new_set() for _ in range(n_sets)]
+    sh = stream.cuda_stream
+
+    def pack(t):
+        rc = binding.ulys_pack_seq2head_qkv(t["xq"].data_ptr(), t["xk"].data_ptr(),
+                                            t["xv"].data_ptr(), t["yq"].data_ptr(),
+                                            t["yk"].data_ptr(), t["yv"].data_ptr(), w.s, w.b,
+                                            w.h, w.h_kv, w.d, w.P, code, sh)
+        if rc != 0:
+            raise RuntimeError(f"pack qkv: {binding.ulys_status_string(rc)}")
+
+    def unpack(t):
+        rc = binding.ulys_unpack_head2seq(t["o"].data_ptr(), t["xo"].data_ptr(), w.s, w.b, w.h,
+                                          w.d, w.P, code, sh)
+        if rc != 0:
+            raise RuntimeError(f"unpack o: {binding.ulys_status_string(rc)}")
+
+    def timed(fn, passes):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for _ in range(passes):
+            for t in sets:
+                fn(t)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e3 / (passes * n_sets)  # us per call
+
+    for t in sets:
+        pack(t)
+        unpack(t)
+    passes = max(1, args.layout_calls // n_sets)
+    pack_us, unpack_us = timed(pack, passes), timed(unpack, passes)
+    del sets
+    gbps = (pack_bytes + unpack_bytes) / ((pack_us + unpack_us) * 1e-6) / 1e9
+    return {"sets": n_sets, "set_bytes": pack_bytes + unpack_bytes, "calls": passes * n_sets,
+            "pack_qkv_us": round(pack_us, 2),
+            "pack_gbps": round(pack_bytes / (pack_us * 1e-6) / 1e9, 1),
+            "unpack_o_us": round(unpack_us, 2),
+            "unpack_gbps": round(unpack_bytes / (unpack_us * 1e-6) / 1e9, 1),
+            "gbps": round(gbps, 1), "frac_hbm_peak": round(gbps / PEAK_HBM_GBPS, 4)}
 
 
 def bench_backward(args, w, binding, torch, np, q, k, v, code, stream):
@@ -420,6 +487,8 @@ def main():
                      "unit": "TFLOP/s", "frac": round(attn_tflops / peak, 4),
                      "traffic": counter_traffic(kernel_src, w.name)},
     }
+    if args.layout_calls > 0:
+        rec["layout_hbm"] = bench_layout_hbm(args, w, binding, torch, tdt, code, stream)
     if args.merge_steps > 0:
         rec["merge"] = bench_merge(args, w, binding, torch, np, o, code, stream)
     if args.push_steps > 0:
