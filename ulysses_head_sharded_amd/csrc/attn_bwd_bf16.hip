@@ -41,6 +41,8 @@
 // of bank conflicts on the 64-bank LDS.
 #include <math.h>
 
+#include <type_traits>
+
 #include "cdna4.h"
 #include "internal.h"
 
@@ -312,17 +314,18 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dq_kernel(BwdParams p) {
   if (t_lo < t_hi) load_tile(t_lo, 0);
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
-  for (int t = t_lo; t < t_hi; ++t) {
-    const int cur = (t - t_lo) & 1;
+  // one key tile t in buffer CUR
+  auto dq_step = [&](int t, auto cur_tag) __attribute__((always_inline)) {
+    constexpr int cur = decltype(cur_tag)::value;
     if (t + 1 < t_hi) load_tile(t + 1, cur ^ 1);
     if (t < wave_tiles) {
       const uint8_t* kl = lds + cur * kTile;
       const uint8_t* vl = lds + (2 + cur) * kTile;
       const int k0 = t * kBN;
-      // the tile's two 32-key halves in turn (kept apart to bound registers).
+      // the tile's two 32-key halves in turn.
       // S^T and dP^T of half kb: keys k0 + 32 kb + (8 (r/4) + 4 hh + r%4),
       // query my_q
-#pragma unroll 1
+#pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
         const uint8_t* kh = kl + kb * 32 * ROW;
         f32x16 sc, dp;
@@ -369,6 +372,11 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dq_kernel(BwdParams p) {
     }
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
+  };
+  // unrolled by two so every buffer index is a compile-time constant
+  for (int t = t_lo; t < t_hi; t += 2) {
+    dq_step(t, std::integral_constant<int, 0>{});
+    if (t + 1 < t_hi) dq_step(t + 1, std::integral_constant<int, 1>{});
   }
   if (p.q_split) {
     store_part<D / 32>(p.part + (int64_t)blockIdx.x * kDqPart, acc, wave, lane);
@@ -416,12 +424,14 @@ __device__ __forceinline__ KItem decode_k_item(const BwdParams& p, int rank) {
 
 template <bool CAUSAL>
 __global__ __launch_bounds__(kThreads, 1) void bwd_dkv_kernel(BwdParams p) {
-  // LDS: V block | Q0 Q1 | dout0 dout1 | stats0 stats1
+  // LDS: Q0 Q1 | dout0 dout1 | V block | stats0 stats1.  The tiles first:
+  // with the buffer and half indices compile-time constants, every tile read
+  // is one lane register plus an offset that fits the instruction's 16 bits.
   __shared__ __attribute__((aligned(16))) uint8_t lds[kDkvLds];
-  uint8_t* vblk = lds;
-  uint8_t* qt = lds + kVBlock;
+  uint8_t* qt = lds;
   uint8_t* gt = qt + 2 * kQTile;
-  uint8_t* stt = gt + 2 * kQTile;
+  uint8_t* vblk = gt + 2 * kQTile;
+  uint8_t* stt = vblk + kVBlock;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
   const int l32 = lane & 31, hh = lane >> 5;
@@ -512,11 +522,12 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkv_kernel(BwdParams p) {
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
   const uint8_t* vrow = vblk + wave * 32 * ROW;  // this wave's V rows
-  for (int st = st_lo; st < st_hi; ++st) {
-    const int cur = (st - st_lo) & 1;
+  // one step: query tile st in buffer CUR, its two 32-query halves
+  auto dkv_step = [&](int st, auto cur_tag) __attribute__((always_inline)) {
+    constexpr int cur = decltype(cur_tag)::value;
     if (st + 1 < st_hi) load_step(st + 1, cur ^ 1);
     const int q0 = step_q0(st);
-#pragma unroll 1
+#pragma unroll
     for (int hq = 0; hq < kQT / 32; ++hq) {
       const int qr = q0 + 32 * hq;  // first query of this 32-query half
       // the wave's keys all come after these queries (causal), or either
@@ -589,6 +600,11 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkv_kernel(BwdParams p) {
     }
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
+  };
+  // unrolled by two so every buffer index is a compile-time constant
+  for (int st = st_lo; st < st_hi; st += 2) {
+    dkv_step(st, std::integral_constant<int, 0>{});
+    if (st + 1 < st_hi) dkv_step(st + 1, std::integral_constant<int, 1>{});
   }
   if (p.kv_split) {
     float* base = p.part + (int64_t)unit * kDkvPart;
