@@ -185,12 +185,15 @@ hipError_t launch_replicate_vec(const void* in, void* out, uint32_t A, uint32_t 
 // ---- Q, K and V packed by one launch.  Each segment is a pack whose output
 // run r*A + a (rank r, token-batch row a) comes from input run
 // a*C + r*C/P: C = P is the plain pack (run = the rank's head group), C = h_kv
-// < P the replicating one (run = one KV head).  Thread g finds its segment
-// from the segments' starting vectors, then walks that output in order.
+// < P the replicating one (run = one KV head).  Every segment starts at a
+// multiple of the workgroup size, so a workgroup finds its segment from its
+// first thread index (uniform: the segment's fields become scalar loads),
+// then each thread walks that output in order.
 struct PackSeg {
   const u32x4* in;
   u32x4* out;
-  uint32_t start;    // first global vector index of this segment
+  uint32_t start;    // first global vector index of this segment (a multiple of kThreads)
+  uint32_t n;        // vectors of this segment
   FastDiv vpr;       // vectors per run
   FastDiv rows_a;    // A = s/P * b
   uint32_t cols_c;   // input runs per token-batch row
@@ -202,11 +205,11 @@ struct PackSegs {
 };
 
 __global__ __launch_bounds__(kThreads) void pack_segments(PackSegs ps) {
-  const uint32_t g = blockIdx.x * kThreads + threadIdx.x;
-  if (g >= ps.total) return;
-  const int k = (g >= ps.seg[2].start) ? 2 : (g >= ps.seg[1].start) ? 1 : 0;
-  const PackSeg sg = ps.seg[k];
-  const uint32_t gl = g - sg.start;
+  const uint32_t g0 = blockIdx.x * kThreads;
+  const int k = (g0 >= ps.seg[2].start) ? 2 : (g0 >= ps.seg[1].start) ? 1 : 0;
+  const PackSeg& sg = ps.seg[k];
+  const uint32_t gl = g0 - sg.start + threadIdx.x;
+  if (gl >= sg.n) return;  // the padding up to the next segment's start
   const uint32_t run = fast_div(gl, sg.vpr);  // r*A + a
   const uint32_t c = gl - run * sg.vpr.div;
   const uint32_t r = fast_div(run, sg.rows_a);
@@ -298,11 +301,14 @@ hipError_t launch_pack_qkv(const void* const in[3], void* const out[3], uint32_t
     const uint32_t vpr = run_bytes[k] / 16;
     ps.seg[k].in = static_cast<const u32x4*>(in[k]);
     ps.seg[k].out = static_cast<u32x4*>(out[k]);
+    const uint64_t n = (uint64_t)P * A * vpr;
+    if (n >= (1ull << 32)) return hipErrorInvalidValue;
     ps.seg[k].start = (uint32_t)start;
+    ps.seg[k].n = (uint32_t)n;
     ps.seg[k].vpr = make_fastdiv(vpr);
     ps.seg[k].rows_a = make_fastdiv(A);
     ps.seg[k].cols_c = cols[k];
-    start += (uint64_t)P * A * vpr;
+    start += (n + kThreads - 1) / kThreads * kThreads;
     if (start >= (1ull << 32) - kThreads) return hipErrorInvalidValue;
   }
   ps.ranks = make_fastdiv(P);
