@@ -50,6 +50,10 @@ def parse_args():
     ap.add_argument("--layout-calls", type=int, default=64,
                     help="pack and unpack calls over rotating buffer sets of >= 2 GiB, "
                          "reported under 'layout_hbm'; 0 skips them")
+    ap.add_argument("--push-attn-calls", type=int, default=50,
+                    help="timed calls of the attention with the O exchange in its epilogue "
+                         "(ulys_attn_fwd_push) and of attention + unpack, reported under "
+                         "'attn_push'; 0 skips them")
     ap.add_argument("--bwd-steps", type=int, default=100,
                     help="timed backward steps (pack dO, attention backward, unpack dQ, dK, "
                          "dV) reported under 'backward'; 0 skips them")
@@ -264,6 +268,51 @@ def bench_layout_hbm(args, w, binding, torch, tdt, code, stream):
             "unpack_o_us": round(unpack_us, 2),
             "unpack_gbps": round(unpack_bytes / (unpack_us * 1e-6) / 1e9, 1),
             "gbps": round(gbps, 1), "frac_hbm_peak": round(gbps / PEAK_HBM_GBPS, 4)}
+
+
+def bench_attn_push(args, w, binding, torch, yq, yk, yv, o, xo, tdt, code, ws, ws_bytes, stream):
+    """The attention with the head->seq exchange in its epilogue
+    (ulys_attn_fwd_push, rank 0 writing its head columns into P destination
+    shards on this GPU) against the step's attention followed by the O unpack,
+    each timed back to back over the same number of calls."""
+    sl = w.s // w.P
+    dst = [torch.empty((sl, w.b, w.h, w.d), dtype=tdt, device=o.device) for _ in range(w.P)]
+    ptrs = [t.data_ptr() for t in dst]
+    sh = stream.cuda_stream
+
+    def fused():
+        rc = binding.ulys_attn_fwd_push(yq.data_ptr(), yk.data_ptr(), yv.data_ptr(), ptrs, 0, None,
+                                        w.s, w.b, w.h, w.h_kv, w.d, w.P, int(w.causal), code,
+                                        ws.data_ptr(), ws_bytes, sh)
+        if rc != 0:
+            raise RuntimeError(f"attn push: {binding.ulys_status_string(rc)}")
+
+    def separate():
+        rc = binding.ulys_attn_fwd_ws(yq.data_ptr(), yk.data_ptr(), yv.data_ptr(), o.data_ptr(),
+                                      None, w.s, w.b, w.h, w.h_kv, w.d, w.P, int(w.causal), code,
+                                      ws.data_ptr(), ws_bytes, sh)
+        if rc == 0:
+            rc = binding.ulys_unpack_head2seq(o.data_ptr(), xo.data_ptr(), w.s, w.b, w.h, w.d,
+                                              w.P, code, sh)
+        if rc != 0:
+            raise RuntimeError(f"attn + unpack: {binding.ulys_status_string(rc)}")
+
+    def timed(fn):
+        for _ in range(3):
+            fn()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for _ in range(args.push_attn_calls):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e3 / args.push_attn_calls
+
+    sep_us, fused_us = timed(separate), timed(fused)
+    return {"calls": args.push_attn_calls, "attn_then_unpack_us": round(sep_us, 2),
+            "attn_push_us": round(fused_us, 2),
+            "tflops": round(w.attn_flops() / (fused_us * 1e-6) / 1e12, 2)}
 
 
 def bench_backward(args, w, binding, torch, np, q, k, v, code, stream):
@@ -493,6 +542,9 @@ def main():
         rec["merge"] = bench_merge(args, w, binding, torch, np, o, code, stream)
     if args.push_steps > 0:
         rec["exchange_push"] = bench_push(args, w, binding, torch, np, xq, tdt, code, stream)
+    if args.push_attn_calls > 0 and w.dtype == "bf16":
+        rec["attn_push"] = bench_attn_push(args, w, binding, torch, yq, yk, yv, o, xo, tdt, code,
+                                           ws, ws_bytes, stream)
     if args.bwd_steps > 0 and w.dtype == "bf16":
         rec["backward"] = bench_backward(args, w, binding, torch, np, yq, yk, yv, code, stream)
     if not args.no_cpu_baseline:

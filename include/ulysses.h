@@ -287,6 +287,33 @@ int ulys_head2seq_push(const void* o, void* const* x_ranks, int32_t rank, int64_
                        int64_t h, int64_t d_h, int32_t P, int32_t dtype, void* stream);
 
 /*
+ * Attention of one rank's share with the head->seq exchange fused into its
+ * epilogue: the result of ulys_attn_fwd_ws followed by ulys_head2seq_push,
+ * without the output tensor in between.  Query row t of the share (global
+ * position t) is written, rounded once to bf16, into rank j = t / sl's shard
+ * x_ranks[j] [sl, b, h, d_h] at token t % sl, heads [rank*hp, (rank+1)*hp)
+ * ([ATLAS] §2: the reverse exchange sends by sequence segment, the receiver
+ * concatenates along heads; [ATLAS] §1 / [DSU] step 4 for the attention).
+ * On a node the destinations are the ranks' shards mapped into this process,
+ * so the output crosses xGMI once, straight from the attention kernel.
+ *
+ *   q, k, v, lse, s, b, h, h_kv, d_h, P, causal, workspace: as
+ *             ulys_attn_fwd_ws (lse [b, hp, s] stays local; may be NULL)
+ *   x_ranks : HOST array of P device pointers, rank j's shard; only this
+ *             rank's head columns are written
+ *   rank    : this rank, 0 <= rank < P <= ULYS_MAX_RANKS
+ *   dtype   : ULYS_BF16 only (ULYS_ERR_UNSUPPORTED otherwise)
+ * Same values, bit for bit, as ulys_attn_fwd_ws with the same workspace
+ * followed by ulys_head2seq_push.  Errors: as ulys_attn_fwd_ws and
+ * ulys_head2seq_push (a written range of a destination overlapping q, k, v,
+ * lse, the workspace or another destination's is ULYS_ERR_ALIAS).
+ */
+int ulys_attn_fwd_push(const void* q, const void* k, const void* v, void* const* x_ranks,
+                       int32_t rank, float* lse, int64_t s, int64_t b, int64_t h, int64_t h_kv,
+                       int64_t d_h, int32_t P, int32_t causal, int32_t dtype, void* workspace,
+                       int64_t workspace_bytes, void* stream);
+
+/*
  * Merge of two partial attention results of one share over disjoint key sets.
  * [SPCP] (Ring section): each query row's online-softmax state -- running
  * max, scaled sum, scaled weighted sum of values -- is brought to a common max
@@ -319,7 +346,7 @@ const char* ulys_status_string(int status);
 /* ABI version of this header: (major << 16) | minor. */
 int ulys_abi_version(void);
 
-#define ULYS_ABI_VERSION ((1 << 16) | 6)
+#define ULYS_ABI_VERSION ((1 << 16) | 7)
 
 #ifdef __cplusplus
 }

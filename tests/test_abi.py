@@ -36,7 +36,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_version(lib):
-    assert B.ulys_abi_version() == (1 << 16) | 6
+    assert B.ulys_abi_version() == (1 << 16) | 7
 
 
 def test_status_strings(lib):
@@ -301,3 +301,44 @@ def test_push_rejects(lib, fn, kw, expect):
     a.update(kw)
     assert fn(a["x"], a["dst"], a["rank"], a["s"], a["b"], a["h"], a["d"], a["P"],
               a["dtype"]) == expect
+
+
+# ------------------------------------------------------ attention with a pushing epilogue
+AQ, AK, AV = (0x7F0000000000 + (40 + i) * (1 << 32) for i in range(3))
+AD = [0x7F0000000000 + (50 + r) * (1 << 32) for r in range(4)]
+AL, AW = 0x7F0000000000 + 60 * (1 << 32), 0x7F0000000000 + 61 * (1 << 32)
+
+
+@pytest.mark.parametrize("kw,expect", [
+    (dict(q=None), B.ULYS_ERR_NULL),
+    (dict(dst=None), B.ULYS_ERR_NULL),
+    (dict(dst=[AD[0], None, AD[2], AD[3]]), B.ULYS_ERR_NULL),
+    (dict(rank=4), B.ULYS_ERR_DIM),
+    (dict(rank=-1), B.ULYS_ERR_DIM),
+    (dict(s=18), B.ULYS_ERR_DIVISIBILITY),
+    (dict(h_kv=3), B.ULYS_ERR_DIVISIBILITY),
+    (dict(dtype=B.ULYS_F32), B.ULYS_ERR_UNSUPPORTED),  # fp32 has no pushing epilogue
+    (dict(d=96), B.ULYS_ERR_UNSUPPORTED),
+    (dict(q=AQ + 8), B.ULYS_ERR_ALIGNMENT),
+    (dict(dst=[AD[0], AD[1], AD[2] + 4, AD[3]]), B.ULYS_ERR_ALIGNMENT),
+    (dict(lse=AL + 4), B.ULYS_ERR_ALIGNMENT),
+    (dict(dst=[AD[0], AD[0], AD[2], AD[3]]), B.ULYS_ERR_ALIAS),     # two ranks, one buffer
+    (dict(dst=[AD[0], AQ, AD[2], AD[3]]), B.ULYS_ERR_ALIAS),        # over q
+    # rank 1 writes from byte hp*d*2 = 512 of each destination on: over lse
+    (dict(dst=[AD[0], AD[1], AD[2], AL - 512]), B.ULYS_ERR_ALIAS),
+    (dict(dst=[AW, AD[1], AD[2], AD[3]], ws=AW, wsb=1 << 20), B.ULYS_ERR_ALIAS),
+    (dict(lse=AK), B.ULYS_ERR_ALIAS),
+])
+def test_attn_push_rejects(lib, kw, expect):
+    a = dict(q=AQ, k=AK, v=AV, dst=AD, rank=1, lse=AL, s=64, b=1, h=8, h_kv=4, d=128, P=4,
+             causal=1, dtype=B.ULYS_BF16, ws=None, wsb=0)
+    a.update(kw)
+    if a["dst"] is None:
+        rc = B.load().ulys_attn_fwd_push(a["q"], a["k"], a["v"], None, a["rank"], a["lse"], a["s"],
+                                         a["b"], a["h"], a["h_kv"], a["d"], a["P"], a["causal"],
+                                         a["dtype"], a["ws"], a["wsb"], None)
+    else:
+        rc = B.ulys_attn_fwd_push(a["q"], a["k"], a["v"], a["dst"], a["rank"], a["lse"], a["s"],
+                                  a["b"], a["h"], a["h_kv"], a["d"], a["P"], a["causal"],
+                                  a["dtype"], a["ws"], a["wsb"])
+    assert rc == expect

@@ -110,3 +110,51 @@ def test_layer_on_pushes(causal):
     err = np.max(np.abs(as_f64(got) - ref))
     print(f"  o: max err {err:.3e}", flush=True)
     assert err <= 2e-2
+
+
+# (s, b, h, h_kv, d, P, rank, causal): a wave's 32 rows inside one sequence
+# segment (sl = 64) and across segment boundaries (sl = 25, 40, 125), GQA,
+# d = 64, and the 32K share, whose workspace path splits every item
+ATTN_PUSH = [(256, 1, 8, 4, 128, 4, 1, True), (100, 2, 8, 8, 128, 4, 3, False),
+             (320, 1, 16, 2, 64, 8, 5, True), (1000, 1, 8, 2, 128, 8, 0, True),
+             (1000, 2, 8, 8, 128, 8, 7, False), (32768, 1, 16, 16, 128, 8, 3, True)]
+
+
+@pytest.mark.parametrize("ws", [False, True], ids=["plain", "ws"])
+@pytest.mark.parametrize("s,b,h,h_kv,d,P,rank,causal", ATTN_PUSH)
+def test_attn_push_equals_attn_then_push(s, b, h, h_kv, d, P, rank, causal, ws):
+    """ulys_attn_fwd_push writes, bit for bit, what ulys_attn_fwd_ws followed by
+    ulys_head2seq_push writes: this rank's head columns of every destination
+    shard (the rest, and the guard bands, untouched), and the same lse."""
+    print(f"case attn_push s={s} b={b} h={h} h_kv={h_kv} d={d} P={P} rank={rank} "
+          f"causal={causal} ws={ws}", flush=True)
+    sl, hp, hkvp = s // P, h // P, binding.kv_heads_per_rank(h_kv, P)
+    from gpu_util import share_inputs
+    q, k, v = share_inputs(40 + P, s, b, hp, hkvp, d, "bf16")
+    qd, kd, vd = to_dev(q), to_dev(k), to_dev(v)
+    code = binding.ULYS_BF16
+    nbytes = binding.ulys_attn_fwd_workspace_size(s, b, h, h_kv, d, P, int(causal), code) if ws else 0
+    assert nbytes >= 0
+    wsbuf = torch.empty(max(nbytes, 16), dtype=torch.uint8, device="cuda")
+    wsp = wsbuf.data_ptr() if nbytes > 0 else None
+    o = torch.empty((s, b, hp, d), dtype=torch.bfloat16, device="cuda")
+    lse_ref = torch.empty((b, hp, s), dtype=torch.float32, device="cuda")
+    rc = binding.ulys_attn_fwd_ws(qd.data_ptr(), kd.data_ptr(), vd.data_ptr(), o.data_ptr(),
+                                  lse_ref.data_ptr(), s, b, h, h_kv, d, P, int(causal), code, wsp,
+                                  nbytes, stream())
+    assert rc == 0, binding.ulys_status_string(rc)
+    ref = [Guarded((sl, b, h, d), torch.bfloat16) for _ in range(P)]
+    rc = binding.ulys_head2seq_push(o.data_ptr(), [g.tensor.data_ptr() for g in ref], rank, s, b,
+                                    h, d, P, code, stream())
+    assert rc == 0, binding.ulys_status_string(rc)
+    got = [Guarded((sl, b, h, d), torch.bfloat16) for _ in range(P)]
+    lse = Guarded((b, hp, s), torch.float32)
+    rc = binding.ulys_attn_fwd_push(qd.data_ptr(), kd.data_ptr(), vd.data_ptr(),
+                                    [g.tensor.data_ptr() for g in got], rank, lse.tensor.data_ptr(),
+                                    s, b, h, h_kv, d, P, int(causal), code, wsp, nbytes, stream())
+    assert rc == 0, binding.ulys_status_string(rc)
+    torch.cuda.synchronize()
+    for j in range(P):
+        assert torch.equal(got[j].raw, ref[j].raw), j
+    assert lse.guards_intact()
+    assert torch.equal(lse.tensor, lse_ref)

@@ -23,7 +23,7 @@ ULYS_ERR_UNSUPPORTED, ULYS_ERR_ALIGNMENT, ULYS_ERR_ALIAS, ULYS_ERR_HIP = -4, -5,
 EXPORTED = ("ulys_pack_seq2head", "ulys_unpack_head2seq", "ulys_pack_seq2head_kv",
             "ulys_unpack_head2seq_kv", "ulys_pack_seq2head_qkv", "ulys_attn_fwd", "ulys_attn_fwd_ws",
             "ulys_attn_fwd_workspace_size", "ulys_attn_bwd", "ulys_attn_bwd_workspace_size",
-            "ulys_attn_merge", "ulys_seq2head_push", "ulys_head2seq_push",
+            "ulys_attn_merge", "ulys_seq2head_push", "ulys_head2seq_push", "ulys_attn_fwd_push",
             "ulys_status_string", "ulys_abi_version")
 
 _lib = None
@@ -72,6 +72,9 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.ulys_seq2head_push.restype = ctypes.c_int
     lib.ulys_head2seq_push.argtypes = push
     lib.ulys_head2seq_push.restype = ctypes.c_int
+    lib.ulys_attn_fwd_push.argtypes = [vp, vp, vp, ctypes.POINTER(vp), i32, vp] + [i64] * 5 + \
+        [i32, i32, i32, vp, i64, vp]
+    lib.ulys_attn_fwd_push.restype = ctypes.c_int
     lib.ulys_attn_merge.argtypes = [vp] * 6 + [i64] * 4 + [i32, vp]
     lib.ulys_attn_merge.restype = ctypes.c_int
     lib.ulys_status_string.argtypes = [ctypes.c_int]
@@ -146,6 +149,13 @@ def ulys_seq2head_push(x, y_ranks, rank, s, b, h, d_h, P, dtype, stream=None) ->
 def ulys_head2seq_push(o, x_ranks, rank, s, b, h, d_h, P, dtype, stream=None) -> int:
     """x_ranks: sequence of P device addresses (ints)."""
     return load().ulys_head2seq_push(o, _ptr_table(x_ranks), rank, s, b, h, d_h, P, dtype, stream)
+
+
+def ulys_attn_fwd_push(q, k, v, x_ranks, rank, lse, s, b, h, h_kv, d_h, P, causal, dtype,
+                       workspace, workspace_bytes, stream=None) -> int:
+    """x_ranks: sequence of P device addresses (ints)."""
+    return load().ulys_attn_fwd_push(q, k, v, _ptr_table(x_ranks), rank, lse, s, b, h, h_kv, d_h,
+                                     P, causal, dtype, workspace, workspace_bytes, stream)
 
 
 def ulys_status_string(status: int) -> str:

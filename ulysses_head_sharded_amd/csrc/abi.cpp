@@ -422,6 +422,56 @@ int ulys_head2seq_push(const void* o, void* const* x_ranks, int32_t rank, int64_
   return e == hipSuccess ? ULYS_OK : ULYS_ERR_HIP;
 }
 
+int ulys_attn_fwd_push(const void* q, const void* k, const void* v, void* const* x_ranks,
+                       int32_t rank, float* lse, int64_t s, int64_t b, int64_t h, int64_t h_kv,
+                       int64_t d_h, int32_t P, int32_t causal, int32_t dtype, void* workspace,
+                       int64_t workspace_bytes, void* stream) {
+  if (!q || !k || !v || !x_ranks) return ULYS_ERR_NULL;
+  int64_t nq = 0, nkv = 0, nl = 0;
+  const int rc = check_attn_shape(s, b, h, h_kv, d_h, P, dtype, &nq, &nkv, &nl);
+  if (rc != ULYS_OK) return rc;
+  if (dtype != ULYS_BF16) return ULYS_ERR_UNSUPPORTED;
+  if (P > ULYS_MAX_RANKS || rank < 0 || rank >= P) return ULYS_ERR_DIM;
+  if (workspace && workspace_bytes < 0) return ULYS_ERR_DIM;
+  for (int32_t r = 0; r < P; ++r)
+    if (!x_ranks[r]) return ULYS_ERR_NULL;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v)) return ULYS_ERR_ALIGNMENT;
+  if ((lse && !aligned16(lse)) || (workspace && !aligned16(workspace))) return ULYS_ERR_ALIGNMENT;
+  for (int32_t r = 0; r < P; ++r)
+    if (!aligned16(x_ranks[r])) return ULYS_ERR_ALIGNMENT;
+  // a destination shard [s/P, b, h, d_h] has the share's bytes; this call
+  // writes head group `rank` of each of its rows: the span from the first
+  // to the last such run
+  const int64_t n = nq;
+  const int64_t run = (h / P) * d_h * 2;
+  const int64_t span = n - (int64_t)(P - 1) * run;
+  const int64_t w = (workspace && workspace_bytes > 0) ? workspace_bytes : 0;
+  if (lse && (overlaps(lse, nl, q, nq) || overlaps(lse, nl, k, nkv) || overlaps(lse, nl, v, nkv)))
+    return ULYS_ERR_ALIAS;
+  if (w && (overlaps(workspace, w, q, nq) || overlaps(workspace, w, k, nkv) ||
+            overlaps(workspace, w, v, nkv) || (lse && overlaps(workspace, w, lse, nl))))
+    return ULYS_ERR_ALIAS;
+  for (int32_t r = 0; r < P; ++r) {
+    const char* lo = static_cast<const char*>(x_ranks[r]) + (int64_t)rank * run;
+    if (overlaps(lo, span, q, nq) || overlaps(lo, span, k, nkv) || overlaps(lo, span, v, nkv) ||
+        (lse && overlaps(lo, span, lse, nl)) || (w && overlaps(lo, span, workspace, w)))
+      return ULYS_ERR_ALIAS;
+    for (int32_t j = 0; j < r; ++j)
+      if (overlaps(lo, span, static_cast<const char*>(x_ranks[j]) + (int64_t)rank * run, span))
+        return ULYS_ERR_ALIAS;
+  }
+  ulys::AttnArgs a = make_args(q, k, v, nullptr, lse, s, b, h, h_kv, d_h, P, causal);
+  if (w) {
+    a.workspace = workspace;
+    a.workspace_bytes = workspace_bytes;
+  }
+  a.o_ranks = x_ranks;
+  a.ranks = P;
+  a.rank = rank;
+  const hipError_t e = ulys::launch_attn_bf16(a, (hipStream_t)stream);
+  return e == hipSuccess ? ULYS_OK : ULYS_ERR_HIP;
+}
+
 int ulys_attn_merge(const void* o_a, const float* lse_a, const void* o_b, const float* lse_b,
                     void* o, float* lse, int64_t s, int64_t b, int64_t hp, int64_t d_h,
                     int32_t dtype, void* stream) {

@@ -58,6 +58,7 @@ constexpr int kWaves = 8;
 constexpr int kThreads = 64 * kWaves;
 constexpr int kBN = 64;  // keys per tile
 constexpr int kQW = 32;  // queries per wave
+constexpr int kMaxPushRanks = 64;  // destinations of the pushing epilogue
 
 template <int D>
 struct Cfg {
@@ -96,6 +97,11 @@ struct Params {
   int q_bytes, kv_bytes;  // tensor sizes in bytes (bounds of the buffer resources)
   float c;     // log2(e) / sqrt(d_h)
   float lazy;  // 8 / c: margin (raw score units) by which a row max may pass m_run
+  // push (o_rank set): row t of the share goes to shard o_rank[t / sl] at
+  // token t % sl, this rank's head columns, instead of to o
+  int push, sl;
+  int push_tok_bytes, push_be_bytes, push_head_off, push_bytes;
+  uint16_t* o_rank[kMaxPushRanks];
 };
 
 // LDS tiles are unpadded, with the 16-byte chunks of row r XOR-swizzled so
@@ -146,13 +152,18 @@ __device__ __forceinline__ Item decode_item(const Params& p, int rank, int wave,
 
 // O = A / l rounded once to bf16, and lse in natural log, for this lane's
 // query (rows past s fall outside the buffer resource and are dropped).
+// With push set, the row goes straight to its place after the head->seq
+// exchange ("02 · DeepSpeed-Ulysses" §2: the output is sent by sequence
+// segment and the receiver concatenates along heads): shard o_rank[j] of the
+// rank that owns segment j = my_q / sl, token my_q % sl, this rank's head
+// columns.  A wave's 32 rows may span several segments; the wave takes them
+// one uniform segment at a time, so every destination pointer is a scalar.
 template <int D>
 __device__ __forceinline__ void store_output(const Params& p, const f32x16* oacc, float m_run,
                                              float l_run, int be, int head, int my_q, int hh) {
   const float l_tot = xsum32(l_run);
   const float inv = 1.f / l_tot;
-  const __amdgpu_buffer_rsrc_t ro = rsrc(p.o, p.q_bytes);
-  const int ooff = my_q * p.q_tok_bytes + (be * p.hp + head) * D * 2 + hh * 8;
+  u32x2 w[D / 32][4];
 #pragma unroll
   for (int db = 0; db < D / 32; ++db)
 #pragma unroll
@@ -161,13 +172,40 @@ __device__ __forceinline__ void store_output(const Params& p, const f32x16* oacc
       const __bf16 x1 = (__bf16)(oacc[db][4 * g4 + 1] * inv);
       const __bf16 x2 = (__bf16)(oacc[db][4 * g4 + 2] * inv);
       const __bf16 x3 = (__bf16)(oacc[db][4 * g4 + 3] * inv);
-      const uint32_t w0 = (uint32_t)__builtin_bit_cast(uint16_t, x0) |
-                          ((uint32_t)__builtin_bit_cast(uint16_t, x1) << 16);
-      const uint32_t w1 = (uint32_t)__builtin_bit_cast(uint16_t, x2) |
-                          ((uint32_t)__builtin_bit_cast(uint16_t, x3) << 16);
-      __builtin_amdgcn_raw_buffer_store_b64(u32x2{w0, w1}, ro, ooff + (db * 32 + 8 * g4) * 2, 0,
-                                            0);
+      w[db][g4] = u32x2{(uint32_t)__builtin_bit_cast(uint16_t, x0) |
+                            ((uint32_t)__builtin_bit_cast(uint16_t, x1) << 16),
+                        (uint32_t)__builtin_bit_cast(uint16_t, x2) |
+                            ((uint32_t)__builtin_bit_cast(uint16_t, x3) << 16)};
     }
+  if (!p.push) {
+    const __amdgpu_buffer_rsrc_t ro = rsrc(p.o, p.q_bytes);
+    const int ooff = my_q * p.q_tok_bytes + (be * p.hp + head) * D * 2 + hh * 8;
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4)
+        __builtin_amdgcn_raw_buffer_store_b64(w[db][g4], ro, ooff + (db * 32 + 8 * g4) * 2, 0,
+                                              0);
+  } else {
+    const int j = (my_q < p.s) ? my_q / p.sl : -1;
+    uint64_t todo = __ballot(j >= 0);
+    while (todo) {
+      const int jj = __builtin_amdgcn_readlane(j, (int)__builtin_ctzll(todo));
+      const bool mine = j == jj;
+      todo &= ~__ballot(mine);
+      if (mine) {
+        const __amdgpu_buffer_rsrc_t rd = rsrc(p.o_rank[jj], p.push_bytes);
+        const int off = (my_q - jj * p.sl) * p.push_tok_bytes + be * p.push_be_bytes +
+                        p.push_head_off + head * D * 2 + hh * 8;
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+          for (int g4 = 0; g4 < 4; ++g4)
+            __builtin_amdgcn_raw_buffer_store_b64(w[db][g4], rd, off + (db * 32 + 8 * g4) * 2, 0,
+                                                  0);
+      }
+    }
+  }
   if (p.lse && hh == 0 && my_q < p.s)
     p.lse[(int64_t)(be * p.hp + head) * p.s + my_q] =
         (m_run * p.c + __builtin_amdgcn_logf(l_tot)) * 0.69314718055994531f;
@@ -612,6 +650,21 @@ hipError_t launch_d(const AttnArgs& a, hipStream_t stream) {
   p.kv_bytes = (int)(a.s * a.b * a.hkvp * D * 2);
   p.c = (float)(1.4426950408889634 / sqrt((double)D));
   p.lazy = 8.f / p.c;
+  p.push = a.o_ranks != nullptr;
+  p.sl = p.push_tok_bytes = p.push_be_bytes = p.push_head_off = p.push_bytes = 0;
+  for (int r = 0; r < kMaxPushRanks; ++r) p.o_rank[r] = nullptr;
+  if (p.push) {
+    if (a.ranks <= 0 || a.ranks > kMaxPushRanks || a.rank < 0 || a.rank >= a.ranks ||
+        a.s % a.ranks != 0)
+      return hipErrorInvalidValue;
+    const int64_t h = a.hp * a.ranks;
+    p.sl = (int)(a.s / a.ranks);
+    p.push_be_bytes = (int)(h * D * 2);
+    p.push_tok_bytes = (int)(a.b * h * D * 2);
+    p.push_head_off = (int)(a.rank * a.hp * D * 2);
+    p.push_bytes = (int)((int64_t)p.sl * p.push_tok_bytes);
+    for (int r = 0; r < a.ranks; ++r) p.o_rank[r] = static_cast<uint16_t*>(a.o_ranks[r]);
+  }
   const int64_t items = (int64_t)p.n_qblk * p.b * p.hkvp * p.nsub;
   if (items <= 0) return hipSuccess;
   if (items > 0x7FFFFFFF) return hipErrorInvalidValue;

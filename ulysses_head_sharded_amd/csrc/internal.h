@@ -81,6 +81,10 @@ struct AttnArgs {
   int causal;
   void* workspace;          // may be null
   int64_t workspace_bytes;
+  // non-null (bf16 only): the output rows are pushed into these `ranks`
+  // shards [s/ranks, b, hp*ranks, d] at head columns of rank `rank`, not to o
+  void* const* o_ranks = nullptr;
+  int ranks = 0, rank = 0;
 };
 
 hipError_t launch_attn_bf16(const AttnArgs& a, hipStream_t stream);
