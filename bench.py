@@ -2,10 +2,14 @@
 
 A step is one pass of the whole path over one rank's share of a layer:
 pack Q, K, V (seq->head send side), head-sharded attention over the whole
-sequence, unpack O (head->seq receive side).  The all-to-all itself is not
-part of a one-GPU step: the rank's own send buffer stands in for its receive
-buffer (same shape, [s, b, h/P, d]), so the attention consumes the pack's
-output and the unpack consumes the attention's output.
+sequence, and the output's head->seq exchange.  The first all-to-all itself
+is not part of a one-GPU step: the rank's own send buffer stands in for its
+receive buffer (same shape, [s, b, h/P, d]), so the attention consumes the
+pack's output.  For bf16 the attention writes its output rows straight into
+the P destination shards (ulys_attn_fwd_push: the O exchange and unpack in
+its epilogue; the destinations are P buffers on this GPU); fp32 runs the
+attention and then the unpack.  The pack and unpack kernels are also timed
+alone, streaming from HBM (layout_hbm).
 
 Prints ONE JSON line.  ``value`` is attention FLOPs per step over the whole
 step time (TFLOP/s); per-kernel durations come from HIP events recorded on
@@ -457,6 +461,11 @@ def main():
             raise RuntimeError(f"{what}: {binding.ulys_status_string(rc)}")
 
     ev = {n: [] for n in ("pack0", "pack1", "attn1", "unpack1")}
+    # bf16: the attention pushes its rows into rank 0's P destination shards
+    fused = w.dtype == "bf16"
+    dst = [torch.empty((sl, w.b, w.h, w.d), dtype=tdt, device=dev) for _ in range(w.P)] \
+        if fused else []
+    dst_ptrs = [t.data_ptr() for t in dst]
 
     def step(record: bool):
         if record:
@@ -469,13 +478,20 @@ def main():
         if record:
             e[1].record(stream)
         # the send buffers stand in for the receive buffers: [P, s/P, b, hp, d] == [s, b, hp, d]
-        call(binding.ulys_attn_fwd_ws(yq.data_ptr(), yk.data_ptr(), yv.data_ptr(), o.data_ptr(),
-                                      None, w.s, w.b, w.h, w.h_kv, w.d, w.P, int(w.causal), code,
-                                      ws.data_ptr(), ws_bytes, sh), "attn")
+        if fused:
+            call(binding.ulys_attn_fwd_push(yq.data_ptr(), yk.data_ptr(), yv.data_ptr(), dst_ptrs,
+                                            0, None, w.s, w.b, w.h, w.h_kv, w.d, w.P,
+                                            int(w.causal), code, ws.data_ptr(), ws_bytes, sh),
+                 "attn push")
+        else:
+            call(binding.ulys_attn_fwd_ws(yq.data_ptr(), yk.data_ptr(), yv.data_ptr(),
+                                          o.data_ptr(), None, w.s, w.b, w.h, w.h_kv, w.d, w.P,
+                                          int(w.causal), code, ws.data_ptr(), ws_bytes, sh), "attn")
         if record:
             e[2].record(stream)
-        call(binding.ulys_unpack_head2seq(o.data_ptr(), xo.data_ptr(), w.s, w.b, w.h, w.d, w.P,
-                                          code, sh), "unpack o")
+        if not fused:
+            call(binding.ulys_unpack_head2seq(o.data_ptr(), xo.data_ptr(), w.s, w.b, w.h, w.d,
+                                              w.P, code, sh), "unpack o")
         if record:
             e[3].record(stream)
             ev["pack0"].append(e[0])
@@ -503,8 +519,18 @@ def main():
     pack_bytes = 2 * w.shard_bytes() + 2 * (w.shard_bytes(kv=True) + w.kv_blocks_bytes())
     unpack_bytes = 2 * w.shard_bytes()
     pack_gbps = pack_bytes / (pack_ms * 1e-3) / 1e9
-    unpack_gbps = unpack_bytes / (unpack_ms * 1e-3) / 1e9
-    layout_gbps = (pack_bytes + unpack_bytes) / ((pack_ms + unpack_ms) * 1e-3) / 1e9
+    if fused:  # the O exchange is inside the attention call
+        layout = {"pack_qkv_us": round(pack_ms * 1e3, 2), "pack_gbps": round(pack_gbps, 1),
+                  "frac_hbm_peak": round(pack_gbps / PEAK_HBM_GBPS, 4), "bytes": pack_bytes,
+                  "o_exchange": "in the attention epilogue (ulys_attn_fwd_push)"}
+    else:
+        unpack_gbps = unpack_bytes / (unpack_ms * 1e-3) / 1e9
+        layout_gbps = (pack_bytes + unpack_bytes) / ((pack_ms + unpack_ms) * 1e-3) / 1e9
+        layout = {"pack_qkv_us": round(pack_ms * 1e3, 2), "unpack_o_us": round(unpack_ms * 1e3, 2),
+                  "pack_gbps": round(pack_gbps, 1), "unpack_gbps": round(unpack_gbps, 1),
+                  "gbps": round(layout_gbps, 1),
+                  "frac_hbm_peak": round(layout_gbps / PEAK_HBM_GBPS, 4),
+                  "bytes": pack_bytes + unpack_bytes}
     kernel_src = os.path.join(ROOT, "ulysses_head_sharded_amd", "csrc",
                               "attn_bf16.hip" if w.dtype == "bf16" else "attn_f32.hip")
 
@@ -527,17 +553,17 @@ def main():
         "attn": {"ms": round(attn_ms, 4), "tflops": round(attn_tflops, 2),
                  "frac_peak": round(attn_tflops / peak, 4), "flops": flops,
                  "workspace_bytes": int(ws_bytes)},
-        "layout": {"pack_qkv_us": round(pack_ms * 1e3, 2), "unpack_o_us": round(unpack_ms * 1e3, 2),
-                   "pack_gbps": round(pack_gbps, 1), "unpack_gbps": round(unpack_gbps, 1),
-                   "gbps": round(layout_gbps, 1),
-                   "frac_hbm_peak": round(layout_gbps / PEAK_HBM_GBPS, 4),
-                   "bytes": pack_bytes + unpack_bytes},
+        "layout": layout,
         "roofline": {"bound": "mfma", "achieved": round(attn_tflops, 2), "peak": peak,
                      "unit": "TFLOP/s", "frac": round(attn_tflops / peak, 4),
                      "traffic": counter_traffic(kernel_src, w.name)},
     }
     if args.layout_calls > 0:
         rec["layout_hbm"] = bench_layout_hbm(args, w, binding, torch, tdt, code, stream)
+    if fused:  # o itself, the merge's input, is filled by a plain call
+        call(binding.ulys_attn_fwd_ws(yq.data_ptr(), yk.data_ptr(), yv.data_ptr(), o.data_ptr(),
+                                      None, w.s, w.b, w.h, w.h_kv, w.d, w.P, int(w.causal), code,
+                                      ws.data_ptr(), ws_bytes, sh), "attn")
     if args.merge_steps > 0:
         rec["merge"] = bench_merge(args, w, binding, torch, np, o, code, stream)
     if args.push_steps > 0:
