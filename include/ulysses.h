@@ -314,6 +314,31 @@ int ulys_attn_fwd_push(const void* q, const void* k, const void* v, void* const*
                        int64_t workspace_bytes, void* stream);
 
 /*
+ * Attention backward with the gradients' head->seq exchange fused into its
+ * epilogues: the result of ulys_attn_bwd followed by ulys_head2seq_push of
+ * dQ (h heads) and of dK, dV (h_kv heads), without the dq, dk, dv tensors
+ * in between.  [ATLAS] §5: the exchanges' backward is the same all-to-all
+ * with its axes swapped, so the gradient of a share goes back by sequence
+ * segment and the receiver concatenates along heads ([ATLAS] §2).
+ *
+ *   q, k, v, o, dout, lse, s, b, h, h_kv, d_h, P, causal, workspace: as
+ *             ulys_attn_bwd
+ *   dq_ranks, dk_ranks, dv_ranks : HOST arrays of P device pointers; rank
+ *             j's shards [s/P, b, h, d_h] (dQ) and [s/P, b, h_kv, d_h] (dK,
+ *             dV); only this rank's head columns are written
+ *   rank    : this rank, 0 <= rank < P <= ULYS_MAX_RANKS
+ * Same values, bit for bit, as the separate calls.  Errors: as
+ * ulys_attn_bwd and ulys_head2seq_push; ULYS_ERR_UNSUPPORTED when the KV
+ * heads would be replicated (h_kv < P: the copies' gradients have to be
+ * summed, which ulys_unpack_head2seq_kv does after the exchange).
+ */
+int ulys_attn_bwd_push(const void* q, const void* k, const void* v, const void* o,
+                       const void* dout, const float* lse, void* const* dq_ranks,
+                       void* const* dk_ranks, void* const* dv_ranks, int32_t rank, int64_t s,
+                       int64_t b, int64_t h, int64_t h_kv, int64_t d_h, int32_t P, int32_t causal,
+                       int32_t dtype, void* workspace, int64_t workspace_bytes, void* stream);
+
+/*
  * Merge of two partial attention results of one share over disjoint key sets.
  * [SPCP] (Ring section): each query row's online-softmax state -- running
  * max, scaled sum, scaled weighted sum of values -- is brought to a common max
@@ -346,7 +371,7 @@ const char* ulys_status_string(int status);
 /* ABI version of this header: (major << 16) | minor. */
 int ulys_abi_version(void);
 
-#define ULYS_ABI_VERSION ((1 << 16) | 7)
+#define ULYS_ABI_VERSION ((1 << 16) | 8)
 
 #ifdef __cplusplus
 }

@@ -36,7 +36,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_version(lib):
-    assert B.ulys_abi_version() == (1 << 16) | 7
+    assert B.ulys_abi_version() == (1 << 16) | 8
 
 
 def test_status_strings(lib):
@@ -341,4 +341,37 @@ def test_attn_push_rejects(lib, kw, expect):
         rc = B.ulys_attn_fwd_push(a["q"], a["k"], a["v"], a["dst"], a["rank"], a["lse"], a["s"],
                                   a["b"], a["h"], a["h_kv"], a["d"], a["P"], a["causal"],
                                   a["dtype"], a["ws"], a["wsb"])
+    assert rc == expect
+
+
+# ------------------------------------------------ attention backward with pushing epilogues
+BQ, BK, BV, BO, BG = (0x7F0000000000 + (70 + i) * (1 << 32) for i in range(5))
+BL, BW = 0x7F0000000000 + 76 * (1 << 32), 0x7F0000000000 + 77 * (1 << 32)
+BDQ = [0x7F0000000000 + (80 + r) * (1 << 32) for r in range(4)]
+BDK = [0x7F0000000000 + (90 + r) * (1 << 32) for r in range(4)]
+BDV = [0x7F0000000000 + (100 + r) * (1 << 32) for r in range(4)]
+
+
+@pytest.mark.parametrize("kw,expect", [
+    (dict(q=None), B.ULYS_ERR_NULL),
+    (dict(ws=None), B.ULYS_ERR_NULL),
+    (dict(dk=[BDK[0], None, BDK[2], BDK[3]]), B.ULYS_ERR_NULL),
+    (dict(wsb=16), B.ULYS_ERR_DIM),                 # smaller than the workspace it needs
+    (dict(rank=4), B.ULYS_ERR_DIM),
+    (dict(s=18), B.ULYS_ERR_DIVISIBILITY),
+    (dict(h_kv=2), B.ULYS_ERR_UNSUPPORTED),         # replicated KV heads
+    (dict(dtype=B.ULYS_F32), B.ULYS_ERR_UNSUPPORTED),
+    (dict(dv=[BDV[0], BDV[1] + 8, BDV[2], BDV[3]]), B.ULYS_ERR_ALIGNMENT),
+    (dict(dq=[BDQ[0], BDQ[1], BDK[2], BDQ[3]]), B.ULYS_ERR_ALIAS),   # a dQ shard over a dK one
+    (dict(dv=[BDV[0], BDV[0], BDV[2], BDV[3]]), B.ULYS_ERR_ALIAS),   # two ranks, one buffer
+    (dict(dq=[BO, BDQ[1], BDQ[2], BDQ[3]]), B.ULYS_ERR_ALIAS),       # over o
+    (dict(dk=[BDK[0], BDK[1], BW, BDK[3]]), B.ULYS_ERR_ALIAS),       # over the workspace
+])
+def test_attn_bwd_push_rejects(lib, kw, expect):
+    a = dict(q=BQ, k=BK, v=BV, o=BO, g=BG, lse=BL, dq=BDQ, dk=BDK, dv=BDV, rank=1, s=64, b=1,
+             h=8, h_kv=4, d=128, P=4, causal=1, dtype=B.ULYS_BF16, ws=BW, wsb=1 << 24)
+    a.update(kw)
+    rc = B.ulys_attn_bwd_push(a["q"], a["k"], a["v"], a["o"], a["g"], a["lse"], a["dq"], a["dk"],
+                              a["dv"], a["rank"], a["s"], a["b"], a["h"], a["h_kv"], a["d"],
+                              a["P"], a["causal"], a["dtype"], a["ws"], a["wsb"])
     assert rc == expect

@@ -158,3 +158,49 @@ def test_attn_push_equals_attn_then_push(s, b, h, h_kv, d, P, rank, causal, ws):
         assert torch.equal(got[j].raw, ref[j].raw), j
     assert lse.guards_intact()
     assert torch.equal(lse.tensor, lse_ref)
+
+
+# (s, b, h, h_kv, P, rank, causal), d = 128: segments of 64, 25 and 125 rows,
+# GQA, and the 32K share, whose backward splits both its dQ and dK/dV items
+BWD_PUSH = [(256, 1, 8, 4, 4, 1, True), (100, 2, 8, 8, 4, 3, False),
+            (1000, 1, 16, 8, 8, 0, True), (32768, 1, 16, 16, 8, 6, True)]
+
+
+@pytest.mark.parametrize("s,b,h,h_kv,P,rank,causal", BWD_PUSH)
+def test_attn_bwd_push_equals_bwd_then_push(s, b, h, h_kv, P, rank, causal):
+    """ulys_attn_bwd_push writes, bit for bit, what ulys_attn_bwd followed by
+    ulys_head2seq_push of dQ, dK and dV writes (the rest of every destination
+    shard, and its guard bands, untouched)."""
+    print(f"case attn_bwd_push s={s} b={b} h={h} h_kv={h_kv} P={P} rank={rank} causal={causal}",
+          flush=True)
+    d, sl, hp, hkvp = 128, s // P, h // P, h_kv // P
+    from gpu_util import share_inputs
+    q, k, v = share_inputs(60 + P, s, b, hp, hkvp, d, "bf16")
+    g = synth.tensor(6000 + s, (s, b, hp, d), "bf16")
+    qd, kd, vd, gd = to_dev(q), to_dev(k), to_dev(v), to_dev(g)
+    o, lse = binding.attn_fwd(qd, kd, vd, P=P, causal=causal, lse=True)
+    dq, dk, dv = binding.attn_bwd(qd, kd, vd, o, gd, lse, P=P, causal=causal)
+    code = binding.ULYS_BF16
+    ref = {}
+    for name, t, heads in (("dq", dq, h), ("dk", dk, h_kv), ("dv", dv, h_kv)):
+        ref[name] = [Guarded((sl, b, heads, d), torch.bfloat16) for _ in range(P)]
+        rc = binding.ulys_head2seq_push(t.data_ptr(), [x.tensor.data_ptr() for x in ref[name]],
+                                        rank, s, b, heads, d, P, code, stream())
+        assert rc == 0, binding.ulys_status_string(rc)
+    got = {"dq": [Guarded((sl, b, h, d), torch.bfloat16) for _ in range(P)],
+           "dk": [Guarded((sl, b, h_kv, d), torch.bfloat16) for _ in range(P)],
+           "dv": [Guarded((sl, b, h_kv, d), torch.bfloat16) for _ in range(P)]}
+    nbytes = binding.ulys_attn_bwd_workspace_size(s, b, h, h_kv, d, P, int(causal), code)
+    assert nbytes > 0
+    ws = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    rc = binding.ulys_attn_bwd_push(qd.data_ptr(), kd.data_ptr(), vd.data_ptr(), o.data_ptr(),
+                                    gd.data_ptr(), lse.data_ptr(),
+                                    *[[x.tensor.data_ptr() for x in got[n]]
+                                      for n in ("dq", "dk", "dv")],
+                                    rank, s, b, h, h_kv, d, P, int(causal), code, ws.data_ptr(),
+                                    nbytes, stream())
+    assert rc == 0, binding.ulys_status_string(rc)
+    torch.cuda.synchronize()
+    for name in ("dq", "dk", "dv"):
+        for j in range(P):
+            assert torch.equal(got[name][j].raw, ref[name][j].raw), (name, j)

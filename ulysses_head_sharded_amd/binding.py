@@ -24,6 +24,7 @@ EXPORTED = ("ulys_pack_seq2head", "ulys_unpack_head2seq", "ulys_pack_seq2head_kv
             "ulys_unpack_head2seq_kv", "ulys_pack_seq2head_qkv", "ulys_attn_fwd", "ulys_attn_fwd_ws",
             "ulys_attn_fwd_workspace_size", "ulys_attn_bwd", "ulys_attn_bwd_workspace_size",
             "ulys_attn_merge", "ulys_seq2head_push", "ulys_head2seq_push", "ulys_attn_fwd_push",
+            "ulys_attn_bwd_push",
             "ulys_status_string", "ulys_abi_version")
 
 _lib = None
@@ -75,6 +76,10 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.ulys_attn_fwd_push.argtypes = [vp, vp, vp, ctypes.POINTER(vp), i32, vp] + [i64] * 5 + \
         [i32, i32, i32, vp, i64, vp]
     lib.ulys_attn_fwd_push.restype = ctypes.c_int
+    pp = ctypes.POINTER(vp)
+    lib.ulys_attn_bwd_push.argtypes = [vp] * 6 + [pp, pp, pp, i32] + [i64] * 5 + \
+        [i32, i32, i32, vp, i64, vp]
+    lib.ulys_attn_bwd_push.restype = ctypes.c_int
     lib.ulys_attn_merge.argtypes = [vp] * 6 + [i64] * 4 + [i32, vp]
     lib.ulys_attn_merge.restype = ctypes.c_int
     lib.ulys_status_string.argtypes = [ctypes.c_int]
@@ -156,6 +161,15 @@ def ulys_attn_fwd_push(q, k, v, x_ranks, rank, lse, s, b, h, h_kv, d_h, P, causa
     """x_ranks: sequence of P device addresses (ints)."""
     return load().ulys_attn_fwd_push(q, k, v, _ptr_table(x_ranks), rank, lse, s, b, h, h_kv, d_h,
                                      P, causal, dtype, workspace, workspace_bytes, stream)
+
+
+def ulys_attn_bwd_push(q, k, v, o, dout, lse, dq_ranks, dk_ranks, dv_ranks, rank, s, b, h, h_kv,
+                       d_h, P, causal, dtype, workspace, workspace_bytes, stream=None) -> int:
+    """dq_ranks, dk_ranks, dv_ranks: sequences of P device addresses (ints)."""
+    return load().ulys_attn_bwd_push(q, k, v, o, dout, lse, _ptr_table(dq_ranks),
+                                     _ptr_table(dk_ranks), _ptr_table(dv_ranks), rank, s, b, h,
+                                     h_kv, d_h, P, causal, dtype, workspace, workspace_bytes,
+                                     stream)
 
 
 def ulys_status_string(status: int) -> str:

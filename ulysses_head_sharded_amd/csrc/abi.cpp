@@ -263,6 +263,80 @@ int ulys_attn_bwd(const void* q, const void* k, const void* v, const void* o, co
   return e == hipSuccess ? ULYS_OK : ULYS_ERR_HIP;
 }
 
+int ulys_attn_bwd_push(const void* q, const void* k, const void* v, const void* o,
+                       const void* dout, const float* lse, void* const* dq_ranks,
+                       void* const* dk_ranks, void* const* dv_ranks, int32_t rank, int64_t s,
+                       int64_t b, int64_t h, int64_t h_kv, int64_t d_h, int32_t P, int32_t causal,
+                       int32_t dtype, void* workspace, int64_t workspace_bytes, void* stream) {
+  if (!q || !k || !v || !o || !dout || !lse || !dq_ranks || !dk_ranks || !dv_ranks ||
+      !workspace)
+    return ULYS_ERR_NULL;
+  const int64_t need = ulys_attn_bwd_workspace_size(s, b, h, h_kv, d_h, P, causal, dtype);
+  if (need < 0) return (int)need;
+  if (workspace_bytes < need) return ULYS_ERR_DIM;
+  int64_t nq = 0, nkv = 0, nl = 0;
+  const int rc = check_attn_shape(s, b, h, h_kv, d_h, P, dtype, &nq, &nkv, &nl);
+  if (rc != ULYS_OK) return rc;
+  // replicated KV heads: the copies' gradients must be summed across ranks
+  if (h_kv % P != 0) return ULYS_ERR_UNSUPPORTED;
+  if (P > ULYS_MAX_RANKS || rank < 0 || rank >= P) return ULYS_ERR_DIM;
+  void* const* tables[] = {dq_ranks, dk_ranks, dv_ranks};
+  for (void* const* t : tables)
+    for (int32_t r = 0; r < P; ++r) {
+      if (!t[r]) return ULYS_ERR_NULL;
+      if (!aligned16(t[r])) return ULYS_ERR_ALIGNMENT;
+    }
+  const void* ins[] = {q, k, v, o, dout, lse, workspace};
+  const int64_t in_bytes[] = {nq, nkv, nkv, nq, nq, nl, need};
+  for (const void* p : ins)
+    if (!aligned16(p)) return ULYS_ERR_ALIGNMENT;
+  if (overlaps(workspace, need, q, nq) || overlaps(workspace, need, k, nkv) ||
+      overlaps(workspace, need, v, nkv) || overlaps(workspace, need, o, nq) ||
+      overlaps(workspace, need, dout, nq) || overlaps(workspace, need, lse, nl))
+    return ULYS_ERR_ALIAS;
+  // written span of each destination: head group `rank` of every row of a
+  // shard of the share's bytes (dQ: nq; dK, dV: nkv)
+  const int64_t run_q = (h / P) * d_h * 2, run_kv = (h_kv / P) * d_h * 2;
+  const int64_t span[] = {nq - (int64_t)(P - 1) * run_q, nkv - (int64_t)(P - 1) * run_kv,
+                          nkv - (int64_t)(P - 1) * run_kv};
+  const int64_t run[] = {run_q, run_kv, run_kv};
+  for (int t = 0; t < 3; ++t)
+    for (int32_t r = 0; r < P; ++r) {
+      const char* lo = static_cast<const char*>(tables[t][r]) + (int64_t)rank * run[t];
+      for (int i = 0; i < 7; ++i)
+        if (overlaps(lo, span[t], ins[i], in_bytes[i])) return ULYS_ERR_ALIAS;
+      for (int t2 = 0; t2 <= t; ++t2)
+        for (int32_t r2 = 0; r2 < (t2 == t ? r : P); ++r2)
+          if (overlaps(lo, span[t],
+                       static_cast<const char*>(tables[t2][r2]) + (int64_t)rank * run[t2],
+                       span[t2]))
+            return ULYS_ERR_ALIAS;
+    }
+  ulys::AttnBwdArgs a;
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.o = o;
+  a.dout = dout;
+  a.lse = lse;
+  a.dq = a.dk = a.dv = nullptr;
+  a.s = s;
+  a.b = b;
+  a.hp = h / P;
+  a.hkvp = h_kv / P;
+  a.d = d_h;
+  a.causal = causal != 0;
+  a.workspace = workspace;
+  a.workspace_bytes = workspace_bytes;
+  a.dq_ranks = dq_ranks;
+  a.dk_ranks = dk_ranks;
+  a.dv_ranks = dv_ranks;
+  a.ranks = P;
+  a.rank = rank;
+  const hipError_t e = ulys::launch_attn_bwd_bf16(a, (hipStream_t)stream);
+  return e == hipSuccess ? ULYS_OK : ULYS_ERR_HIP;
+}
+
 // Shared validation of the two KV layout entry points; *rep is set when the
 // heads are replicated (h_kv < P), else the plain layout applies.
 static int check_layout_kv(const void* in, const void* out, int64_t s, int64_t b, int64_t h_kv,

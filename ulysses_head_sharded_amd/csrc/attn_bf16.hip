@@ -158,7 +158,9 @@ __device__ __forceinline__ Item decode_item(const Params& p, int rank, int wave,
 // rank that owns segment j = my_q / sl, token my_q % sl, this rank's head
 // columns.  A wave's 32 rows may span several segments; the wave takes them
 // one uniform segment at a time, so every destination pointer is a scalar.
-template <int D>
+// PUSH is a separate instantiation of the kernels, so the plain ones compile
+// as if the pushing epilogue did not exist.
+template <int D, bool PUSH>
 __device__ __forceinline__ void store_output(const Params& p, const f32x16* oacc, float m_run,
                                              float l_run, int be, int head, int my_q, int hh) {
   const float l_tot = xsum32(l_run);
@@ -177,7 +179,7 @@ __device__ __forceinline__ void store_output(const Params& p, const f32x16* oacc
                         (uint32_t)__builtin_bit_cast(uint16_t, x2) |
                             ((uint32_t)__builtin_bit_cast(uint16_t, x3) << 16)};
     }
-  if (!p.push) {
+  if constexpr (!PUSH) {
     const __amdgpu_buffer_rsrc_t ro = rsrc(p.o, p.q_bytes);
     const int ooff = my_q * p.q_tok_bytes + (be * p.hp + head) * D * 2 + hh * 8;
 #pragma unroll
@@ -211,7 +213,7 @@ __device__ __forceinline__ void store_output(const Params& p, const f32x16* oacc
         (m_run * p.c + __builtin_amdgcn_logf(l_tot)) * 0.69314718055994531f;
 }
 
-template <int D, bool CAUSAL>
+template <int D, bool CAUSAL, bool PUSH>
 __global__ __launch_bounds__(kThreads, 1) void attn_bf16_kernel(Params p) {
   using C = Cfg<D>;
   __shared__ __attribute__((aligned(16))) uint8_t lds[C::LDS_BYTES];
@@ -569,7 +571,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bf16_kernel(Params p) {
     part[(D / 2 + 1) * 64] = l_run;
     return;
   }
-  store_output<D>(p, oacc, m_run, l_run, be, head, my_q, hh);
+  store_output<D, PUSH>(p, oacc, m_run, l_run, be, head, my_q, hh);
 }
 
 // Workgroups of this kernel resident at once on the current device: one per
@@ -602,7 +604,7 @@ int64_t attn_bf16_workspace_bytes(const AttnArgs& a) {
 
 // Merge of the two halves of every item: the same rescaling as the online
 // softmax, applied once to two partial states over disjoint key ranges.
-template <int D, bool CAUSAL>
+template <int D, bool CAUSAL, bool PUSH>
 __global__ __launch_bounds__(kThreads) void attn_merge_kernel(Params p) {
   using C = Cfg<D>;
   const int tid = threadIdx.x;
@@ -624,7 +626,17 @@ __global__ __launch_bounds__(kThreads) void attn_merge_kernel(Params p) {
 #pragma unroll
     for (int r = 0; r < 16; ++r)
       oacc[db][r] = p0[(db * 16 + r) * 64] * a0 + p1[(db * 16 + r) * 64] * a1;
-  store_output<D>(p, oacc, m, l, item.be, item.head, item.q0 + l32, hh);
+  store_output<D, PUSH>(p, oacc, m, l, item.be, item.head, item.q0 + l32, hh);
+}
+
+template <int D, bool CAUSAL, bool PUSH>
+void launch_kernels(const Params& p, unsigned units, unsigned items, int nsplit,
+                    hipStream_t stream) {
+  hipLaunchKernelGGL((attn_bf16_kernel<D, CAUSAL, PUSH>), dim3(units), dim3(kThreads), 0, stream,
+                     p);
+  if (nsplit == 2)
+    hipLaunchKernelGGL((attn_merge_kernel<D, CAUSAL, PUSH>), dim3(items), dim3(kThreads), 0,
+                       stream, p);
 }
 
 template <int D>
@@ -673,20 +685,15 @@ hipError_t launch_d(const AttnArgs& a, hipStream_t stream) {
   const int nsplit = (ws_need > 0 && a.workspace && a.workspace_bytes >= ws_need) ? 2 : 1;
   p.nsplit = nsplit;
   p.ws = nsplit == 2 ? (float*)a.workspace : nullptr;
-  if (a.causal)
-    hipLaunchKernelGGL((attn_bf16_kernel<D, true>), dim3((unsigned)(items * nsplit)),
-                       dim3(kThreads), 0, stream, p);
+  const unsigned units = (unsigned)(items * nsplit);
+  if (a.causal && p.push)
+    launch_kernels<D, true, true>(p, units, (unsigned)items, nsplit, stream);
+  else if (a.causal)
+    launch_kernels<D, true, false>(p, units, (unsigned)items, nsplit, stream);
+  else if (p.push)
+    launch_kernels<D, false, true>(p, units, (unsigned)items, nsplit, stream);
   else
-    hipLaunchKernelGGL((attn_bf16_kernel<D, false>), dim3((unsigned)(items * nsplit)),
-                       dim3(kThreads), 0, stream, p);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess || nsplit == 1) return e;
-  if (a.causal)
-    hipLaunchKernelGGL((attn_merge_kernel<D, true>), dim3((unsigned)items), dim3(kThreads), 0,
-                       stream, p);
-  else
-    hipLaunchKernelGGL((attn_merge_kernel<D, false>), dim3((unsigned)items), dim3(kThreads), 0,
-                       stream, p);
+    launch_kernels<D, false, false>(p, units, (unsigned)items, nsplit, stream);
   return hipGetLastError();
 }
 

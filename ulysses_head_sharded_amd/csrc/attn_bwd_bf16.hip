@@ -54,6 +54,7 @@ constexpr int ROW = D * 2;           // bytes of one bf16 row
 constexpr int CHUNKS = ROW / 16;     // 16-byte chunks per row
 constexpr int kWaves = 8;
 constexpr int kThreads = 64 * kWaves;
+constexpr int kMaxPushRanks = 64;  // destinations of the pushing epilogues
 
 __device__ __forceinline__ int dswz(int r) {
   const int i = r & 3;
@@ -114,6 +115,14 @@ struct BwdParams {
   int kv_split;  // 1: every dkv item runs as two halves of its query steps
   int kv_units;  // dkv work units: items << kv_split
   int kv_xcd;    // 1: dkv units dispatched in the XCD-aware order (see xcd_unit)
+  // push (non-zero): the gradient rows go to the shards of the head->seq
+  // exchange instead of to dq, dk, dv (see store_t_push)
+  int push, sl;
+  int q_ptok, q_pbe, q_phead, q_pbytes;      // dQ shards [s/P, b, h, d]
+  int kv_ptok, kv_pbe, kv_phead, kv_pbytes;  // dK, dV shards [s/P, b, h_kv, d]
+  uint16_t* dq_rank[kMaxPushRanks];
+  uint16_t* dk_rank[kMaxPushRanks];
+  uint16_t* dv_rank[kMaxPushRanks];
 };
 
 // XCD-aware order of the dkv units.  The dispatcher sends workgroup b to XCD
@@ -151,6 +160,72 @@ __device__ __forceinline__ void store_t(__amdgpu_buffer_rsrc_t r, const f32x16* 
       __builtin_amdgcn_raw_buffer_store_b64(u32x2{w0, w1}, r, off + (db * 32 + 8 * g4) * 2, 0,
                                             0);
     }
+}
+
+// store_t's rows pushed to their place after the head->seq exchange
+// ("02 · DeepSpeed-Ulysses" §2, §5: the gradients go back by sequence
+// segment and the receiver concatenates along heads): row `row` of the share
+// goes to shard table[row / sl] at token row % sl, `col_off` bytes into the
+// token (batch, this rank's head columns, the head).  A wave's 32 rows may
+// span several segments; it takes them one uniform segment at a time, so
+// every destination pointer is a scalar load.
+__device__ __forceinline__ void store_t_push(uint16_t* const* table, int dst_bytes,
+                                             const f32x16* acc, float scale, int row, int s,
+                                             int sl, int tok_bytes, int col_off, int hh) {
+  u32x2 w[D / 32][4];
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+    for (int g4 = 0; g4 < 4; ++g4) {
+      const __bf16 x0 = (__bf16)(acc[db][4 * g4 + 0] * scale);
+      const __bf16 x1 = (__bf16)(acc[db][4 * g4 + 1] * scale);
+      const __bf16 x2 = (__bf16)(acc[db][4 * g4 + 2] * scale);
+      const __bf16 x3 = (__bf16)(acc[db][4 * g4 + 3] * scale);
+      w[db][g4] = u32x2{(uint32_t)__builtin_bit_cast(uint16_t, x0) |
+                            ((uint32_t)__builtin_bit_cast(uint16_t, x1) << 16),
+                        (uint32_t)__builtin_bit_cast(uint16_t, x2) |
+                            ((uint32_t)__builtin_bit_cast(uint16_t, x3) << 16)};
+    }
+  const int j = (row < s) ? row / sl : -1;
+  uint64_t todo = __ballot(j >= 0);
+  while (todo) {
+    const int jj = __builtin_amdgcn_readlane(j, (int)__builtin_ctzll(todo));
+    const bool mine = j == jj;
+    todo &= ~__ballot(mine);
+    if (mine) {
+      const __amdgpu_buffer_rsrc_t r = rsrc(table[jj], dst_bytes);
+      const int off = (row - jj * sl) * tok_bytes + col_off + hh * 8;
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+        for (int g4 = 0; g4 < 4; ++g4)
+          __builtin_amdgcn_raw_buffer_store_b64(w[db][g4], r, off + (db * 32 + 8 * g4) * 2, 0, 0);
+    }
+  }
+}
+// The three outputs' stores: to dq / dk / dv, or pushed (PUSH, a separate
+// instantiation of every kernel, so the plain kernels compile as if the
+// pushing epilogue did not exist)
+template <bool PUSH>
+__device__ __forceinline__ void store_dq(const BwdParams& p, const f32x16* acc, int row, int be,
+                                         int head, int hh) {
+  if constexpr (PUSH)
+    store_t_push(p.dq_rank, p.q_pbytes, acc, p.inv_sd, row, p.s, p.sl, p.q_ptok,
+                 be * p.q_pbe + p.q_phead + head * ROW, hh);
+  else
+    store_t(rsrc(p.dq, p.q_bytes), acc, p.inv_sd, row, p.q_tok_bytes, (be * p.hp + head) * ROW,
+            hh);
+}
+template <bool PUSH>
+__device__ __forceinline__ void store_dkv(const BwdParams& p, const f32x16* acc, bool is_dk,
+                                          int row, int be, int kvg, int hh) {
+  const float scale = is_dk ? p.inv_sd : 1.f;
+  if constexpr (PUSH)
+    store_t_push(is_dk ? p.dk_rank : p.dv_rank, p.kv_pbytes, acc, scale, row, p.s, p.sl,
+                 p.kv_ptok, be * p.kv_pbe + p.kv_phead + kvg * ROW, hh);
+  else
+    store_t(rsrc(is_dk ? p.dk : p.dv, p.kv_bytes), acc, scale, row, p.kv_tok_bytes,
+            (be * p.hkvp + kvg) * ROW, hh);
 }
 
 // Partial sums of a split unit: n accumulator blocks per lane, stored lane
@@ -235,7 +310,7 @@ __device__ __forceinline__ QItem decode_q_item(const BwdParams& p, int rank, int
   return it;
 }
 
-template <bool CAUSAL>
+template <bool CAUSAL, bool PUSH>
 __global__ __launch_bounds__(kThreads, 1) void bwd_dq_kernel(BwdParams p) {
   // LDS: K0 K1 V0 V1
   __shared__ __attribute__((aligned(16))) uint8_t lds[4 * kTile];
@@ -382,11 +457,11 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dq_kernel(BwdParams p) {
     store_part<D / 32>(p.part + (int64_t)blockIdx.x * kDqPart, acc, wave, lane);
     return;
   }
-  store_t(rsrc(p.dq, p.q_bytes), acc, p.inv_sd, my_q, p.q_tok_bytes, q_head_off, hh);
+  store_dq<PUSH>(p, acc, my_q, it.be, it.head, hh);
 }
 
 // The two halves of every dq item: added in a fixed order, scaled, rounded.
-template <bool CAUSAL>
+template <bool CAUSAL, bool PUSH>
 __global__ __launch_bounds__(kThreads) void bwd_dq_merge_kernel(BwdParams p) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int l32 = lane & 31, hh = lane >> 5;
@@ -394,8 +469,7 @@ __global__ __launch_bounds__(kThreads) void bwd_dq_merge_kernel(BwdParams p) {
   const float* u0 = p.part + (int64_t)(2 * blockIdx.x) * kDqPart;
   f32x16 acc[D / 32];
   add_parts<D / 32>(u0, u0 + kDqPart, acc, wave, lane);
-  store_t(rsrc(p.dq, p.q_bytes), acc, p.inv_sd, it.q0 + l32, p.q_tok_bytes,
-          (it.be * p.hp + it.head) * ROW, hh);
+  store_dq<PUSH>(p, acc, it.q0 + l32, it.be, it.head, hh);
 }
 
 // ------------------------------------------------------------------ dk, dv
@@ -422,7 +496,7 @@ __device__ __forceinline__ KItem decode_k_item(const BwdParams& p, int rank) {
   return it;
 }
 
-template <bool CAUSAL>
+template <bool CAUSAL, bool PUSH>
 __global__ __launch_bounds__(kThreads, 1) void bwd_dkv_kernel(BwdParams p) {
   // LDS: Q0 Q1 | dout0 dout1 | V block | stats0 stats1.  The tiles first:
   // with the buffer and half indices compile-time constants, every tile read
@@ -612,24 +686,24 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkv_kernel(BwdParams p) {
     store_part<D / 32>(base + kDkvPart / 2, dva, wave, lane);
     return;
   }
-  store_t(rsrc(p.dk, p.kv_bytes), dka, p.inv_sd, my_key, p.kv_tok_bytes, kv_head_off, hh);
-  store_t(rsrc(p.dv, p.kv_bytes), dva, 1.f, my_key, p.kv_tok_bytes, kv_head_off, hh);
+  store_dkv<PUSH>(p, dka, true, my_key, it.be, it.kvg, hh);
+  store_dkv<PUSH>(p, dva, false, my_key, it.be, it.kvg, hh);
 }
 
 // The two halves of every dkv item: added in a fixed order, scaled, rounded.
+template <bool PUSH>
 __global__ __launch_bounds__(kThreads) void bwd_dkv_merge_kernel(BwdParams p) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int l32 = lane & 31, hh = lane >> 5;
   const KItem it = decode_k_item(p, blockIdx.x);
   const int my_key = it.kblk * kKB + wave * 32 + l32;
-  const int kv_head_off = (it.be * p.hkvp + it.kvg) * ROW;
   const float* u0 = p.part + (int64_t)(2 * blockIdx.x) * kDkvPart;
   const float* u1 = u0 + kDkvPart;
   f32x16 acc[D / 32];
   add_parts<D / 32>(u0, u1, acc, wave, lane);
-  store_t(rsrc(p.dk, p.kv_bytes), acc, p.inv_sd, my_key, p.kv_tok_bytes, kv_head_off, hh);
+  store_dkv<PUSH>(p, acc, true, my_key, it.be, it.kvg, hh);
   add_parts<D / 32>(u0 + kDkvPart / 2, u1 + kDkvPart / 2, acc, wave, lane);
-  store_t(rsrc(p.dv, p.kv_bytes), acc, 1.f, my_key, p.kv_tok_bytes, kv_head_off, hh);
+  store_dkv<PUSH>(p, acc, false, my_key, it.be, it.kvg, hh);
 }
 
 // Work layout for one call: statistics, split decisions, partial-sum bytes.
@@ -682,6 +756,19 @@ int64_t attn_bwd_bf16_workspace_size(const AttnBwdArgs& a) {
   return pl.part_bytes > 0 ? pl.part_offset + pl.part_bytes : 2 * pl.stat_floats * 4;
 }
 
+template <bool CAUSAL, bool PUSH>
+void launch_kernels(const BwdParams& p, const BwdPlan& pl, unsigned q_grid, unsigned k_grid,
+                    hipStream_t stream) {
+  hipLaunchKernelGGL((bwd_dq_kernel<CAUSAL, PUSH>), dim3(q_grid), dim3(kThreads), 0, stream, p);
+  if (pl.q_split)
+    hipLaunchKernelGGL((bwd_dq_merge_kernel<CAUSAL, PUSH>), dim3((unsigned)pl.q_items),
+                       dim3(kThreads), 0, stream, p);
+  hipLaunchKernelGGL((bwd_dkv_kernel<CAUSAL, PUSH>), dim3(k_grid), dim3(kThreads), 0, stream, p);
+  if (pl.kv_split)
+    hipLaunchKernelGGL((bwd_dkv_merge_kernel<PUSH>), dim3((unsigned)pl.k_items), dim3(kThreads), 0,
+                       stream, p);
+}
+
 hipError_t launch_attn_bwd_bf16(const AttnBwdArgs& a, hipStream_t stream) {
   if (a.d != D) return hipErrorInvalidValue;
   const BwdPlan pl = plan(a);
@@ -723,6 +810,30 @@ hipError_t launch_attn_bwd_bf16(const AttnBwdArgs& a, hipStream_t stream) {
   p.stat_bytes = (int)(pl.stat_floats * 4);
   p.c = (float)(1.4426950408889634 / sqrt((double)D));
   p.inv_sd = (float)(1.0 / sqrt((double)D));
+  p.push = a.dq_ranks != nullptr;
+  p.sl = p.q_ptok = p.q_pbe = p.q_phead = p.q_pbytes = 0;
+  p.kv_ptok = p.kv_pbe = p.kv_phead = p.kv_pbytes = 0;
+  for (int r = 0; r < kMaxPushRanks; ++r) p.dq_rank[r] = p.dk_rank[r] = p.dv_rank[r] = nullptr;
+  if (p.push) {
+    if (!a.dk_ranks || !a.dv_ranks || a.ranks <= 0 || a.ranks > kMaxPushRanks || a.rank < 0 ||
+        a.rank >= a.ranks || a.s % a.ranks != 0)
+      return hipErrorInvalidValue;
+    const int64_t h = a.hp * a.ranks, h_kv = a.hkvp * a.ranks;
+    p.sl = (int)(a.s / a.ranks);
+    p.q_pbe = (int)(h * ROW);
+    p.q_ptok = (int)(a.b * h * ROW);
+    p.q_phead = (int)(a.rank * a.hp * ROW);
+    p.q_pbytes = (int)((int64_t)p.sl * p.q_ptok);
+    p.kv_pbe = (int)(h_kv * ROW);
+    p.kv_ptok = (int)(a.b * h_kv * ROW);
+    p.kv_phead = (int)(a.rank * a.hkvp * ROW);
+    p.kv_pbytes = (int)((int64_t)p.sl * p.kv_ptok);
+    for (int r = 0; r < a.ranks; ++r) {
+      p.dq_rank[r] = static_cast<uint16_t*>(a.dq_ranks[r]);
+      p.dk_rank[r] = static_cast<uint16_t*>(a.dk_ranks[r]);
+      p.dv_rank[r] = static_cast<uint16_t*>(a.dv_ranks[r]);
+    }
+  }
   p.QH = pl.QH;
   p.QB = pl.QB;
   p.n_qblk = pl.n_qblk;
@@ -734,19 +845,14 @@ hipError_t launch_attn_bwd_bf16(const AttnBwdArgs& a, hipStream_t stream) {
   p.kv_xcd = (a.causal && p.kv_units % 16 == 0) ? 1 : 0;
   const unsigned q_grid = (unsigned)(pl.q_items << pl.q_split);
   const unsigned k_grid = (unsigned)(pl.k_items << pl.kv_split);
-  if (a.causal) {
-    hipLaunchKernelGGL(bwd_dq_kernel<true>, dim3(q_grid), dim3(kThreads), 0, stream, p);
-    if (pl.q_split)
-      hipLaunchKernelGGL(bwd_dq_merge_kernel<true>, dim3((unsigned)pl.q_items), dim3(kThreads), 0,
-                         stream, p);
-    hipLaunchKernelGGL(bwd_dkv_kernel<true>, dim3(k_grid), dim3(kThreads), 0, stream, p);
-  } else {
-    hipLaunchKernelGGL(bwd_dq_kernel<false>, dim3(q_grid), dim3(kThreads), 0, stream, p);
-    hipLaunchKernelGGL(bwd_dkv_kernel<false>, dim3(k_grid), dim3(kThreads), 0, stream, p);
-  }
-  if (pl.kv_split)
-    hipLaunchKernelGGL(bwd_dkv_merge_kernel, dim3((unsigned)pl.k_items), dim3(kThreads), 0, stream,
-                       p);
+  if (a.causal && p.push)
+    launch_kernels<true, true>(p, pl, q_grid, k_grid, stream);
+  else if (a.causal)
+    launch_kernels<true, false>(p, pl, q_grid, k_grid, stream);
+  else if (p.push)
+    launch_kernels<false, true>(p, pl, q_grid, k_grid, stream);
+  else
+    launch_kernels<false, false>(p, pl, q_grid, k_grid, stream);
   return hipGetLastError();
 }
 

@@ -106,6 +106,13 @@ struct AttnBwdArgs {
   int causal;
   void* workspace;
   int64_t workspace_bytes;
+  // non-null: dQ, dK, dV rows are pushed into these `ranks` shards each
+  // ([s/ranks, b, heads*ranks, d], head columns of rank `rank`), not stored
+  // to dq, dk, dv (the KV heads must not be replicated)
+  void* const* dq_ranks = nullptr;
+  void* const* dk_ranks = nullptr;
+  void* const* dv_ranks = nullptr;
+  int ranks = 0, rank = 0;
 };
 
 hipError_t launch_attn_bwd_bf16(const AttnBwdArgs& a, hipStream_t stream);
