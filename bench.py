@@ -321,9 +321,11 @@ def bench_attn_push(args, w, binding, torch, yq, yk, yv, o, xo, tdt, code, ws, w
 
 def bench_backward(args, w, binding, torch, np, q, k, v, code, stream):
     """The backward of the same step: the output gradient's pack (seq->head),
-    the attention backward on the share, the unpack (head->seq) of dQ, dK and
-    dV: the exchanges' backward is the same pair of layout kernels with the
-    directions swapped.  q, k, v are the forward's packed shares."""
+    the attention backward on the share, and the head->seq exchange of dQ, dK
+    and dV -- in the backward's epilogues (ulys_attn_bwd_push into P
+    destination shards of each on this GPU), or, with replicated KV heads
+    (whose gradient copies are summed after the exchange), by the unpack
+    kernels.  q, k, v are the forward's packed shares."""
     from ulysses_head_sharded_amd import synth
 
     dev = q.device
@@ -340,6 +342,11 @@ def bench_backward(args, w, binding, torch, np, q, k, v, code, stream):
     xdq = torch.empty((sl, w.b, w.h, w.d), dtype=q.dtype, device=dev)
     xdk = torch.empty((sl, w.b, w.h_kv, w.d), dtype=q.dtype, device=dev)
     xdv = torch.empty_like(xdk)
+    fused = w.h_kv % w.P == 0
+    if fused:
+        dst = {n: [torch.empty((sl, w.b, heads, w.d), dtype=q.dtype, device=dev)
+                   for _ in range(w.P)] for n, heads in (("dq", w.h), ("dk", w.h_kv), ("dv", w.h_kv))}
+        dst_ptrs = {n: [t.data_ptr() for t in ts] for n, ts in dst.items()}
     nbytes = binding.ulys_attn_bwd_workspace_size(w.s, w.b, w.h, w.h_kv, w.d, w.P,
                                                   int(w.causal), code)
     if nbytes < 0:
@@ -360,18 +367,27 @@ def bench_backward(args, w, binding, torch, np, q, k, v, code, stream):
                                         code, sh), "pack dO")
         if record:
             e[1].record(stream)
-        call(binding.ulys_attn_bwd(qs.data_ptr(), ks.data_ptr(), vs.data_ptr(), o.data_ptr(),
-                                   gy.data_ptr(), lse.data_ptr(), dq.data_ptr(), dk.data_ptr(),
-                                   dv.data_ptr(), w.s, w.b, w.h, w.h_kv, w.d, w.P,
-                                   int(w.causal), code, ws.data_ptr(), nbytes, sh), "attn bwd")
+        if fused:
+            call(binding.ulys_attn_bwd_push(qs.data_ptr(), ks.data_ptr(), vs.data_ptr(),
+                                            o.data_ptr(), gy.data_ptr(), lse.data_ptr(),
+                                            dst_ptrs["dq"], dst_ptrs["dk"], dst_ptrs["dv"], 0,
+                                            w.s, w.b, w.h, w.h_kv, w.d, w.P, int(w.causal), code,
+                                            ws.data_ptr(), nbytes, sh), "attn bwd push")
+        else:
+            call(binding.ulys_attn_bwd(qs.data_ptr(), ks.data_ptr(), vs.data_ptr(), o.data_ptr(),
+                                       gy.data_ptr(), lse.data_ptr(), dq.data_ptr(),
+                                       dk.data_ptr(), dv.data_ptr(), w.s, w.b, w.h, w.h_kv, w.d,
+                                       w.P, int(w.causal), code, ws.data_ptr(), nbytes, sh),
+                 "attn bwd")
         if record:
             e[2].record(stream)
-        call(binding.ulys_unpack_head2seq(dq.data_ptr(), xdq.data_ptr(), w.s, w.b, w.h, w.d,
-                                          w.P, code, sh), "unpack dq")
-        # dK, dV: with replicated KV heads the copies' gradients are summed
-        for src, dst in ((dk, xdk), (dv, xdv)):
-            call(binding.ulys_unpack_head2seq_kv(src.data_ptr(), dst.data_ptr(), w.s, w.b,
-                                                 w.h_kv, w.d, w.P, code, sh), "unpack dkv")
+        if not fused:
+            call(binding.ulys_unpack_head2seq(dq.data_ptr(), xdq.data_ptr(), w.s, w.b, w.h, w.d,
+                                              w.P, code, sh), "unpack dq")
+            # dK, dV: the replicated KV heads' gradient copies are summed
+            for src, dst_t in ((dk, xdk), (dv, xdv)):
+                call(binding.ulys_unpack_head2seq_kv(src.data_ptr(), dst_t.data_ptr(), w.s, w.b,
+                                                     w.h_kv, w.d, w.P, code, sh), "unpack dkv")
         if record:
             e.append(torch.cuda.Event(enable_timing=True))
             e[3].record(stream)
@@ -388,7 +404,15 @@ def bench_backward(args, w, binding, torch, np, q, k, v, code, stream):
     attn_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in marks]))
     layout_ms = float(np.mean([e[0].elapsed_time(e[1]) + e[2].elapsed_time(e[3]) for e in marks]))
     flops = w.attn_bwd_flops()
-    layout_bytes = w.layout_bytes()  # pack dO + unpack dQ: as pack Q + unpack O; dK, dV as K, V
+    if fused:  # the pack of dO only; the gradients' exchange is in the backward's epilogues
+        layout_bytes = 2 * w.shard_bytes()
+        layout = {"pack_do_us": round(layout_ms * 1e3, 2),
+                  "gbps": round(layout_bytes / (layout_ms * 1e-3) / 1e9, 1), "bytes": layout_bytes,
+                  "dqkv_exchange": "in the backward's epilogues (ulys_attn_bwd_push)"}
+    else:
+        layout_bytes = w.layout_bytes()  # pack dO + unpack dQ as pack Q + unpack O; dK, dV as K, V
+        layout = {"pack_do_unpack_dqkv_us": round(layout_ms * 1e3, 2),
+                  "gbps": round(layout_bytes / (layout_ms * 1e-3) / 1e9, 1), "bytes": layout_bytes}
     return {
         "steps": args.bwd_steps, "ms_per_step": round(ms_step, 4),
         "tflops_step": round(flops / (ms_step * 1e-3) / 1e12, 2),
@@ -396,9 +420,7 @@ def bench_backward(args, w, binding, torch, np, q, k, v, code, stream):
                      "frac_peak": round(flops / (attn_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
                      "flops": flops, "flops_rule": "10 d b hp pairs (five products)",
                      "workspace_bytes": int(nbytes)},
-        "layout": {"pack_do_unpack_dqkv_us": round(layout_ms * 1e3, 2),
-                   "gbps": round(layout_bytes / (layout_ms * 1e-3) / 1e9, 1),
-                   "bytes": layout_bytes},
+        "layout": layout,
     }
 
 
