@@ -122,6 +122,45 @@ def test_full_size_sampled_parity(name):
     assert np.max(np.abs(of)) <= np.max(np.abs(as_f64(v))) + TOL[w.dtype]
 
 
+@pytest.mark.parametrize("name", [n for n in FULL if WORKLOADS[n].dtype == "bf16"])
+def test_full_size_sampled_parity_push(name):
+    """The bench step's attention: ulys_attn_fwd_push (rank P-1 writing its
+    head columns into P destination shards, with the workspace) at the full
+    share, the sampled rows read back from the shards they landed in."""
+    w = WORKLOADS[name]
+    print(f"case push {name}: s={w.s} b={w.b} hp={w.hp} hkvp={w.hkvp} causal={w.causal}",
+          flush=True)
+    q, k, v = share_inputs(w.c, w.s, w.b, w.hp, w.hkvp, w.d, w.dtype)
+    dev()
+    qd, kd, vd = to_dev(q), to_dev(k), to_dev(v)
+    sl, rank, code = w.s // w.P, w.P - 1, binding.ULYS_BF16
+    shards = [torch.empty((sl, w.b, w.h, w.d), dtype=torch.bfloat16, device="cuda")
+              for _ in range(w.P)]
+    lse = torch.empty((w.b, w.hp, w.s), dtype=torch.float32, device="cuda")
+    nbytes = binding.ulys_attn_fwd_workspace_size(w.s, w.b, w.h, w.h_kv, w.d, w.P,
+                                                  int(w.causal), code)
+    ws = torch.empty(max(nbytes, 16), dtype=torch.uint8, device="cuda")
+    rc = binding.ulys_attn_fwd_push(qd.data_ptr(), kd.data_ptr(), vd.data_ptr(),
+                                    [t.data_ptr() for t in shards], rank, lse.data_ptr(), w.s, w.b,
+                                    w.h, w.h_kv, w.d, w.P, int(w.causal), code,
+                                    ws.data_ptr() if nbytes > 0 else None, nbytes,
+                                    torch.cuda.current_stream().cuda_stream)
+    assert rc == 0, binding.ulys_status_string(rc)
+    torch.cuda.synchronize()
+    rows = synth.row_sample(100 * w.c + 7, w.s, w.b, w.hp, tile_bounds=(64, 128),
+                            **FULL[name])
+    o_ref, lse_ref = oracle.attn_rows(q, k, v, rows, w.s, w.b, w.h, w.h_kv, w.d, w.P,
+                                      w.causal)
+    # row (be, i, t) of the share sits in shard t // sl, token t % sl, head rank*hp + i
+    got = np.stack([from_dev(shards[int(t) // sl][int(t) % sl, int(be), rank * w.hp + int(i)])
+                    for be, i, t in rows])
+    err = np.max(np.abs(as_f64(got) - o_ref))
+    print(f"  {rows.shape[0]} rows, max err {err:.3e}", flush=True)
+    assert err <= TOL[w.dtype]
+    lse_h = from_dev(lse)
+    assert np.max(np.abs(lse_h[rows[:, 0], rows[:, 1], rows[:, 2]] - lse_ref)) <= LSE_TOL[w.dtype]
+
+
 @pytest.mark.parametrize("causal", [False, True])
 def test_value_ones_gives_ones(causal):
     s, b, h, h_kv, d, P = 777, 1, 4, 2, 128, 1
