@@ -19,7 +19,7 @@ def test_more_than_one_gpu_is_refused():
 
 def test_workload_flops_and_bytes():
     w = WORKLOADS["gpt1.2b-32k"]
-    # 4 d_h b hp s(s+1)/2, the survey's 5.4977e11 for this share
+    # 4 d_h b hp s(s+1)/2 = 5.4977e11 for this share
     assert w.attn_flops() == 4 * 128 * 1 * 2 * (32768 * 32769 // 2)
     assert abs(w.attn_flops() - 5.4977e11) / 5.4977e11 < 1e-4
     assert w.attn_bwd_flops() == 2.5 * w.attn_flops()
