@@ -431,7 +431,7 @@ def main():
         return
     if args.gpus != 1:
         print(f"bench.py measures one rank's share on ONE GPU; --gpus {args.gpus} is not "
-              "supported (the all-to-all across GPUs is not part of this build)",
+              "supported (the all-to-all across GPUs is not implemented here)",
               file=sys.stderr)
         sys.exit(2)
 

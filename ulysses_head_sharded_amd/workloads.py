@@ -74,8 +74,9 @@ WORKLOADS = {
                          "MHA long share: 32 heads, s=131072, P=8, causal"),
     "gqa-64k": Workload("gqa-64k", 4, 8, 65536, 2, 32, 8, 128, "bf16", True,
                         "GQA share: 32 Q / 8 KV heads, s=65536, b=2, P=8, causal"),
-    # not in the task's list: the GQA share at twice the ranks it has KV heads
-    # for, possible only with KV-head replication (each rank gets one KV head)
+    # an extra share beside the ones above: the GQA share at twice the ranks it
+    # has KV heads for, possible only with KV-head replication (each rank gets
+    # one KV head)
     "gqa-64k-p16": Workload("gqa-64k-p16", 6, 16, 65536, 2, 32, 8, 128, "bf16", True,
                             "GQA share with fewer KV heads than ranks: 32 Q / 8 KV heads, "
                             "s=65536, b=2, P=16 (KV heads replicated), causal"),
