@@ -227,7 +227,7 @@ int64_t ulys_attn_fwd_workspace_size(int64_t s, int64_t b, int64_t h, int64_t h_
  *                contents ignored on entry, undefined on return.
  * Gradients are accumulated in fp32 and rounded once (nearest-even).  No
  * atomics: the result does not depend on scheduling.
- * Supported: ULYS_BF16 with d_h = 128.
+ * Supported: ULYS_BF16 with d_h in {64, 128}.
  * Errors: as ulys_attn_fwd, plus ULYS_ERR_NULL for any missing pointer
  * (lse and workspace included), ULYS_ERR_UNSUPPORTED for another dtype or
  * head size, ULYS_ERR_DIM for a workspace smaller than required, and
@@ -371,7 +371,7 @@ const char* ulys_status_string(int status);
 /* ABI version of this header: (major << 16) | minor. */
 int ulys_abi_version(void);
 
-#define ULYS_ABI_VERSION ((1 << 16) | 8)
+#define ULYS_ABI_VERSION ((1 << 16) | 9)
 
 #ifdef __cplusplus
 }

@@ -36,7 +36,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_version(lib):
-    assert B.ulys_abi_version() == (1 << 16) | 8
+    assert B.ulys_abi_version() == (1 << 16) | 9
 
 
 def test_status_strings(lib):
@@ -162,7 +162,7 @@ def bwd_args(**kw):
     (dict(s=66), B.ULYS_ERR_DIVISIBILITY),
     (dict(h=12, h_kv=6), B.ULYS_ERR_DIVISIBILITY),
     (dict(h_kv=3), B.ULYS_ERR_DIVISIBILITY),
-    (dict(d=64), B.ULYS_ERR_UNSUPPORTED),
+    (dict(d=96), B.ULYS_ERR_UNSUPPORTED),
     (dict(dtype=B.ULYS_F32), B.ULYS_ERR_UNSUPPORTED),
     (dict(nbytes=16), B.ULYS_ERR_DIM),
     (dict(dk=DK + 4), B.ULYS_ERR_ALIGNMENT),
@@ -179,7 +179,8 @@ def test_attn_bwd_workspace_size(lib):
     # D and lse * log2(e) per query row, rows padded to 4 queries
     assert B.ulys_attn_bwd_workspace_size(64, 1, 8, 8, 128, 4, 1, B.ULYS_BF16) == 2 * 2 * 64 * 4
     assert B.ulys_attn_bwd_workspace_size(66, 1, 8, 8, 128, 2, 1, B.ULYS_BF16) == 2 * 4 * 68 * 4
-    assert B.ulys_attn_bwd_workspace_size(64, 1, 8, 8, 64, 4, 1, B.ULYS_BF16) == B.ULYS_ERR_UNSUPPORTED
+    assert B.ulys_attn_bwd_workspace_size(64, 1, 8, 8, 64, 4, 1, B.ULYS_BF16) == 2 * 2 * 64 * 4
+    assert B.ulys_attn_bwd_workspace_size(64, 1, 8, 8, 96, 4, 1, B.ULYS_BF16) == B.ULYS_ERR_UNSUPPORTED
     assert B.ulys_attn_bwd_workspace_size(64, 1, 8, 8, 128, 4, 1, B.ULYS_F32) == B.ULYS_ERR_UNSUPPORTED
     assert B.ulys_attn_bwd_workspace_size(0, 1, 8, 8, 128, 4, 1, B.ULYS_BF16) == B.ULYS_ERR_DIM
 

@@ -74,20 +74,22 @@ def gpu_fwd(q, k, v, s, b, h, h_kv, d, P, causal):
 
 
 # s spans several 32-query and 64-key tiles with ragged tails; heads cover MHA,
-# GQA 4:1 and 8:1 (two subgroups per KV head in the dq kernel) and MQA
+# GQA 4:1 and 8:1 (two subgroups per KV head in the dq kernel) and MQA; both
+# head sizes (d_h = 64 on a subset of the lengths)
 SMALL = []
 for (s, b) in [(1, 1), (5, 2), (32, 1), (33, 1), (64, 1), (100, 2), (200, 1), (321, 1), (640, 1)]:
     for (h, h_kv, P) in [(2, 2, 1), (8, 2, 2), (16, 2, 1), (8, 8, 4), (4, 1, 1)]:
         if s % P:
             continue
         for causal in (False, True):
-            SMALL.append((s, b, h, h_kv, P, causal))
+            SMALL.append((s, b, h, h_kv, 128, P, causal))
+            if s in (1, 33, 100, 321, 640):
+                SMALL.append((s, b, h, h_kv, 64, P, causal))
 
 
-@pytest.mark.parametrize("s,b,h,h_kv,P,causal", SMALL)
-def test_bwd_small_parity(s, b, h, h_kv, P, causal):
-    d = 128
-    print(f"case bwd s={s} b={b} h={h} h_kv={h_kv} P={P} causal={causal}", flush=True)
+@pytest.mark.parametrize("s,b,h,h_kv,d,P,causal", SMALL)
+def test_bwd_small_parity(s, b, h, h_kv, d, P, causal):
+    print(f"case bwd s={s} b={b} h={h} h_kv={h_kv} d={d} P={P} causal={causal}", flush=True)
     q, k, v = share_inputs(7, s, b, h // P, h_kv // P, d, "bf16")
     dout = synth.tensor(704, (s, b, h // P, d), "bf16")
     o, lse = oracle_fwd_inputs(q, k, v, s, b, h, h_kv, d, P, causal)
@@ -98,13 +100,13 @@ def test_bwd_small_parity(s, b, h, h_kv, P, causal):
     check("dv", dv, rv)
 
 
-@pytest.mark.parametrize("s,b,h,h_kv,P,causal", [(300, 2, 8, 2, 2, True), (257, 1, 4, 4, 1, False),
-                                                  (1024, 1, 2, 2, 1, True), (1024, 1, 2, 2, 1, False),
-                                                  (2048, 1, 8, 2, 1, True)])
-def test_bwd_chain_after_gpu_forward(s, b, h, h_kv, P, causal):
+@pytest.mark.parametrize("s,b,h,h_kv,d,P,causal", [
+    (300, 2, 8, 2, 128, 2, True), (257, 1, 4, 4, 128, 1, False), (1024, 1, 2, 2, 128, 1, True),
+    (1024, 1, 2, 2, 128, 1, False), (2048, 1, 8, 2, 128, 1, True), (2048, 1, 8, 2, 64, 1, True),
+    (1000, 2, 4, 4, 64, 2, False)])
+def test_bwd_chain_after_gpu_forward(s, b, h, h_kv, d, P, causal):
     """The backward fed by the GPU forward's o and lse (as a training step)."""
-    d = 128
-    print(f"case chain s={s} b={b} h={h} h_kv={h_kv} P={P} causal={causal}", flush=True)
+    print(f"case chain s={s} b={b} h={h} h_kv={h_kv} d={d} P={P} causal={causal}", flush=True)
     q, k, v = share_inputs(8, s, b, h // P, h_kv // P, d, "bf16")
     dout = synth.tensor(804, (s, b, h // P, d), "bf16")
     o, lse = gpu_fwd(q, k, v, s, b, h, h_kv, d, P, causal)

@@ -160,20 +160,22 @@ def test_attn_push_equals_attn_then_push(s, b, h, h_kv, d, P, rank, causal, ws):
     assert torch.equal(lse.tensor, lse_ref)
 
 
-# (s, b, h, h_kv, P, rank, causal), d = 128: segments of 64, 25 and 125 rows,
-# GQA, and the 32K share, whose backward splits both its dQ and dK/dV items
-BWD_PUSH = [(256, 1, 8, 4, 4, 1, True), (100, 2, 8, 8, 4, 3, False),
-            (1000, 1, 16, 8, 8, 0, True), (32768, 1, 16, 16, 8, 6, True)]
+# (s, b, h, h_kv, d, P, rank, causal): segments of 64, 25 and 125 rows, GQA,
+# both head sizes, and the 32K share, whose backward splits both its dQ and
+# dK/dV items
+BWD_PUSH = [(256, 1, 8, 4, 128, 4, 1, True), (100, 2, 8, 8, 128, 4, 3, False),
+            (1000, 1, 16, 8, 128, 8, 0, True), (32768, 1, 16, 16, 128, 8, 6, True),
+            (1000, 1, 16, 8, 64, 8, 5, True)]
 
 
-@pytest.mark.parametrize("s,b,h,h_kv,P,rank,causal", BWD_PUSH)
-def test_attn_bwd_push_equals_bwd_then_push(s, b, h, h_kv, P, rank, causal):
+@pytest.mark.parametrize("s,b,h,h_kv,d,P,rank,causal", BWD_PUSH)
+def test_attn_bwd_push_equals_bwd_then_push(s, b, h, h_kv, d, P, rank, causal):
     """ulys_attn_bwd_push writes, bit for bit, what ulys_attn_bwd followed by
     ulys_head2seq_push of dQ, dK and dV writes (the rest of every destination
     shard, and its guard bands, untouched)."""
-    print(f"case attn_bwd_push s={s} b={b} h={h} h_kv={h_kv} P={P} rank={rank} causal={causal}",
-          flush=True)
-    d, sl, hp, hkvp = 128, s // P, h // P, h_kv // P
+    print(f"case attn_bwd_push s={s} b={b} h={h} h_kv={h_kv} d={d} P={P} rank={rank} "
+          f"causal={causal}", flush=True)
+    sl, hp, hkvp = s // P, h // P, h_kv // P
     from gpu_util import share_inputs
     q, k, v = share_inputs(60 + P, s, b, hp, hkvp, d, "bf16")
     g = synth.tensor(6000 + s, (s, b, hp, d), "bf16")

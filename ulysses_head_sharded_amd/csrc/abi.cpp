@@ -201,7 +201,7 @@ int64_t ulys_attn_bwd_workspace_size(int64_t s, int64_t b, int64_t h, int64_t h_
   int64_t nq = 0, nkv = 0, nl = 0;
   const int rc = check_attn_shape(s, b, h, h_kv, d_h, P, dtype, &nq, &nkv, &nl);
   if (rc != ULYS_OK) return rc;
-  if (dtype != ULYS_BF16 || d_h != 128) return ULYS_ERR_UNSUPPORTED;
+  if (dtype != ULYS_BF16) return ULYS_ERR_UNSUPPORTED;
   ulys::AttnBwdArgs a;
   a.s = s;
   a.b = b;

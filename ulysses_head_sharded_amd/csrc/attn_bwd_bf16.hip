@@ -49,31 +49,59 @@
 namespace ulys {
 namespace {
 
-constexpr int D = 128;               // head size served here
-constexpr int ROW = D * 2;           // bytes of one bf16 row
-constexpr int CHUNKS = ROW / 16;     // 16-byte chunks per row
 constexpr int kWaves = 8;
 constexpr int kThreads = 64 * kWaves;
 constexpr int kMaxPushRanks = 64;  // destinations of the pushing epilogues
+constexpr int kBN = 64;            // dq: keys per tile
+constexpr int kKB = 32 * kWaves;   // dkv: keys per workgroup
+constexpr int kQT = 64;            // dkv: queries per step
+constexpr int kStatBuf = 2048;     // dkv: nlse (first 256 bytes of 1 KiB) then ndelta
 
+// Sizes that follow from the head size D (64 or 128).
+template <int D>
+struct Geo {
+  static constexpr int ROW = D * 2;        // bytes of one bf16 row
+  static constexpr int CHUNKS = ROW / 16;  // 16-byte chunks per row
+  static constexpr int RPL = 64 / CHUNKS;  // rows filled by one 64-lane 16-byte load
+  // dq
+  static constexpr int kTile = kBN * ROW;                         // one K or V tile
+  static constexpr int kQLoads = kBN * CHUNKS / (64 * kWaves);    // loads per lane per tensor
+  static constexpr int kDqPart = kWaves * 64 * (D / 2);           // floats of one split unit
+  // dkv
+  static constexpr int kQTile = kQT * ROW;                        // one Q or dout tile
+  static constexpr int kVBlock = kKB * ROW;                       // the workgroup's V rows
+  static constexpr int kKLoads = kQT * CHUNKS / (64 * kWaves);    // loads per lane per tensor
+  static constexpr int kVLoads = kVBlock / (1024 * kWaves);       // loads per lane, V block
+  static constexpr int kDkvPart = kWaves * 64 * D;                // floats of one split unit
+  static constexpr int kDkvLds = kVBlock + 4 * kQTile + 2 * kStatBuf;
+};
+
+// Chunk swizzle g(r) of row r (the tile layout above).
+template <int D>
 __device__ __forceinline__ int dswz(int r) {
   const int i = r & 3;
-  return ((4 * i) ^ ((i >> 1) << 1)) ^ ((r >> 2) & 3);
+  if constexpr (D == 128)
+    return ((4 * i) ^ ((i >> 1) << 1)) ^ ((r >> 2) & 3);
+  else
+    return (4 * (i >> 1)) ^ ((r >> 2) & 3);
 }
 
 // ------------------------------------------------------------------ prep
-// 16 lanes per query row (8 bf16 each); rows enumerated in memory order
+// D / 8 lanes per query row (8 bf16 each); rows enumerated in memory order
 // r = (t * b + be) * hp + i of the [s, b, hp, d] tensors.  Writes
 // ndelta = -D and nlse = -lse * sqrt(d_h): with c = log2(e) / sqrt(d_h),
 // P = exp2(c (q.k + nlse)).
+template <int D>
 __global__ __launch_bounds__(256) void bwd_prep_kernel(const uint16_t* __restrict__ o,
                                                        const uint16_t* __restrict__ dout,
                                                        const float* __restrict__ lse,
                                                        float* __restrict__ ndelta,
                                                        float* __restrict__ nlse, int rows,
                                                        int s, int s_pad, int bhp, float sqrt_d) {
+  constexpr int LPR = D / 8, SH = (D == 128) ? 4 : 3;  // lanes per row, log2
+  static_assert(LPR == 1 << SH, "head size");
   const int gid = blockIdx.x * 256 + threadIdx.x;
-  const int r = gid >> 4, part = gid & 15;
+  const int r = gid >> SH, part = gid & (LPR - 1);
   float acc = 0.f;
   if (r < rows) {
     const u32x4 a = *reinterpret_cast<const u32x4*>(o + (int64_t)r * D + part * 8);
@@ -83,7 +111,7 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(const uint16_t* __restric
     for (int e = 0; e < 8; ++e) acc = fmaf((float)av[e], (float)gv[e], acc);
   }
 #pragma unroll
-  for (int w = 8; w >= 1; w >>= 1) acc += __shfl_xor(acc, w, 16);
+  for (int w = LPR / 2; w >= 1; w >>= 1) acc += __shfl_xor(acc, w, LPR);
   if (r < rows && part == 0) {
     const int t = r / bhp, rem = r - t * bhp;  // rem = be * hp + i
     ndelta[(int64_t)rem * s_pad + t] = -acc;
@@ -142,6 +170,7 @@ __device__ __forceinline__ int xcd_unit(int b, int n) {
 // Transposed 32 x 32 accumulator (rows = features, column = lane % 32) scaled
 // and rounded once to bf16, stored at row `col` of a [tokens, heads, d] tensor
 // with token stride tok_bytes and head offset head_off (bytes).
+template <int D>
 __device__ __forceinline__ void store_t(__amdgpu_buffer_rsrc_t r, const f32x16* acc, float scale,
                                         int col, int tok_bytes, int head_off, int hh) {
   const int off = col * tok_bytes + head_off + hh * 8;
@@ -169,6 +198,7 @@ __device__ __forceinline__ void store_t(__amdgpu_buffer_rsrc_t r, const f32x16* 
 // token (batch, this rank's head columns, the head).  A wave's 32 rows may
 // span several segments; it takes them one uniform segment at a time, so
 // every destination pointer is a scalar load.
+template <int D>
 __device__ __forceinline__ void store_t_push(uint16_t* const* table, int dst_bytes,
                                              const f32x16* acc, float scale, int row, int s,
                                              int sl, int tok_bytes, int col_off, int hh) {
@@ -206,25 +236,27 @@ __device__ __forceinline__ void store_t_push(uint16_t* const* table, int dst_byt
 // The three outputs' stores: to dq / dk / dv, or pushed (PUSH, a separate
 // instantiation of every kernel, so the plain kernels compile as if the
 // pushing epilogue did not exist)
-template <bool PUSH>
+template <int D, bool PUSH>
 __device__ __forceinline__ void store_dq(const BwdParams& p, const f32x16* acc, int row, int be,
                                          int head, int hh) {
+  constexpr int ROW = Geo<D>::ROW;
   if constexpr (PUSH)
-    store_t_push(p.dq_rank, p.q_pbytes, acc, p.inv_sd, row, p.s, p.sl, p.q_ptok,
+    store_t_push<D>(p.dq_rank, p.q_pbytes, acc, p.inv_sd, row, p.s, p.sl, p.q_ptok,
                  be * p.q_pbe + p.q_phead + head * ROW, hh);
   else
-    store_t(rsrc(p.dq, p.q_bytes), acc, p.inv_sd, row, p.q_tok_bytes, (be * p.hp + head) * ROW,
+    store_t<D>(rsrc(p.dq, p.q_bytes), acc, p.inv_sd, row, p.q_tok_bytes, (be * p.hp + head) * ROW,
             hh);
 }
-template <bool PUSH>
+template <int D, bool PUSH>
 __device__ __forceinline__ void store_dkv(const BwdParams& p, const f32x16* acc, bool is_dk,
                                           int row, int be, int kvg, int hh) {
+  constexpr int ROW = Geo<D>::ROW;
   const float scale = is_dk ? p.inv_sd : 1.f;
   if constexpr (PUSH)
-    store_t_push(is_dk ? p.dk_rank : p.dv_rank, p.kv_pbytes, acc, scale, row, p.s, p.sl,
+    store_t_push<D>(is_dk ? p.dk_rank : p.dv_rank, p.kv_pbytes, acc, scale, row, p.s, p.sl,
                  p.kv_ptok, be * p.kv_pbe + p.kv_phead + kvg * ROW, hh);
   else
-    store_t(rsrc(is_dk ? p.dk : p.dv, p.kv_bytes), acc, scale, row, p.kv_tok_bytes,
+    store_t<D>(rsrc(is_dk ? p.dk : p.dv, p.kv_bytes), acc, scale, row, p.kv_tok_bytes,
             (be * p.hkvp + kvg) * ROW, hh);
 }
 
@@ -250,47 +282,49 @@ __device__ __forceinline__ void add_parts(const float* u0, const float* u1, f32x
     for (int r = 0; r < 16; ++r) acc[n][r] = a[(n * 16 + r) * 64] + b[(n * 16 + r) * 64];
 }
 
-// Lane parts of the LDS addresses into a swizzled tile of 256-byte rows.
+// Lane parts of the LDS addresses into a swizzled tile of ROW-byte rows.
 //  row reads (A operand of 32 rows x 16 features): row l%32 of a 32-row
 //  block, logical chunk 2 dk + hh;
 //  transposed reads (A operand of 32 features x 16 rows), feature block db,
 //  16-row step: rows 4 hh + (l%16)/4 (lo) and + 8 (hi), byte column
 //  64 db + 32 ((l/16)%2) + 8 (l%4).  Row offsets that are multiples of 16
-//  leave the swizzle unchanged; +8 rows flips bit 1 of g.
+//  leave the swizzle unchanged.
 //  Since 2 dk has bit 0 clear, (2 dk + hh) ^ g = 2 (dk ^ (g >> 1)) + ((hh ^ g) & 1),
-//  so the row read of step dk is at row_base ^ (32 dk): one register.
+//  so the row read of step dk is at row_base ^ (32 dk): one register (the
+//  XOR stays below bit 8 for D = 128 and below bit 7 for D = 64, where g < 8).
+template <int D>
 struct TileAddr {
   int row_base;
   int tr_lo[D / 32], tr_hi[D / 32];
   __device__ __forceinline__ int row_rd(int dk) const { return row_base ^ (dk << 5); }
 };
-__device__ __forceinline__ TileAddr tile_addr(int lane) {
-  TileAddr a;
+template <int D>
+__device__ __forceinline__ TileAddr<D> tile_addr(int lane) {
+  constexpr int ROW = Geo<D>::ROW;
+  TileAddr<D> a;
   const int l32 = lane & 31, hh = lane >> 5;
-  a.row_base = l32 * ROW + ((hh ^ dswz(l32)) << 4);
+  a.row_base = l32 * ROW + ((hh ^ dswz<D>(l32)) << 4);
   const int vr = 4 * hh + ((lane & 15) >> 2);
 #pragma unroll
   for (int db = 0; db < D / 32; ++db) {
     const int c = 4 * db + 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1);
-    a.tr_lo[db] = vr * ROW + ((c ^ dswz(vr)) << 4) + 8 * (lane & 1);
-    a.tr_hi[db] = (vr + 8) * ROW + ((c ^ dswz(vr + 8)) << 4) + 8 * (lane & 1);
+    a.tr_lo[db] = vr * ROW + ((c ^ dswz<D>(vr)) << 4) + 8 * (lane & 1);
+    a.tr_hi[db] = (vr + 8) * ROW + ((c ^ dswz<D>(vr + 8)) << 4) + 8 * (lane & 1);
   }
   return a;
 }
 
 // A operand of a transposed read at 16-row step base `tile + 16 ks * ROW`.
-__device__ __forceinline__ bf16x8 read_tr(const uint8_t* tile, const TileAddr& a, int ks, int db) {
+template <int D>
+__device__ __forceinline__ bf16x8 read_tr(const uint8_t* tile, const TileAddr<D>& a, int ks,
+                                          int db) {
+  constexpr int ROW = Geo<D>::ROW;
   const u32x2 lo = lds_read_tr(reinterpret_cast<const uint16_t*>(tile + ks * 16 * ROW + a.tr_lo[db]));
   const u32x2 hi = lds_read_tr(reinterpret_cast<const uint16_t*>(tile + ks * 16 * ROW + a.tr_hi[db]));
   return as_bf16x8(u32x4{lo[0], lo[1], hi[0], hi[1]});
 }
 
 // ------------------------------------------------------------------ dq
-constexpr int kBN = 64;              // keys per tile
-constexpr int kTile = kBN * ROW;     // one K or V tile (16 KiB)
-constexpr int kQLoads = kBN * CHUNKS / (64 * kWaves);  // 16-byte loads per lane per tensor
-constexpr int kDqPart = kWaves * 64 * (D / 2);         // floats of one split dq unit
-
 struct QItem {
   int qblk, be, kvg, head, q0;
 };
@@ -310,8 +344,10 @@ __device__ __forceinline__ QItem decode_q_item(const BwdParams& p, int rank, int
   return it;
 }
 
-template <bool CAUSAL, bool PUSH>
+template <int D, bool CAUSAL, bool PUSH>
 __global__ __launch_bounds__(kThreads, 1) void bwd_dq_kernel(BwdParams p) {
+  constexpr int ROW = Geo<D>::ROW, CHUNKS = Geo<D>::CHUNKS, RPL = Geo<D>::RPL;
+  constexpr int kTile = Geo<D>::kTile, kQLoads = Geo<D>::kQLoads;
   // LDS: K0 K1 V0 V1
   __shared__ __attribute__((aligned(16))) uint8_t lds[4 * kTile];
   const int lane = threadIdx.x & 63;
@@ -362,12 +398,12 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dq_kernel(BwdParams p) {
   const int wave_last_q = min(it.q0 + 32, p.s) - 1;
   const int wave_tiles = (it.q0 >= p.s) ? 0 : (CAUSAL ? wave_last_q / kBN + 1 : n_item);
 
-  // direct loads: wave w, load i fills rows (w*kQLoads + i)*4 .. +3 of a tile
+  // direct loads: wave w, load i fills rows (w*kQLoads + i)*RPL .. +RPL-1 of a tile
   int src[kQLoads];
 #pragma unroll
   for (int i = 0; i < kQLoads; ++i) {
-    const int row = (wave * kQLoads + i) * 4 + lane / CHUNKS;
-    src[i] = row * p.kv_tok_bytes + kv_head_off + (((lane % CHUNKS) ^ dswz(row)) << 4);
+    const int row = (wave * kQLoads + i) * RPL + lane / CHUNKS;
+    src[i] = row * p.kv_tok_bytes + kv_head_off + (((lane % CHUNKS) ^ dswz<D>(row)) << 4);
   }
   auto load_tile = [&](int t, int buf) {
     const int koff = t * kBN * p.kv_tok_bytes;
@@ -378,7 +414,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dq_kernel(BwdParams p) {
       load_lds16(rv, lds + (2 + buf) * kTile + dst, src[i] + koff);
     }
   };
-  const TileAddr ta = tile_addr(lane);
+  const TileAddr<D> ta = tile_addr<D>(lane);
 
   f32x16 acc[D / 32];
 #pragma unroll
@@ -441,7 +477,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dq_kernel(BwdParams p) {
         for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
           for (int db = 0; db < D / 32; ++db)
-            acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(read_tr(kh, ta, ks, db), dsb[ks],
+            acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(read_tr<D>(kh, ta, ks, db), dsb[ks],
                                                               acc[db], 0, 0, 0);
       }
     }
@@ -454,35 +490,26 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dq_kernel(BwdParams p) {
     if (t + 1 < t_hi) dq_step(t + 1, std::integral_constant<int, 1>{});
   }
   if (p.q_split) {
-    store_part<D / 32>(p.part + (int64_t)blockIdx.x * kDqPart, acc, wave, lane);
+    store_part<D / 32>(p.part + (int64_t)blockIdx.x * Geo<D>::kDqPart, acc, wave, lane);
     return;
   }
-  store_dq<PUSH>(p, acc, my_q, it.be, it.head, hh);
+  store_dq<D, PUSH>(p, acc, my_q, it.be, it.head, hh);
 }
 
 // The two halves of every dq item: added in a fixed order, scaled, rounded.
-template <bool CAUSAL, bool PUSH>
+template <int D, bool CAUSAL, bool PUSH>
 __global__ __launch_bounds__(kThreads) void bwd_dq_merge_kernel(BwdParams p) {
+  constexpr int kDqPart = Geo<D>::kDqPart;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int l32 = lane & 31, hh = lane >> 5;
   const QItem it = decode_q_item(p, blockIdx.x, wave, CAUSAL);
   const float* u0 = p.part + (int64_t)(2 * blockIdx.x) * kDqPart;
   f32x16 acc[D / 32];
   add_parts<D / 32>(u0, u0 + kDqPart, acc, wave, lane);
-  store_dq<PUSH>(p, acc, it.q0 + l32, it.be, it.head, hh);
+  store_dq<D, PUSH>(p, acc, it.q0 + l32, it.be, it.head, hh);
 }
 
 // ------------------------------------------------------------------ dk, dv
-constexpr int kKB = 32 * kWaves;        // keys per workgroup
-constexpr int kQT = 64;                 // queries per step
-constexpr int kQTile = kQT * ROW;       // one Q or dout tile (16 KiB)
-constexpr int kVBlock = kKB * ROW;      // the workgroup's V rows (64 KiB)
-constexpr int kStatBuf = 2048;          // nlse (first 256 bytes of 1 KiB) then ndelta
-constexpr int kKLoads = kQT * CHUNKS / (64 * kWaves);   // loads per lane per tile tensor
-constexpr int kVLoads = kVBlock / (1024 * kWaves);      // loads per lane for the V block
-constexpr int kDkvPart = kWaves * 64 * D;               // floats of one split dkv unit
-constexpr int kDkvLds = kVBlock + 4 * kQTile + 2 * kStatBuf;
-
 struct KItem {
   int kblk, be, kvg;
 };
@@ -496,12 +523,16 @@ __device__ __forceinline__ KItem decode_k_item(const BwdParams& p, int rank) {
   return it;
 }
 
-template <bool CAUSAL, bool PUSH>
+template <int D, bool CAUSAL, bool PUSH>
 __global__ __launch_bounds__(kThreads, 1) void bwd_dkv_kernel(BwdParams p) {
+  constexpr int ROW = Geo<D>::ROW, CHUNKS = Geo<D>::CHUNKS, RPL = Geo<D>::RPL;
+  constexpr int kQTile = Geo<D>::kQTile, kVBlock = Geo<D>::kVBlock;
+  constexpr int kKLoads = Geo<D>::kKLoads, kVLoads = Geo<D>::kVLoads;
+  constexpr int kDkvPart = Geo<D>::kDkvPart;
   // LDS: Q0 Q1 | dout0 dout1 | V block | stats0 stats1.  The tiles first:
   // with the buffer and half indices compile-time constants, every tile read
   // is one lane register plus an offset that fits the instruction's 16 bits.
-  __shared__ __attribute__((aligned(16))) uint8_t lds[kDkvLds];
+  __shared__ __attribute__((aligned(16))) uint8_t lds[Geo<D>::kDkvLds];
   uint8_t* qt = lds;
   uint8_t* gt = qt + 2 * kQTile;
   uint8_t* vblk = gt + 2 * kQTile;
@@ -538,10 +569,10 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkv_kernel(BwdParams p) {
   // the workgroup's V rows into LDS (swizzled like the tiles)
 #pragma unroll
   for (int i = 0; i < kVLoads; ++i) {
-    const int row = (wave * kVLoads + i) * 4 + lane / CHUNKS;
+    const int row = (wave * kVLoads + i) * RPL + lane / CHUNKS;
     load_lds16(rv, vblk + (wave * kVLoads + i) * 1024,
                (it.kblk * kKB + row) * p.kv_tok_bytes + kv_head_off +
-                   (((lane % CHUNKS) ^ dswz(row)) << 4));
+                   (((lane % CHUNKS) ^ dswz<D>(row)) << 4));
   }
 #pragma unroll
   for (int dk = 0; dk < D / 16; ++dk) asm volatile("" ::"v"(kf[dk]));
@@ -559,8 +590,8 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkv_kernel(BwdParams p) {
   int src[kKLoads];
 #pragma unroll
   for (int i = 0; i < kKLoads; ++i) {
-    const int row = (wave * kKLoads + i) * 4 + lane / CHUNKS;
-    src[i] = row * p.q_tok_bytes + (((lane % CHUNKS) ^ dswz(row)) << 4);
+    const int row = (wave * kKLoads + i) * RPL + lane / CHUNKS;
+    src[i] = row * p.q_tok_bytes + (((lane % CHUNKS) ^ dswz<D>(row)) << 4);
   }
   // statistics: lanes 0..15 of waves 0 (nlse) and 1 (ndelta) fetch the 64
   // rows of the step, 16 bytes each; the other lanes read past the
@@ -584,7 +615,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkv_kernel(BwdParams p) {
       load_lds16(rstat, stt + buf * kStatBuf + wave * 1024, soff);
     }
   };
-  const TileAddr ta = tile_addr(lane);
+  const TileAddr<D> ta = tile_addr<D>(lane);
 
   f32x16 dka[D / 32], dva[D / 32];
 #pragma unroll
@@ -666,9 +697,9 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkv_kernel(BwdParams p) {
       for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
         for (int db = 0; db < D / 32; ++db) {
-          dva[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(read_tr(gl, ta, ks, db), pb[ks],
+          dva[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(read_tr<D>(gl, ta, ks, db), pb[ks],
                                                             dva[db], 0, 0, 0);
-          dka[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(read_tr(ql, ta, ks, db), dsb[ks],
+          dka[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(read_tr<D>(ql, ta, ks, db), dsb[ks],
                                                             dka[db], 0, 0, 0);
         }
     }
@@ -686,13 +717,14 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkv_kernel(BwdParams p) {
     store_part<D / 32>(base + kDkvPart / 2, dva, wave, lane);
     return;
   }
-  store_dkv<PUSH>(p, dka, true, my_key, it.be, it.kvg, hh);
-  store_dkv<PUSH>(p, dva, false, my_key, it.be, it.kvg, hh);
+  store_dkv<D, PUSH>(p, dka, true, my_key, it.be, it.kvg, hh);
+  store_dkv<D, PUSH>(p, dva, false, my_key, it.be, it.kvg, hh);
 }
 
 // The two halves of every dkv item: added in a fixed order, scaled, rounded.
-template <bool PUSH>
+template <int D, bool PUSH>
 __global__ __launch_bounds__(kThreads) void bwd_dkv_merge_kernel(BwdParams p) {
+  constexpr int kDkvPart = Geo<D>::kDkvPart;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int l32 = lane & 31, hh = lane >> 5;
   const KItem it = decode_k_item(p, blockIdx.x);
@@ -701,9 +733,9 @@ __global__ __launch_bounds__(kThreads) void bwd_dkv_merge_kernel(BwdParams p) {
   const float* u1 = u0 + kDkvPart;
   f32x16 acc[D / 32];
   add_parts<D / 32>(u0, u1, acc, wave, lane);
-  store_dkv<PUSH>(p, acc, true, my_key, it.be, it.kvg, hh);
+  store_dkv<D, PUSH>(p, acc, true, my_key, it.be, it.kvg, hh);
   add_parts<D / 32>(u0 + kDkvPart / 2, u1 + kDkvPart / 2, acc, wave, lane);
-  store_dkv<PUSH>(p, acc, false, my_key, it.be, it.kvg, hh);
+  store_dkv<D, PUSH>(p, acc, false, my_key, it.be, it.kvg, hh);
 }
 
 // Work layout for one call: statistics, split decisions, partial-sum bytes.
@@ -723,6 +755,7 @@ int64_t device_cus() {
   return (int64_t)cus;
 }
 
+template <int D>
 BwdPlan plan(const AttnBwdArgs& a) {
   BwdPlan pl;
   pl.s_pad = (a.s + 3) / 4 * 4;
@@ -742,44 +775,40 @@ BwdPlan plan(const AttnBwdArgs& a) {
   pl.kv_split = (a.causal && cus > 0 && pl.k_items < 2 * cus) ? 1 : 0;
   // the dq partials are consumed by their merge before the dkv kernel runs,
   // so both use the same region
-  const int64_t qpart = pl.q_split ? pl.q_items * 2 * kDqPart * 4 : 0;
-  const int64_t kpart = pl.kv_split ? pl.k_items * 2 * kDkvPart * 4 : 0;
+  const int64_t qpart = pl.q_split ? pl.q_items * 2 * Geo<D>::kDqPart * 4 : 0;
+  const int64_t kpart = pl.kv_split ? pl.k_items * 2 * Geo<D>::kDkvPart * 4 : 0;
   pl.part_offset = (2 * pl.stat_floats * 4 + 255) / 256 * 256;
   pl.part_bytes = qpart > kpart ? qpart : kpart;
   return pl;
 }
 
-}  // namespace
-
-int64_t attn_bwd_bf16_workspace_size(const AttnBwdArgs& a) {
-  const BwdPlan pl = plan(a);
-  return pl.part_bytes > 0 ? pl.part_offset + pl.part_bytes : 2 * pl.stat_floats * 4;
-}
-
-template <bool CAUSAL, bool PUSH>
+template <int D, bool CAUSAL, bool PUSH>
 void launch_kernels(const BwdParams& p, const BwdPlan& pl, unsigned q_grid, unsigned k_grid,
                     hipStream_t stream) {
-  hipLaunchKernelGGL((bwd_dq_kernel<CAUSAL, PUSH>), dim3(q_grid), dim3(kThreads), 0, stream, p);
+  hipLaunchKernelGGL((bwd_dq_kernel<D, CAUSAL, PUSH>), dim3(q_grid), dim3(kThreads), 0, stream,
+                     p);
   if (pl.q_split)
-    hipLaunchKernelGGL((bwd_dq_merge_kernel<CAUSAL, PUSH>), dim3((unsigned)pl.q_items),
+    hipLaunchKernelGGL((bwd_dq_merge_kernel<D, CAUSAL, PUSH>), dim3((unsigned)pl.q_items),
                        dim3(kThreads), 0, stream, p);
-  hipLaunchKernelGGL((bwd_dkv_kernel<CAUSAL, PUSH>), dim3(k_grid), dim3(kThreads), 0, stream, p);
+  hipLaunchKernelGGL((bwd_dkv_kernel<D, CAUSAL, PUSH>), dim3(k_grid), dim3(kThreads), 0, stream,
+                     p);
   if (pl.kv_split)
-    hipLaunchKernelGGL((bwd_dkv_merge_kernel<PUSH>), dim3((unsigned)pl.k_items), dim3(kThreads), 0,
-                       stream, p);
+    hipLaunchKernelGGL((bwd_dkv_merge_kernel<D, PUSH>), dim3((unsigned)pl.k_items),
+                       dim3(kThreads), 0, stream, p);
 }
 
-hipError_t launch_attn_bwd_bf16(const AttnBwdArgs& a, hipStream_t stream) {
-  if (a.d != D) return hipErrorInvalidValue;
-  const BwdPlan pl = plan(a);
+template <int D>
+hipError_t launch_d(const AttnBwdArgs& a, hipStream_t stream) {
+  constexpr int ROW = Geo<D>::ROW;
+  const BwdPlan pl = plan<D>(a);
   float* ndelta = static_cast<float*>(a.workspace);
   float* nlse = ndelta + pl.stat_floats;
   const int64_t rows = a.s * a.b * a.hp;
   if (rows <= 0) return hipSuccess;
   if (pl.q_items > 0x3FFFFFFF || pl.k_items > 0x3FFFFFFF) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(bwd_prep_kernel, dim3((unsigned)((rows * 16 + 255) / 256)), dim3(256), 0,
-                     stream, (const uint16_t*)a.o, (const uint16_t*)a.dout, a.lse, ndelta, nlse,
-                     (int)rows, (int)a.s, (int)pl.s_pad, (int)(a.b * a.hp),
+  hipLaunchKernelGGL(bwd_prep_kernel<D>, dim3((unsigned)((rows * (D / 8) + 255) / 256)),
+                     dim3(256), 0, stream, (const uint16_t*)a.o, (const uint16_t*)a.dout, a.lse,
+                     ndelta, nlse, (int)rows, (int)a.s, (int)pl.s_pad, (int)(a.b * a.hp),
                      (float)sqrt((double)D));
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
@@ -846,14 +875,31 @@ hipError_t launch_attn_bwd_bf16(const AttnBwdArgs& a, hipStream_t stream) {
   const unsigned q_grid = (unsigned)(pl.q_items << pl.q_split);
   const unsigned k_grid = (unsigned)(pl.k_items << pl.kv_split);
   if (a.causal && p.push)
-    launch_kernels<true, true>(p, pl, q_grid, k_grid, stream);
+    launch_kernels<D, true, true>(p, pl, q_grid, k_grid, stream);
   else if (a.causal)
-    launch_kernels<true, false>(p, pl, q_grid, k_grid, stream);
+    launch_kernels<D, true, false>(p, pl, q_grid, k_grid, stream);
   else if (p.push)
-    launch_kernels<false, true>(p, pl, q_grid, k_grid, stream);
+    launch_kernels<D, false, true>(p, pl, q_grid, k_grid, stream);
   else
-    launch_kernels<false, false>(p, pl, q_grid, k_grid, stream);
+    launch_kernels<D, false, false>(p, pl, q_grid, k_grid, stream);
   return hipGetLastError();
+}
+
+int64_t workspace_bytes(const BwdPlan& pl) {
+  return pl.part_bytes > 0 ? pl.part_offset + pl.part_bytes : 2 * pl.stat_floats * 4;
+}
+
+}  // namespace
+
+int64_t attn_bwd_bf16_workspace_size(const AttnBwdArgs& a) {
+  if (a.d == 64) return workspace_bytes(plan<64>(a));
+  return workspace_bytes(plan<128>(a));
+}
+
+hipError_t launch_attn_bwd_bf16(const AttnBwdArgs& a, hipStream_t stream) {
+  if (a.d == 128) return launch_d<128>(a, stream);
+  if (a.d == 64) return launch_d<64>(a, stream);
+  return hipErrorInvalidValue;
 }
 
 }  // namespace ulys
