@@ -43,9 +43,10 @@
 //    one tile that the sum passes 2^64 flag the wave, which then redoes its
 //    rows with the row max on every tile, reading K and V from global memory.
 //  * Work items are ordered longest-first (causal), which the dispatcher turns
-//    into a longest-processing-time-first schedule; with a workspace, causal
-//    shares with few items split every item's keys in two halves that a
-//    second kernel merges.
+//    into a longest-processing-time-first schedule (with the first round's
+//    order adapted to how it hands workgroups to shader engines, see
+//    first_round_unit); with a workspace, causal shares with few items split
+//    every item's keys in two halves that a second kernel merges.
 #include <math.h>
 
 #include "cdna4.h"
@@ -92,6 +93,7 @@ struct Params {
   int n_qblk;  // ceil(s / QB)
   int nsub;    // G / QH
   int nsplit;  // 1: one unit per item; 2: each item's key tiles split in two halves
+  int rev_units;  // workgroups below this index (the first round) run first_round_unit
   float* ws;   // nsplit == 2: partial states, PART_FLOATS per (item, half)
   int q_tok_bytes, kv_tok_bytes;  // bytes between consecutive tokens
   int q_bytes, kv_bytes;  // tensor sizes in bytes (bounds of the buffer resources)
@@ -213,6 +215,21 @@ __device__ __forceinline__ void store_output(const Params& p, const f32x16* oacc
         (m_run * p.c + __builtin_amdgcn_logf(l_tot)) * 0.69314718055994531f;
 }
 
+// Unit run by workgroup b.  The dispatcher sends workgroup b to XCD b % 8 and
+// hands each XCD's workgroups, in order, to its four shader engines in a fixed
+// rotation, each waiting for a free CU in its own engine.  Units are ranked
+// longest first, so in the first round (one workgroup per CU) each run of four
+// consecutive workgroups of an XCD would free its CUs in the reverse of the
+// rotation, and every second-round workgroup would wait for the last of the
+// four.  Reversing each such run (32 consecutive workgroups: 4 per XCD) in the
+// first round frees the CUs in rotation order; later rounds keep the ranked
+// order, so the longest remaining unit still goes to the first free CU.
+__device__ __forceinline__ int first_round_unit(int b, int rev_units) {
+  if (b >= rev_units) return b;
+  const int r = b & 31;
+  return (b & ~31) | ((3 - (r >> 3)) << 3) | (r & 7);
+}
+
 template <int D, bool CAUSAL, bool PUSH>
 __global__ __launch_bounds__(kThreads, 1) void attn_bf16_kernel(Params p) {
   using C = Cfg<D>;
@@ -226,7 +243,8 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bf16_kernel(Params p) {
   // Items are ranked longest first, so unit sizes never increase and the
   // dispatcher, which hands the next unit to the first CU that frees up,
   // schedules longest-processing-time first.
-  int rank = blockIdx.x;
+  const int unit = first_round_unit(blockIdx.x, p.rev_units);
+  int rank = unit;
   int half_id = 0;
   if (p.nsplit == 2) {
     half_id = rank & 1;
@@ -562,7 +580,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bf16_kernel(Params p) {
 
   if (p.nsplit == 2) {
     // partial state of this half, lanes contiguous: [wave][slot][lane]
-    float* part = p.ws + (int64_t)blockIdx.x * C::PART_FLOATS + wave * (C::PART_SLOTS * 64) + lane;
+    float* part = p.ws + (int64_t)unit * C::PART_FLOATS + wave * (C::PART_SLOTS * 64) + lane;
 #pragma unroll
     for (int db = 0; db < D / 32; ++db)
 #pragma unroll
@@ -684,6 +702,11 @@ hipError_t launch_d(const AttnArgs& a, hipStream_t stream) {
   const int64_t ws_need = attn_bf16_workspace_bytes(a);
   const int nsplit = (ws_need > 0 && a.workspace && a.workspace_bytes >= ws_need) ? 2 : 1;
   p.nsplit = nsplit;
+  {
+    // the first round: one workgroup per CU, whole runs of 32 only
+    const int64_t units = items * nsplit, slots = resident_slots();
+    p.rev_units = (int)((units < slots ? units : slots) & ~int64_t(31));
+  }
   p.ws = nsplit == 2 ? (float*)a.workspace : nullptr;
   const unsigned units = (unsigned)(items * nsplit);
   if (a.causal && p.push)

@@ -143,6 +143,7 @@ struct BwdParams {
   int kv_split;  // 1: every dkv item runs as two halves of its query steps
   int kv_units;  // dkv work units: items << kv_split
   int kv_xcd;    // 1: dkv units dispatched in the XCD-aware order (see xcd_unit)
+  int rev_q, rev_kv;  // dq / dkv workgroups below these run first_round_slot
   // push (non-zero): the gradient rows go to the shards of the head->seq
   // exchange instead of to dq, dk, dv (see store_t_push)
   int push, sl;
@@ -165,6 +166,20 @@ struct BwdParams {
 __device__ __forceinline__ int xcd_unit(int b, int n) {
   const int c = n >> 4, x = b & 7, j = b >> 3;
   return j < c ? x * c + j : (15 - x) * c + (j - c);
+}
+
+// Slot of workgroup b in the ranked order.  Within an XCD the dispatcher hands
+// workgroups, in order, to its four shader engines in a fixed rotation, each
+// waiting for a free CU in its own engine.  In the first round (one workgroup
+// per CU) a run of four consecutive workgroups of an XCD holds units ranked
+// longest first, which free their CUs in the reverse of the rotation, so every
+// second-round workgroup would wait for the last of the four.  Reversing each
+// run (32 consecutive workgroups: 4 per XCD, the XCD b % 8 unchanged) in the
+// first round frees the CUs in rotation order.
+__device__ __forceinline__ int first_round_slot(int b, int rev) {
+  if (b >= rev) return b;
+  const int r = b & 31;
+  return (b & ~31) | ((3 - (r >> 3)) << 3) | (r & 7);
 }
 
 // Transposed 32 x 32 accumulator (rows = features, column = lane % 32) scaled
@@ -353,7 +368,8 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dq_kernel(BwdParams p) {
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
   const int l32 = lane & 31, hh = lane >> 5;
-  int rank = blockIdx.x, half = 0;
+  const int unit = first_round_slot(blockIdx.x, p.rev_q);
+  int rank = unit, half = 0;
   if (p.q_split) {
     half = rank & 1;
     rank >>= 1;
@@ -490,7 +506,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dq_kernel(BwdParams p) {
     if (t + 1 < t_hi) dq_step(t + 1, std::integral_constant<int, 1>{});
   }
   if (p.q_split) {
-    store_part<D / 32>(p.part + (int64_t)blockIdx.x * Geo<D>::kDqPart, acc, wave, lane);
+    store_part<D / 32>(p.part + (int64_t)unit * Geo<D>::kDqPart, acc, wave, lane);
     return;
   }
   store_dq<D, PUSH>(p, acc, my_q, it.be, it.head, hh);
@@ -540,7 +556,8 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkv_kernel(BwdParams p) {
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
   const int l32 = lane & 31, hh = lane >> 5;
-  const int unit = p.kv_xcd ? xcd_unit(blockIdx.x, p.kv_units) : (int)blockIdx.x;
+  const int slot = first_round_slot(blockIdx.x, p.rev_kv);
+  const int unit = p.kv_xcd ? xcd_unit(slot, p.kv_units) : slot;
   int rank = unit, half = 0;
   if (p.kv_split) {
     half = rank & 1;
@@ -874,6 +891,12 @@ hipError_t launch_d(const AttnBwdArgs& a, hipStream_t stream) {
   p.kv_xcd = (a.causal && p.kv_units % 16 == 0) ? 1 : 0;
   const unsigned q_grid = (unsigned)(pl.q_items << pl.q_split);
   const unsigned k_grid = (unsigned)(pl.k_items << pl.kv_split);
+  {
+    // the first round: one workgroup per CU, whole runs of 32 only
+    const int64_t slots = device_cus();
+    p.rev_q = (int)(((int64_t)q_grid < slots ? (int64_t)q_grid : slots) & ~int64_t(31));
+    p.rev_kv = (int)(((int64_t)k_grid < slots ? (int64_t)k_grid : slots) & ~int64_t(31));
+  }
   if (a.causal && p.push)
     launch_kernels<D, true, true>(p, pl, q_grid, k_grid, stream);
   else if (a.causal)
