@@ -273,3 +273,24 @@ def test_workspace_split_matches_plain_32k():
     assert np.max(np.abs(l1.astype(np.float64) - l2)) <= 1e-4
     o3, l3 = gpu_attn(q, k, v, w.s, w.b, w.h, w.h_kv, w.d, w.P, True, w.dtype, ws=True)
     assert np.array_equal(o2, o3) and np.array_equal(l2, l3)  # deterministic
+
+
+# causal shares whose split units (two per item) fill part of one round of
+# workgroups (64, 144 units) or two rounds (512 units, GQA), so that the
+# first-round reordering of units covers whole runs, a partial tail and a
+# second round
+@pytest.mark.parametrize("s,b,h,h_kv,P", [(4096, 1, 16, 16, 8), (6144, 1, 24, 24, 8),
+                                          (8192, 2, 32, 8, 8)])
+def test_split_unit_rounds(s, b, h, h_kv, P):
+    d, hp, hkvp = 128, h // P, h_kv // P
+    print(f"case split rounds s={s} b={b} h={h} h_kv={h_kv} P={P}", flush=True)
+    q, k, v = share_inputs(21, s, b, hp, hkvp, d, "bf16")
+    o, lse = gpu_attn(q, k, v, s, b, h, h_kv, d, P, True, "bf16", ws=True)
+    rows = synth.row_sample(2107, s, b, hp, n_random=96, edge=16, tile_bounds=(64, 256))
+    o_ref, lse_ref = oracle.attn_rows(q, k, v, rows, s, b, h, h_kv, d, P, True)
+    err = np.max(np.abs(as_f64(o[rows[:, 2], rows[:, 0], rows[:, 1]]) - o_ref))
+    print(f"  {rows.shape[0]} rows, max err {err:.3e}", flush=True)
+    assert err <= TOL["bf16"]
+    lse_got = lse[rows[:, 0], rows[:, 1], rows[:, 2]].astype(np.float64)
+    assert np.max(np.abs(lse_got - lse_ref)) <= LSE_TOL["bf16"]
+    assert np.all(np.isfinite(as_f64(o))) and np.all(np.isfinite(lse))

@@ -212,3 +212,26 @@ def test_bwd_full_size_sampled(name):
     print(f"  |sum_j dv_j - sum_t dout_t| = {err:.3e} against sum_j |dv_j| = {scale:.3e}",
           flush=True)
     assert err <= 1e-2 * scale
+
+
+# causal shares whose split dQ and dK/dV units fill part of one round of
+# workgroups or two rounds (8192 x 2 GQA: 512 dQ units), so the first-round
+# reordering of units is exercised with whole runs, tails and a second round
+@pytest.mark.parametrize("s,b,h,h_kv,P", [(4096, 1, 16, 16, 8), (8192, 2, 32, 8, 8)])
+def test_bwd_split_unit_rounds(s, b, h, h_kv, P):
+    d, hp, hkvp = 128, h // P, h_kv // P
+    print(f"case bwd split rounds s={s} b={b} h={h} h_kv={h_kv} P={P}", flush=True)
+    q, k, v = share_inputs(23, s, b, hp, hkvp, d, "bf16")
+    dout = synth.tensor(2304, (s, b, hp, d), "bf16")
+    o, lse = gpu_fwd(q, k, v, s, b, h, h_kv, d, P, True)
+    dq, dk, dv = gpu_bwd(q, k, v, o, lse, dout, s, b, h, h_kv, d, P, True)
+    qrows = synth.row_sample(2307, s, b, hp, n_random=48, edge=8, tile_bounds=(32, 64))
+    n_keys = 12
+    js = s - 1 - np.arange(n_keys) * 5
+    krows = np.stack([np.arange(n_keys) % b, np.arange(n_keys) % hkvp, js], axis=1)
+    rq, rk, rv = oracle.attn_bwd_rows(q, k, v, dout, qrows, krows, s, b, h, h_kv, d, P, True)
+    check("dq rows", dq[qrows[:, 2], qrows[:, 0], qrows[:, 1]], rq)
+    check("dk keys", dk[krows[:, 2], krows[:, 0], krows[:, 1]], rk)
+    check("dv keys", dv[krows[:, 2], krows[:, 0], krows[:, 1]], rv)
+    for g in (dq, dk, dv):
+        assert np.all(np.isfinite(as_f64(g)))
