@@ -169,7 +169,7 @@ int ulys_attn_fwd(const void* q, const void* k, const void* v, void* o, float* l
                   int32_t causal, int32_t dtype, void* stream);
 
 /*
- * ulys_attn_fwd with a caller-owned workspace, used to balance causal work.
+ * ulys_attn_fwd with a caller-owned workspace, used to balance the work.
  * When a causal share has too few 128-query blocks to fill the GPU's resident
  * workgroups twice (e.g. s = 32768 with 2 heads), one block's keys would set
  * the run time; with a workspace of ulys_attn_fwd_workspace_size() bytes the
@@ -178,13 +178,17 @@ int ulys_attn_fwd(const void* q, const void* k, const void* v, void* o, float* l
  * second kernel merges the halves with the online-softmax rescaling
  * ([SPCP] Ring section: partial results over disjoint key ranges combine by
  * rescaling with the running max).  The result equals ulys_attn_fwd's up to
- * fp32 rounding order.
+ * fp32 rounding order.  When a share is four or more rounds of workgroups
+ * (e.g. s = 131072 with 4 heads), the workspace instead holds a counter from
+ * which every workgroup takes the next block, so that XCDs running at
+ * different clocks share the blocks by speed; the result is then identical
+ * to ulys_attn_fwd's.
  *
  *   workspace       : device pointer, 16-byte aligned, or NULL (then this call
  *                     is ulys_attn_fwd); must not overlap q, k, v, o or lse.
  *                     Contents on entry are ignored; on return undefined.
  *   workspace_bytes : its size; a smaller workspace than required disables the
- *                     split (still correct).
+ *                     split or the counter (still correct).
  * Errors: as ulys_attn_fwd, plus ULYS_ERR_DIM for workspace_bytes < 0,
  * ULYS_ERR_ALIGNMENT / ULYS_ERR_ALIAS for the workspace.  Calls that share one
  * workspace must be ordered (same stream).
@@ -196,7 +200,7 @@ int ulys_attn_fwd_ws(const void* q, const void* k, const void* v, void* o, float
 
 /*
  * Workspace bytes ulys_attn_fwd_ws uses for these arguments on the current
- * device (0 when it would not split).  Negative ULYS_ERR_* for arguments
+ * device: the split's partial states, 256 for the block counter, or 0.  Negative ULYS_ERR_* for arguments
  * ulys_attn_fwd would reject on size, divisibility or dtype grounds.
  */
 int64_t ulys_attn_fwd_workspace_size(int64_t s, int64_t b, int64_t h, int64_t h_kv, int64_t d_h,
@@ -371,7 +375,7 @@ const char* ulys_status_string(int status);
 /* ABI version of this header: (major << 16) | minor. */
 int ulys_abi_version(void);
 
-#define ULYS_ABI_VERSION ((1 << 16) | 9)
+#define ULYS_ABI_VERSION ((1 << 16) | 10)
 
 #ifdef __cplusplus
 }

@@ -36,7 +36,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_version(lib):
-    assert B.ulys_abi_version() == (1 << 16) | 9
+    assert B.ulys_abi_version() == (1 << 16) | 10
 
 
 def test_status_strings(lib):

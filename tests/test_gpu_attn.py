@@ -294,3 +294,20 @@ def test_split_unit_rounds(s, b, h, h_kv, P):
     lse_got = lse[rows[:, 0], rows[:, 1], rows[:, 2]].astype(np.float64)
     assert np.max(np.abs(lse_got - lse_ref)) <= LSE_TOL["bf16"]
     assert np.all(np.isfinite(as_f64(o))) and np.all(np.isfinite(lse))
+
+
+# shares of four or more rounds of workgroups (1024 and 2048 work items):
+# with a workspace every workgroup takes its unit from a counter, and the
+# result must be the plain call's, bit for bit (every unit computed once)
+@pytest.mark.parametrize("s,b,h,h_kv,P,causal", [(32768, 1, 64, 64, 8, True),
+                                                 (32768, 1, 64, 64, 8, False),
+                                                 (16384, 4, 64, 16, 8, True)])
+def test_workspace_counter_matches_plain(s, b, h, h_kv, P, causal):
+    d, code = 128, binding.ULYS_BF16
+    print(f"case counter s={s} b={b} h={h} h_kv={h_kv} P={P} causal={causal}", flush=True)
+    assert binding.ulys_attn_fwd_workspace_size(s, b, h, h_kv, d, P, int(causal), code) == 256
+    q, k, v = share_inputs(31, s, b, h // P, h_kv // P, d, "bf16")
+    o1, l1 = gpu_attn(q, k, v, s, b, h, h_kv, d, P, causal, "bf16", ws=False)
+    for _ in range(2):  # the counter is cleared by every call
+        o2, l2 = gpu_attn(q, k, v, s, b, h, h_kv, d, P, causal, "bf16", ws=True)
+        assert np.array_equal(o1, o2) and np.array_equal(l1, l2)

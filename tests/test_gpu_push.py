@@ -114,10 +114,12 @@ def test_layer_on_pushes(causal):
 
 # (s, b, h, h_kv, d, P, rank, causal): a wave's 32 rows inside one sequence
 # segment (sl = 64) and across segment boundaries (sl = 25, 40, 125), GQA,
-# d = 64, and the 32K share, whose workspace path splits every item
+# d = 64, the 32K share, whose workspace path splits every item, and a share
+# of 2048 items, whose workspace path hands out units from a counter
 ATTN_PUSH = [(256, 1, 8, 4, 128, 4, 1, True), (100, 2, 8, 8, 128, 4, 3, False),
              (320, 1, 16, 2, 64, 8, 5, True), (1000, 1, 8, 2, 128, 8, 0, True),
-             (1000, 2, 8, 8, 128, 8, 7, False), (32768, 1, 16, 16, 128, 8, 3, True)]
+             (1000, 2, 8, 8, 128, 8, 7, False), (32768, 1, 16, 16, 128, 8, 3, True),
+             (16384, 4, 64, 16, 128, 8, 5, True)]
 
 
 @pytest.mark.parametrize("ws", [False, True], ids=["plain", "ws"])

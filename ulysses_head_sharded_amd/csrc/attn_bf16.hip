@@ -45,8 +45,10 @@
 //  * Work items are ordered longest-first (causal), which the dispatcher turns
 //    into a longest-processing-time-first schedule (with the first round's
 //    order adapted to how it hands workgroups to shader engines, see
-//    first_round_unit); with a workspace, causal shares with few items split
-//    every item's keys in two halves that a second kernel merges.
+//    first_round_unit).  With a workspace, causal shares with few items split
+//    every item's keys in two halves that a second kernel merges, and shares
+//    of many rounds hand out units from a counter (see
+//    attn_bf16_workspace_bytes).
 #include <math.h>
 
 #include "cdna4.h"
@@ -94,6 +96,7 @@ struct Params {
   int nsub;    // G / QH
   int nsplit;  // 1: one unit per item; 2: each item's key tiles split in two halves
   int rev_units;  // workgroups below this index (the first round) run first_round_unit
+  unsigned* tickets;  // non-null: every workgroup takes its unit from this counter (zeroed first)
   float* ws;   // nsplit == 2: partial states, PART_FLOATS per (item, half)
   int q_tok_bytes, kv_tok_bytes;  // bytes between consecutive tokens
   int q_bytes, kv_bytes;  // tensor sizes in bytes (bounds of the buffer resources)
@@ -243,7 +246,20 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bf16_kernel(Params p) {
   // Items are ranked longest first, so unit sizes never increase and the
   // dispatcher, which hands the next unit to the first CU that frees up,
   // schedules longest-processing-time first.
-  const int unit = first_round_unit(blockIdx.x, p.rev_units);
+  int unit;
+  if (p.tickets) {
+    // the next unit in ranked order, whichever XCD this workgroup runs on;
+    // broadcast through the second V buffer, which the first step's loads
+    // write only after the prologue's barriers
+    int* slot = reinterpret_cast<int*>(lds + C::V_BASE + C::TILE_BYTES);
+    if (tid == 0)
+      *slot = (int)__hip_atomic_fetch_add(p.tickets, 1u, __ATOMIC_RELAXED,
+                                          __HIP_MEMORY_SCOPE_AGENT);
+    __syncthreads();
+    unit = __builtin_amdgcn_readfirstlane(*slot);
+  } else {
+    unit = first_round_unit(blockIdx.x, p.rev_units);
+  }
   int rank = unit;
   int half_id = 0;
   if (p.nsplit == 2) {
@@ -609,12 +625,20 @@ int64_t count_items(const AttnArgs& a) {
   return (a.s + QB - 1) / QB * a.b * a.hkvp * (G / QH);
 }
 
-// Bytes of workspace the split mode needs: causal work with too few items to
-// fill the resident slots twice (the longest item alone would set the run
-// time) is split into two halves per item.  0 when no split is used.
+// Bytes of workspace the call can use (0: none):
+//  * causal work with too few items to fill the resident slots twice (the
+//    longest item alone would set the run time) is split into two halves per
+//    item, whose partial states the workspace holds;
+//  * work of four or more rounds of workgroups takes its units from a counter
+//    in the workspace instead of from the workgroup index.  The dispatcher
+//    binds workgroup b to XCD b % 8, and the XCDs of one GPU run at somewhat
+//    different clocks, so a fixed mapping leaves the slowest XCD finishing
+//    last; with the counter each workgroup, wherever it starts, takes the
+//    longest unit left.
 int64_t attn_bf16_workspace_bytes(const AttnArgs& a) {
   const int64_t items = count_items(a);
   const int64_t slots = resident_slots();
+  if (slots > 0 && items >= 4 * slots) return 256;
   if (!a.causal || slots <= 0 || items >= 2 * slots) return 0;
   const int64_t part = (int64_t)kWaves * 64 * (a.d / 2 + 2) * 4;
   return items * 2 * part;
@@ -647,9 +671,15 @@ __global__ __launch_bounds__(kThreads) void attn_merge_kernel(Params p) {
   store_output<D, PUSH>(p, oacc, m, l, item.be, item.head, item.q0 + l32, hh);
 }
 
+__global__ void clear_tickets(unsigned* t) {
+  if (threadIdx.x == 0) __builtin_nontemporal_store(0u, t);
+}
+
+// The unit counter cleared first, then the attention; with a split, the merge.
 template <int D, bool CAUSAL, bool PUSH>
 void launch_kernels(const Params& p, unsigned units, unsigned items, int nsplit,
                     hipStream_t stream) {
+  if (p.tickets) hipLaunchKernelGGL(clear_tickets, dim3(1), dim3(64), 0, stream, p.tickets);
   hipLaunchKernelGGL((attn_bf16_kernel<D, CAUSAL, PUSH>), dim3(units), dim3(kThreads), 0, stream,
                      p);
   if (nsplit == 2)
@@ -698,10 +728,13 @@ hipError_t launch_d(const AttnArgs& a, hipStream_t stream) {
   const int64_t items = (int64_t)p.n_qblk * p.b * p.hkvp * p.nsub;
   if (items <= 0) return hipSuccess;
   if (items > 0x7FFFFFFF) return hipErrorInvalidValue;
-  // split halves (see attn_bf16_workspace_bytes) when the caller gave room
+  // split halves or the unit counter (see attn_bf16_workspace_bytes) when the
+  // caller gave room
   const int64_t ws_need = attn_bf16_workspace_bytes(a);
-  const int nsplit = (ws_need > 0 && a.workspace && a.workspace_bytes >= ws_need) ? 2 : 1;
+  const bool room = ws_need > 0 && a.workspace && a.workspace_bytes >= ws_need;
+  const int nsplit = (room && ws_need > 256) ? 2 : 1;
   p.nsplit = nsplit;
+  p.tickets = (room && ws_need == 256) ? static_cast<unsigned*>(a.workspace) : nullptr;
   {
     // the first round: one workgroup per CU, whole runs of 32 only
     const int64_t units = items * nsplit, slots = resident_slots();
