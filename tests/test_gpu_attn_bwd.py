@@ -235,3 +235,25 @@ def test_bwd_split_unit_rounds(s, b, h, h_kv, P):
     check("dv keys", dv[krows[:, 2], krows[:, 0], krows[:, 1]], rv)
     for g in (dq, dk, dv):
         assert np.all(np.isfinite(as_f64(g)))
+
+
+def test_bwd_counter_shape_repeats():
+    """A share whose dQ work is four or more rounds of workgroups (2048 items)
+    takes its dQ units from a counter that the prep kernel clears: two calls
+    in a row give the same bits, and sampled rows match the oracle."""
+    s, b, h, h_kv, d, P = 16384, 4, 64, 16, 128, 8
+    hp, hkvp = h // P, h_kv // P
+    q, k, v = share_inputs(24, s, b, hp, hkvp, d, "bf16")
+    dout = synth.tensor(2404, (s, b, hp, d), "bf16")
+    o, lse = gpu_fwd(q, k, v, s, b, h, h_kv, d, P, True)
+    first = gpu_bwd(q, k, v, o, lse, dout, s, b, h, h_kv, d, P, True)
+    second = gpu_bwd(q, k, v, o, lse, dout, s, b, h, h_kv, d, P, True)
+    for x, y in zip(first, second):
+        assert np.array_equal(x, y)
+    qrows = synth.row_sample(2407, s, b, hp, n_random=8, edge=2, tile_bounds=(64,))
+    krows = np.array([[0, 0, s - 1], [3, 1, s - 7]])
+    rq, rk, rv = oracle.attn_bwd_rows(q, k, v, dout, qrows, krows, s, b, h, h_kv, d, P, True)
+    dq, dk, dv = first
+    check("dq rows", dq[qrows[:, 2], qrows[:, 0], qrows[:, 1]], rq)
+    check("dk keys", dk[krows[:, 2], krows[:, 0], krows[:, 1]], rk)
+    check("dv keys", dv[krows[:, 2], krows[:, 0], krows[:, 1]], rv)

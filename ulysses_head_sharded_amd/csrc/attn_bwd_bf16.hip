@@ -97,11 +97,13 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(const uint16_t* __restric
                                                        const float* __restrict__ lse,
                                                        float* __restrict__ ndelta,
                                                        float* __restrict__ nlse, int rows,
-                                                       int s, int s_pad, int bhp, float sqrt_d) {
+                                                       int s, int s_pad, int bhp, float sqrt_d,
+                                                       unsigned* q_tickets) {
   constexpr int LPR = D / 8, SH = (D == 128) ? 4 : 3;  // lanes per row, log2
   static_assert(LPR == 1 << SH, "head size");
   const int gid = blockIdx.x * 256 + threadIdx.x;
   const int r = gid >> SH, part = gid & (LPR - 1);
+  if (q_tickets && gid == 0) __builtin_nontemporal_store(0u, q_tickets);  // for the dq kernel
   float acc = 0.f;
   if (r < rows) {
     const u32x4 a = *reinterpret_cast<const u32x4*>(o + (int64_t)r * D + part * 8);
@@ -144,6 +146,7 @@ struct BwdParams {
   int kv_units;  // dkv work units: items << kv_split
   int kv_xcd;    // 1: dkv units dispatched in the XCD-aware order (see xcd_unit)
   int rev_q, rev_kv;  // dq / dkv workgroups below these run first_round_slot
+  unsigned* q_tickets;  // non-null: dq workgroups take their units from this counter
   // push (non-zero): the gradient rows go to the shards of the head->seq
   // exchange instead of to dq, dk, dv (see store_t_push)
   int push, sl;
@@ -368,7 +371,20 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dq_kernel(BwdParams p) {
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
   const int l32 = lane & 31, hh = lane >> 5;
-  const int unit = first_round_slot(blockIdx.x, p.rev_q);
+  int unit;
+  if (p.q_tickets) {
+    // the next unit in ranked order, whichever XCD this workgroup runs on;
+    // broadcast through K buffer 1, which the first step's loads write only
+    // after the prologue's barrier
+    int* slot = reinterpret_cast<int*>(lds + kTile);
+    if (threadIdx.x == 0)
+      *slot = (int)__hip_atomic_fetch_add(p.q_tickets, 1u, __ATOMIC_RELAXED,
+                                          __HIP_MEMORY_SCOPE_AGENT);
+    __syncthreads();
+    unit = __builtin_amdgcn_readfirstlane(*slot);
+  } else {
+    unit = first_round_slot(blockIdx.x, p.rev_q);
+  }
   int rank = unit, half = 0;
   if (p.q_split) {
     half = rank & 1;
@@ -762,6 +778,8 @@ struct BwdPlan {
   int64_t q_items, k_items;
   int q_split, kv_split;
   int64_t part_offset, part_bytes;  // in the workspace
+  int q_tickets;                    // 1: dq units from a counter at ticket_offset
+  int64_t ticket_offset;
 };
 
 int64_t device_cus() {
@@ -796,6 +814,11 @@ BwdPlan plan(const AttnBwdArgs& a) {
   const int64_t kpart = pl.kv_split ? pl.k_items * 2 * Geo<D>::kDkvPart * 4 : 0;
   pl.part_offset = (2 * pl.stat_floats * 4 + 255) / 256 * 256;
   pl.part_bytes = qpart > kpart ? qpart : kpart;
+  // dq work of four or more rounds takes its units from a counter (cleared by
+  // the prep kernel), so that XCDs running at different clocks share them by
+  // speed; the dkv units keep their XCD-aware order, which the L2 needs
+  pl.q_tickets = (cus > 0 && pl.q_items >= 4 * cus) ? 1 : 0;
+  pl.ticket_offset = pl.part_offset + pl.part_bytes;
   return pl;
 }
 
@@ -820,13 +843,17 @@ hipError_t launch_d(const AttnBwdArgs& a, hipStream_t stream) {
   const BwdPlan pl = plan<D>(a);
   float* ndelta = static_cast<float*>(a.workspace);
   float* nlse = ndelta + pl.stat_floats;
+  unsigned* q_tickets =
+      pl.q_tickets ? reinterpret_cast<unsigned*>(static_cast<uint8_t*>(a.workspace) +
+                                                 pl.ticket_offset)
+                   : nullptr;
   const int64_t rows = a.s * a.b * a.hp;
   if (rows <= 0) return hipSuccess;
   if (pl.q_items > 0x3FFFFFFF || pl.k_items > 0x3FFFFFFF) return hipErrorInvalidValue;
   hipLaunchKernelGGL(bwd_prep_kernel<D>, dim3((unsigned)((rows * (D / 8) + 255) / 256)),
                      dim3(256), 0, stream, (const uint16_t*)a.o, (const uint16_t*)a.dout, a.lse,
                      ndelta, nlse, (int)rows, (int)a.s, (int)pl.s_pad, (int)(a.b * a.hp),
-                     (float)sqrt((double)D));
+                     (float)sqrt((double)D), q_tickets);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
 
@@ -897,6 +924,7 @@ hipError_t launch_d(const AttnBwdArgs& a, hipStream_t stream) {
     p.rev_q = (int)(((int64_t)q_grid < slots ? (int64_t)q_grid : slots) & ~int64_t(31));
     p.rev_kv = (int)(((int64_t)k_grid < slots ? (int64_t)k_grid : slots) & ~int64_t(31));
   }
+  p.q_tickets = q_tickets;
   if (a.causal && p.push)
     launch_kernels<D, true, true>(p, pl, q_grid, k_grid, stream);
   else if (a.causal)
@@ -909,6 +937,7 @@ hipError_t launch_d(const AttnBwdArgs& a, hipStream_t stream) {
 }
 
 int64_t workspace_bytes(const BwdPlan& pl) {
+  if (pl.q_tickets) return pl.ticket_offset + 256;
   return pl.part_bytes > 0 ? pl.part_offset + pl.part_bytes : 2 * pl.stat_floats * 4;
 }
 
