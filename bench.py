@@ -490,8 +490,8 @@ def main():
     dst_ptrs = [t.data_ptr() for t in dst]
 
     def step(record: bool):
-        if record:
-            e = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+        if record:  # the fused step has no unpack call to bracket
+            e = [torch.cuda.Event(enable_timing=True) for _ in range(3 if fused else 4)]
             e[0].record(stream)
         # Q, K and V packed by one call (K and V replicated when h_kv < P)
         call(binding.ulys_pack_seq2head_qkv(xq.data_ptr(), xk.data_ptr(), xv.data_ptr(),
@@ -515,11 +515,12 @@ def main():
             call(binding.ulys_unpack_head2seq(o.data_ptr(), xo.data_ptr(), w.s, w.b, w.h, w.d,
                                               w.P, code, sh), "unpack o")
         if record:
-            e[3].record(stream)
+            if not fused:
+                e[3].record(stream)
+                ev["unpack1"].append(e[3])
             ev["pack0"].append(e[0])
             ev["pack1"].append(e[1])
             ev["attn1"].append(e[2])
-            ev["unpack1"].append(e[3])
 
     for _ in range(args.warmup):
         step(False)
@@ -533,7 +534,8 @@ def main():
 
     pack_ms = float(np.mean([a.elapsed_time(b) for a, b in zip(ev["pack0"], ev["pack1"])]))
     attn_ms = float(np.mean([a.elapsed_time(b) for a, b in zip(ev["pack1"], ev["attn1"])]))
-    unpack_ms = float(np.mean([a.elapsed_time(b) for a, b in zip(ev["attn1"], ev["unpack1"])]))
+    unpack_ms = (0.0 if fused else
+                 float(np.mean([a.elapsed_time(b) for a, b in zip(ev["attn1"], ev["unpack1"])])))
 
     flops = w.attn_flops()
     attn_tflops = flops / (attn_ms * 1e-3) / 1e12
