@@ -299,12 +299,13 @@ def test_split_unit_rounds(s, b, h, h_kv, P):
 # shares of four or more rounds of workgroups (1024 and 2048 work items):
 # with a workspace every workgroup takes its unit from a counter, and the
 # result must be the plain call's, bit for bit (every unit computed once)
-@pytest.mark.parametrize("s,b,h,h_kv,P,causal", [(32768, 1, 64, 64, 8, True),
-                                                 (32768, 1, 64, 64, 8, False),
-                                                 (16384, 4, 64, 16, 8, True)])
-def test_workspace_counter_matches_plain(s, b, h, h_kv, P, causal):
-    d, code = 128, binding.ULYS_BF16
-    print(f"case counter s={s} b={b} h={h} h_kv={h_kv} P={P} causal={causal}", flush=True)
+@pytest.mark.parametrize("s,b,h,h_kv,d,P,causal", [(32768, 1, 64, 64, 128, 8, True),
+                                                   (32768, 1, 64, 64, 128, 8, False),
+                                                   (16384, 4, 64, 16, 128, 8, True),
+                                                   (32768, 1, 64, 64, 64, 8, True)])
+def test_workspace_counter_matches_plain(s, b, h, h_kv, d, P, causal):
+    code = binding.ULYS_BF16
+    print(f"case counter s={s} b={b} h={h} h_kv={h_kv} d={d} P={P} causal={causal}", flush=True)
     assert binding.ulys_attn_fwd_workspace_size(s, b, h, h_kv, d, P, int(causal), code) == 256
     q, k, v = share_inputs(31, s, b, h // P, h_kv // P, d, "bf16")
     o1, l1 = gpu_attn(q, k, v, s, b, h, h_kv, d, P, causal, "bf16", ws=False)
