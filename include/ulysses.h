@@ -227,8 +227,11 @@ int64_t ulys_attn_fwd_workspace_size(int64_t s, int64_t b, int64_t h, int64_t h_
  *   lse        : [b, hp, s] fp32 (required)
  *   dq         : [s, b, hp, d_h]   dk, dv : [s, b, hkvp, d_h]   (dtype of q)
  *   workspace  : device, 16-byte aligned, at least
- *                ulys_attn_bwd_workspace_size() bytes (per-row statistics);
- *                contents ignored on entry, undefined on return.
+ *                ulys_attn_bwd_workspace_size() bytes (per-row statistics;
+ *                partial sums when a causal share is split; on shares of
+ *                four or more rounds of dQ work, a counter from which the dQ
+ *                workgroups take their blocks); contents ignored on entry,
+ *                undefined on return.
  * Gradients are accumulated in fp32 and rounded once (nearest-even).  No
  * atomics: the result does not depend on scheduling.
  * Supported: ULYS_BF16 with d_h in {64, 128}.
