@@ -312,3 +312,30 @@ def test_workspace_counter_matches_plain(s, b, h, h_kv, d, P, causal):
     for _ in range(2):  # the counter is cleared by every call
         o2, l2 = gpu_attn(q, k, v, s, b, h, h_kv, d, P, causal, "bf16", ws=True)
         assert np.array_equal(o1, o2) and np.array_equal(l1, l2)
+
+
+def test_workspace_counter_two_streams():
+    """Two long-share calls in flight at once on two streams, each with its own
+    workspace (and so its own unit counter), give the plain calls' results."""
+    s, b, h, h_kv, d, P = 32768, 1, 64, 64, 128, 8
+    hp, hkvp, code = h // P, h_kv // P, binding.ULYS_BF16
+    nbytes = binding.ulys_attn_fwd_workspace_size(s, b, h, h_kv, d, P, 1, code)
+    assert nbytes == 256
+    dev()
+    ins = [tuple(to_dev(x) for x in share_inputs(41 + i, s, b, hp, hkvp, d, "bf16"))
+           for i in range(2)]
+    plain = [binding.attn_fwd(q, k, v, P=P, causal=True)[0] for q, k, v in ins]
+    torch.cuda.synchronize()
+    streams = [torch.cuda.Stream() for _ in range(2)]
+    outs = [torch.empty_like(ins[i][0]) for i in range(2)]
+    wss = [torch.empty(nbytes, dtype=torch.uint8, device="cuda") for _ in range(2)]
+    for _ in range(3):
+        for i in range(2):
+            q, k, v = ins[i]
+            rc = binding.ulys_attn_fwd_ws(q.data_ptr(), k.data_ptr(), v.data_ptr(),
+                                          outs[i].data_ptr(), None, s, b, h, h_kv, d, P, 1, code,
+                                          wss[i].data_ptr(), nbytes, streams[i].cuda_stream)
+            assert rc == 0, binding.ulys_status_string(rc)
+        torch.cuda.synchronize()
+        for i in range(2):
+            assert torch.equal(outs[i], plain[i])
