@@ -170,7 +170,8 @@ int ulys_attn_fwd(const void* q, const void* k, const void* v, void* o, float* l
 
 /*
  * ulys_attn_fwd with a caller-owned workspace, used to balance the work.
- * When a causal share has too few 128-query blocks to fill the GPU's resident
+ * When a causal share has too few query blocks (256 queries of one head, or
+ * fewer queries of several heads of one GQA group) to fill the GPU's resident
  * workgroups twice (e.g. s = 32768 with 2 heads), one block's keys would set
  * the run time; with a workspace of ulys_attn_fwd_workspace_size() bytes the
  * keys of every block are split into two halves computed by separate
@@ -181,8 +182,9 @@ int ulys_attn_fwd(const void* q, const void* k, const void* v, void* o, float* l
  * fp32 rounding order.  When a share is four or more rounds of workgroups
  * (e.g. s = 131072 with 4 heads), the workspace instead holds a counter from
  * which every workgroup takes the next block, so that XCDs running at
- * different clocks share the blocks by speed; the result is then identical
- * to ulys_attn_fwd's.
+ * different clocks share the blocks by speed (one atomic add per workgroup,
+ * on the counter only; every block is still computed by the same code), so
+ * the result is then identical to ulys_attn_fwd's, bit for bit.
  *
  *   workspace       : device pointer, 16-byte aligned, or NULL (then this call
  *                     is ulys_attn_fwd); must not overlap q, k, v, o or lse.
@@ -233,7 +235,13 @@ int64_t ulys_attn_fwd_workspace_size(int64_t s, int64_t b, int64_t h, int64_t h_
  *                workgroups take their blocks); contents ignored on entry,
  *                undefined on return.
  * Gradients are accumulated in fp32 and rounded once (nearest-even).  No
- * atomics: the result does not depend on scheduling.
+ * gradient is accumulated with atomics: every output element is summed by
+ * one workgroup in a fixed order (split halves are added by a merge kernel in
+ * a fixed order), so the result does not depend on scheduling.  The only
+ * atomic is the dQ kernel's unit counter on long shares: each workgroup takes
+ * the index of the next query block from it, and that block is then computed
+ * by the same code whichever workgroup runs it, so the values are the same
+ * bit for bit as with the static block order.
  * Supported: ULYS_BF16 with d_h in {64, 128}.
  * Errors: as ulys_attn_fwd, plus ULYS_ERR_NULL for any missing pointer
  * (lse and workspace included), ULYS_ERR_UNSUPPORTED for another dtype or

@@ -201,6 +201,27 @@ def _stream(stream):
     return _torch().cuda.current_stream().cuda_stream
 
 
+def _hold(stream, *tensors) -> None:
+    """Tensors allocated here on torch's current stream but used by kernels
+    enqueued on another stream: tell the caching allocator, so that it does not
+    hand their memory to a new allocation before that stream's work is done
+    (a workspace dropped on return would otherwise be reusable while the
+    kernels still read and write it)."""
+    if stream is None:
+        return
+    torch = _torch()
+    live = [t for t in tensors if t is not None]
+    if not live:
+        return
+    handle = int(stream)
+    if handle == torch.cuda.current_stream(live[0].device).cuda_stream:
+        return
+    other = (torch.cuda.default_stream(live[0].device) if handle == 0 else
+             torch.cuda.ExternalStream(handle, device=live[0].device))
+    for t in live:
+        t.record_stream(other)
+
+
 def _check(rc: int, what: str) -> None:
     if rc != ULYS_OK:
         raise UlyssesError(rc, what)
@@ -215,6 +236,7 @@ def pack_seq2head(x, P: int, out=None, stream=None):
         out = _torch().empty((P, sl, b, h // P, d), dtype=x.dtype, device=x.device)
     _check(ulys_pack_seq2head(x.data_ptr(), out.data_ptr(), sl * P, b, h, d, P,
                               dtype_code(x), _stream(stream)), "ulys_pack_seq2head")
+    _hold(stream, out)
     return out
 
 
@@ -225,6 +247,7 @@ def unpack_head2seq(y, out=None, stream=None):
         out = _torch().empty((sl, b, hp * P, d), dtype=y.dtype, device=y.device)
     _check(ulys_unpack_head2seq(y.data_ptr(), out.data_ptr(), sl * P, b, hp * P, d, P,
                                 dtype_code(y), _stream(stream)), "ulys_unpack_head2seq")
+    _hold(stream, out)
     return out
 
 
@@ -242,6 +265,7 @@ def pack_seq2head_kv(x, P: int, out=None, stream=None):
                              device=x.device)
     _check(ulys_pack_seq2head_kv(x.data_ptr(), out.data_ptr(), sl * P, b, h_kv, d, P,
                                  dtype_code(x), _stream(stream)), "ulys_pack_seq2head_kv")
+    _hold(stream, out)
     return out
 
 
@@ -253,6 +277,7 @@ def unpack_head2seq_kv(y, h_kv: int, out=None, stream=None):
         out = _torch().empty((sl, b, h_kv, d), dtype=y.dtype, device=y.device)
     _check(ulys_unpack_head2seq_kv(y.data_ptr(), out.data_ptr(), sl * P, b, h_kv, d, P,
                                    dtype_code(y), _stream(stream)), "ulys_unpack_head2seq_kv")
+    _hold(stream, out)
     return out
 
 
@@ -282,6 +307,7 @@ def attn_fwd(q, k, v, P: int = 1, causal: bool = False, out=None, lse=False, str
                           s, b, h, h_kv, d, P, int(bool(causal)), code,
                           ws.data_ptr() if ws is not None else None, ws_bytes, _stream(stream))
     _check(rc, "ulys_attn_fwd_ws")
+    _hold(stream, ws, out, lse_t)
     return out, lse_t
 
 
@@ -302,6 +328,7 @@ def attn_bwd(q, k, v, o, dout, lse, P: int = 1, causal: bool = False, stream=Non
                        lse.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), s, b, h, h_kv,
                        d, P, int(bool(causal)), code, ws.data_ptr(), ws_bytes, _stream(stream))
     _check(rc, "ulys_attn_bwd")
+    _hold(stream, ws, dq, dk, dv)
     return dq, dk, dv
 
 
@@ -318,4 +345,5 @@ def attn_merge(o_a, lse_a, o_b, lse_b, out=None, lse_out=None, stream=None):
     _check(ulys_attn_merge(o_a.data_ptr(), lse_a.data_ptr(), o_b.data_ptr(), lse_b.data_ptr(),
                            out.data_ptr(), lse_out.data_ptr(), s, b, hp, d, dtype_code(o_a),
                            _stream(stream)), "ulys_attn_merge")
+    _hold(stream, out, lse_out)
     return out, lse_out

@@ -12,7 +12,11 @@
 // dk and dv summed over the query heads of each GQA group (contiguous
 // groups, as in the forward).
 //
-// Kernels, no atomics (the result does not depend on scheduling):
+// Kernels.  No gradient is accumulated with atomics: every output element is
+// summed by one workgroup in a fixed order, so the result does not depend on
+// scheduling.  The one atomic is the dq kernel's unit counter on long shares
+// (each workgroup takes the index of its query block from it; the block is
+// computed by the same code wherever it runs):
 //  * prep: -D and -lse * sqrt(d_h) per query row, into the caller's
 //    workspace (the dkv kernel starts its dP and S accumulators from them,
 //    so that exp2(c S) is P and dP - D comes out of the MFMA);
