@@ -88,14 +88,37 @@ def test_tiny_workload_parity():
     assert np.max(np.abs(lse - lse_ref)) <= LSE_TOL[w.dtype]
 
 
-# full-size workloads: sampled rows (the oracle computes them one by one)
+# full-size workloads: sampled rows (the oracle computes them one by one) plus,
+# where the oracle can afford it, every row of whole work units: the first, a
+# middle and the last query block of the listed local query heads (a work unit
+# is 8 waves x 32 queries spread over the query heads of one KV group, so the
+# GQA share lists all four heads of its group)
 FULL = {
-    "gpt1.2b-32k": dict(n_random=256, edge=32),
-    "mha-128k": dict(n_random=48, edge=16),
-    "gqa-64k": dict(n_random=64, edge=16),
-    "mtok-1m": dict(n_random=12, edge=6),
-    "dit-256k": dict(n_random=6, edge=4),
+    "gpt1.2b-32k": dict(n_random=256, edge=32, unit_heads=(0, 1)),
+    "mha-128k": dict(n_random=48, edge=16, unit_heads=(0, 3)),
+    "gqa-64k": dict(n_random=64, edge=16, unit_heads=(0, 1, 2, 3)),
+    "mtok-1m": dict(n_random=12, edge=6, unit_heads=()),
+    "dit-256k": dict(n_random=6, edge=4, unit_heads=()),
 }
+
+
+def full_rows(name):
+    """The sampled rows of a full-size share and the rows of its whole units."""
+    w = WORKLOADS[name]
+    spec = dict(FULL[name])
+    heads = spec.pop("unit_heads")
+    rows = synth.row_sample(100 * w.c + 7, w.s, w.b, w.hp, tile_bounds=(64, 128), **spec)
+    if heads:
+        G = w.hp // w.hkvp
+        qh = 8 if G % 8 == 0 else 4 if G % 4 == 0 else 2 if G % 2 == 0 else 1
+        qb = 32 * (8 // qh)
+        nblk = (w.s + qb - 1) // qb
+        ts = np.concatenate([np.arange(k * qb, min(w.s, (k + 1) * qb))
+                             for k in sorted({0, nblk // 2, nblk - 1})])
+        units = np.array([(be, i, t) for be in range(w.b) for i in heads for t in ts],
+                         dtype=np.int64)
+        rows = np.unique(np.concatenate([rows, units], axis=0), axis=0)
+    return rows
 
 
 @pytest.mark.parametrize("name", list(FULL))
@@ -106,8 +129,7 @@ def test_full_size_sampled_parity(name):
     # the workspace entry point, as the bench calls it (it splits only where
     # the causal work would otherwise be unbalanced, e.g. the 32K share)
     o, lse = gpu_attn(q, k, v, w.s, w.b, w.h, w.h_kv, w.d, w.P, w.causal, w.dtype, ws=True)
-    rows = synth.row_sample(100 * w.c + 7, w.s, w.b, w.hp, tile_bounds=(64, 128),
-                            **FULL[name])
+    rows = full_rows(name)
     o_ref, lse_ref = oracle.attn_rows(q, k, v, rows, w.s, w.b, w.h, w.h_kv, w.d, w.P,
                                       w.causal)
     got = as_f64(o[rows[:, 2], rows[:, 0], rows[:, 1]])
@@ -147,8 +169,7 @@ def test_full_size_sampled_parity_push(name):
                                     torch.cuda.current_stream().cuda_stream)
     assert rc == 0, binding.ulys_status_string(rc)
     torch.cuda.synchronize()
-    rows = synth.row_sample(100 * w.c + 7, w.s, w.b, w.hp, tile_bounds=(64, 128),
-                            **FULL[name])
+    rows = full_rows(name)
     o_ref, lse_ref = oracle.attn_rows(q, k, v, rows, w.s, w.b, w.h, w.h_kv, w.d, w.P,
                                       w.causal)
     # row (be, i, t) of the share sits in shard t // sl, token t % sl, head rank*hp + i
@@ -324,7 +345,13 @@ def test_workspace_counter_two_streams():
     dev()
     ins = [tuple(to_dev(x) for x in share_inputs(41 + i, s, b, hp, hkvp, d, "bf16"))
            for i in range(2)]
-    plain = [binding.attn_fwd(q, k, v, P=P, causal=True)[0] for q, k, v in ins]
+    # the reference: ulys_attn_fwd, no workspace and so no counter
+    plain = [torch.empty_like(q) for q, _, _ in ins]
+    for (q, k, v), o in zip(ins, plain):
+        rc = binding.ulys_attn_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), None,
+                                   s, b, h, h_kv, d, P, 1, code,
+                                   torch.cuda.current_stream().cuda_stream)
+        assert rc == 0, binding.ulys_status_string(rc)
     torch.cuda.synchronize()
     streams = [torch.cuda.Stream() for _ in range(2)]
     outs = [torch.empty_like(ins[i][0]) for i in range(2)]
@@ -339,3 +366,31 @@ def test_workspace_counter_two_streams():
         torch.cuda.synchronize()
         for i in range(2):
             assert torch.equal(outs[i], plain[i])
+
+
+def test_helper_on_a_side_stream():
+    """The binding's tensor helpers run on the stream they are given; the
+    workspace and outputs they allocate stay reserved for that stream, and the
+    results equal the ones on torch's current stream (a long share, so the
+    forward's workspace holds the unit counter and the backward's the dQ
+    counter)."""
+    s, b, h, h_kv, d, P = 32768, 1, 64, 64, 128, 8
+    dev()
+    q, k, v = (to_dev(x) for x in share_inputs(51, s, b, h // P, h_kv // P, d, "bf16"))
+    g = to_dev(synth.tensor(5104, (s, b, h // P, d), "bf16"))
+    o_ref, l_ref = binding.attn_fwd(q, k, v, P=P, causal=True, lse=True)
+    grads_ref = binding.attn_bwd(q, k, v, o_ref, g, l_ref, P=P, causal=True)
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    for _ in range(2):
+        o, lse = binding.attn_fwd(q, k, v, P=P, causal=True, lse=True, stream=side.cuda_stream)
+        grads = binding.attn_bwd(q, k, v, o, g, lse, P=P, causal=True, stream=side.cuda_stream)
+        # allocations on the current stream meanwhile must not take the
+        # side stream's workspace
+        junk = [torch.full((1 << 20,), 7, dtype=torch.uint8, device="cuda") for _ in range(8)]
+        side.synchronize()
+        assert torch.equal(o, o_ref) and torch.equal(lse, l_ref)
+        for x, y in zip(grads, grads_ref):
+            assert torch.equal(x, y)
+        del junk

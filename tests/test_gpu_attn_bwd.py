@@ -219,22 +219,37 @@ def test_bwd_full_size_sampled(name):
 # reordering of units is exercised with whole runs, tails and a second round
 @pytest.mark.parametrize("s,b,h,h_kv,P", [(4096, 1, 16, 16, 8), (8192, 2, 32, 8, 8)])
 def test_bwd_split_unit_rounds(s, b, h, h_kv, P):
+    """At s = 4096 (the 32K share's heads and split, one eighth of its length)
+    every element of dq, dk and dv is compared with the oracle.  At s = 8192
+    (GQA 4:1, b = 2) sampled query rows, late keys and early and middle keys
+    (j = 0, s/4, s/2, 3s/4 - 1: keys that every later query row sees, so
+    their gradients sum the longest runs of query tiles and both split
+    halves)."""
     d, hp, hkvp = 128, h // P, h_kv // P
     print(f"case bwd split rounds s={s} b={b} h={h} h_kv={h_kv} P={P}", flush=True)
     q, k, v = share_inputs(23, s, b, hp, hkvp, d, "bf16")
     dout = synth.tensor(2304, (s, b, hp, d), "bf16")
     o, lse = gpu_fwd(q, k, v, s, b, h, h_kv, d, P, True)
     dq, dk, dv = gpu_bwd(q, k, v, o, lse, dout, s, b, h, h_kv, d, P, True)
+    for g in (dq, dk, dv):
+        assert np.all(np.isfinite(as_f64(g)))
+    if s <= 4096:
+        rq, rk, rv = oracle.attn_bwd(q, k, v, dout, s, b, h, h_kv, d, P, True)
+        check("dq", dq, rq)
+        check("dk", dk, rk)
+        check("dv", dv, rv)
+        return
     qrows = synth.row_sample(2307, s, b, hp, n_random=48, edge=8, tile_bounds=(32, 64))
     n_keys = 12
     js = s - 1 - np.arange(n_keys) * 5
-    krows = np.stack([np.arange(n_keys) % b, np.arange(n_keys) % hkvp, js], axis=1)
+    late = np.stack([np.arange(n_keys) % b, np.arange(n_keys) % hkvp, js], axis=1)
+    early = np.array([(0, 0, 0), (b - 1, hkvp - 1, 0), (0, 0, s // 4),
+                      (b - 1, hkvp - 1, s // 2), (0, 0, 3 * s // 4 - 1)], dtype=np.int64)
+    krows = np.concatenate([early, late], axis=0)
     rq, rk, rv = oracle.attn_bwd_rows(q, k, v, dout, qrows, krows, s, b, h, h_kv, d, P, True)
     check("dq rows", dq[qrows[:, 2], qrows[:, 0], qrows[:, 1]], rq)
     check("dk keys", dk[krows[:, 2], krows[:, 0], krows[:, 1]], rk)
     check("dv keys", dv[krows[:, 2], krows[:, 0], krows[:, 1]], rv)
-    for g in (dq, dk, dv):
-        assert np.all(np.isfinite(as_f64(g)))
 
 
 def test_bwd_counter_shape_repeats():
@@ -257,3 +272,32 @@ def test_bwd_counter_shape_repeats():
     check("dq rows", dq[qrows[:, 2], qrows[:, 0], qrows[:, 1]], rq)
     check("dk keys", dk[krows[:, 2], krows[:, 0], krows[:, 1]], rk)
     check("dv keys", dv[krows[:, 2], krows[:, 0], krows[:, 1]], rv)
+
+
+def test_bwd_counter_matches_batch_slices():
+    """The dQ counter path against calls without it: a b = 4 share whose dQ
+    work is 2048 items (units from the counter) and the same share cut into
+    four b = 1 calls (512 items each: no counter, no split).  Every dQ unit
+    is computed by the same code whichever workgroup takes it, so dq must be
+    equal bit for bit in every element -- a unit skipped or run twice would
+    show.  dk and dv of the b = 1 calls run their key blocks as split halves
+    (too few items to fill the GPU twice), a different summation order, so
+    they are compared to a bf16 ulp of their scale.  Every gradient finite."""
+    s, b, h, h_kv, d, P = 16384, 4, 64, 16, 128, 8
+    hp, hkvp = h // P, h_kv // P
+    q, k, v = share_inputs(25, s, b, hp, hkvp, d, "bf16")
+    dout = synth.tensor(2504, (s, b, hp, d), "bf16")
+    o, lse = gpu_fwd(q, k, v, s, b, h, h_kv, d, P, True)
+    dq, dk, dv = gpu_bwd(q, k, v, o, lse, dout, s, b, h, h_kv, d, P, True)
+    for g in (dq, dk, dv):
+        assert np.all(np.isfinite(as_f64(g)))
+    for be in range(b):
+        sl = slice(be, be + 1)
+        one = gpu_bwd(*(np.ascontiguousarray(x[:, sl]) for x in (q, k, v, o)),
+                      np.ascontiguousarray(lse[sl]), np.ascontiguousarray(dout[:, sl]),
+                      s, 1, h, h_kv, d, P, True)
+        assert np.array_equal(dq[:, sl], one[0]), f"dq of batch entry {be}"
+        for name, full, part in (("dk", dk, one[1]), ("dv", dv, one[2])):
+            a, c = as_f64(full[:, sl]), as_f64(part)
+            err = np.max(np.abs(a - c))
+            assert err <= 2 ** -7 * max(1.0, np.max(np.abs(c))), (name, be, err)
