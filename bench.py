@@ -11,9 +11,20 @@ its epilogue; the destinations are P buffers on this GPU); fp32 runs the
 attention and then the unpack.  The pack and unpack kernels are also timed
 alone, streaming from HBM (layout_hbm).
 
+Before any timed step the GPU runs untimed steps until its clock has
+settled (a minimum wall time, then two consecutive runs of steps agreeing
+to 1%), whatever --warmup says: the board lowers its clock under sustained
+matrix-core load within the first seconds, so a few warm-up steps would time
+a clock that is still falling.
+
+The headline workload is the 128K MHA share (the largest share the
+throughput targets bind); the 32K GPT share and the 64K GQA share are timed
+the same way and reported as sub-records under "configs".
+
 Prints ONE JSON line.  ``value`` is attention FLOPs per step over the whole
 step time (TFLOP/s); per-kernel durations come from HIP events recorded on
-the stream the kernels run on, inside the timed region.
+the stream the kernels run on, inside the timed region (mean, median and min
+over the timed steps).
 """
 from __future__ import annotations
 
@@ -37,11 +48,15 @@ PROFILE_DIR = os.path.join(ROOT, "profiles")
 def parse_args():
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
-    # the 32k share's step is under a millisecond: a few hundred warm-up steps
-    # let the GPU clock settle before the timed ones
-    ap.add_argument("--steps", type=int, default=500)
-    ap.add_argument("--warmup", type=int, default=200)
-    ap.add_argument("--workload", default="gpt1.2b-32k")
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="mha-128k")
+    ap.add_argument("--also", default="gpt1.2b-32k,gqa-64k",
+                    help="comma-separated workloads timed after the headline one and reported "
+                         "under 'configs' ('' for none)")
+    ap.add_argument("--settle-seconds", type=float, default=2.0,
+                    help="minimum wall time of untimed steps before any timed ones")
+    ap.add_argument("--settle-max-seconds", type=float, default=12.0)
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="wall-time budget of the oracle's cpu_baseline sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -141,9 +156,59 @@ def cpu_baseline(w, q, k, v, budget_s: float):
         rows_done += t.size
     return {
         "value": flops / t_used / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
-        "sample": f"{rows_done} uniformly drawn query rows of the {w.name} share "
-                  f"(fp64 oracle, {t_used:.1f} s wall, algorithmic flops of the sample)",
+        "cpu_model": cpu_model(),
+        "sample": f"{rows_done} uniformly drawn query rows of the {w.name} share the GPU "
+                  f"attends over (fp64 oracle, {t_used:.1f} s wall, algorithmic flops of the "
+                  f"sample)",
     }
+
+
+def cpu_model() -> str:
+    """The host CPU's model name, from /proc/cpuinfo."""
+    try:
+        with open("/proc/cpuinfo", encoding="utf-8") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def settle(torch, run, min_s: float, max_s: float, tol: float = 0.01):
+    """Untimed steps until the GPU clock has settled: runs of steps lasting
+    about a quarter of a second each, for at least min_s seconds and until two
+    consecutive runs agree on the time per step to within tol (at most max_s
+    seconds).  run(n) enqueues n steps.  Returns (seconds spent, steps run,
+    ms per step of the last run)."""
+    t_start = time.perf_counter()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    run(1)
+    torch.cuda.synchronize()
+    per = max(time.perf_counter() - t0, 1e-5)
+    steps, prev = 1, None
+    while True:
+        n = max(1, int(0.25 / per))
+        t0 = time.perf_counter()
+        run(n)
+        torch.cuda.synchronize()
+        per = (time.perf_counter() - t0) / n
+        steps += n
+        spent = time.perf_counter() - t_start
+        if spent >= max_s:
+            break
+        if prev is not None and spent >= min_s and abs(per - prev) <= tol * prev:
+            break
+        prev = per
+    return spent, steps, per * 1e3
+
+
+def stats_ms(xs):
+    """mean, median and min of per-step event windows (ms)."""
+    import numpy as np
+    a = np.asarray(xs, dtype=np.float64)
+    return {"mean": float(a.mean()), "median": float(np.median(a)), "min": float(a.min())}
 
 
 def bench_merge(args, w, binding, torch, np, o, code, stream):
@@ -393,15 +458,18 @@ def bench_backward(args, w, binding, torch, np, q, k, v, code, stream):
             e[3].record(stream)
             marks.append(e)
 
-    for _ in range(max(3, args.bwd_steps // 5)):
-        step(False)
+    settle_s, _, _ = settle(torch, lambda n: [step(False) for _ in range(n)],
+                            args.settle_seconds, args.settle_max_seconds)
+    # the timed steps: at most about two seconds of them
+    per_ms = max(1e-3, settle_probe_ms(torch, step))
+    n_steps = max(5, min(args.bwd_steps, int(2000.0 / per_ms)))
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for _ in range(args.bwd_steps):
+    for _ in range(n_steps):
         step(True)
     torch.cuda.synchronize()
-    ms_step = (time.perf_counter() - t0) * 1e3 / args.bwd_steps
-    attn_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in marks]))
+    ms_step = (time.perf_counter() - t0) * 1e3 / n_steps
+    attn = stats_ms([e[1].elapsed_time(e[2]) for e in marks])
     layout_ms = float(np.mean([e[0].elapsed_time(e[1]) + e[2].elapsed_time(e[3]) for e in marks]))
     flops = w.attn_bwd_flops()
     if fused:  # the pack of dO only; the gradients' exchange is in the backward's epilogues
@@ -413,36 +481,37 @@ def bench_backward(args, w, binding, torch, np, q, k, v, code, stream):
         layout_bytes = w.layout_bytes()  # pack dO + unpack dQ as pack Q + unpack O; dK, dV as K, V
         layout = {"pack_do_unpack_dqkv_us": round(layout_ms * 1e3, 2),
                   "gbps": round(layout_bytes / (layout_ms * 1e-3) / 1e9, 1), "bytes": layout_bytes}
+    tfl = flops / (attn["mean"] * 1e-3) / 1e12
     return {
-        "steps": args.bwd_steps, "ms_per_step": round(ms_step, 4),
+        "steps": n_steps, "settle_s": round(settle_s, 2), "ms_per_step": round(ms_step, 4),
         "tflops_step": round(flops / (ms_step * 1e-3) / 1e12, 2),
-        "attn_bwd": {"ms": round(attn_ms, 4), "tflops": round(flops / (attn_ms * 1e-3) / 1e12, 2),
-                     "frac_peak": round(flops / (attn_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+        "attn_bwd": {"ms": round(attn["mean"], 4), "ms_median": round(attn["median"], 4),
+                     "ms_min": round(attn["min"], 4), "tflops": round(tfl, 2),
+                     "frac_peak": round(tfl / PEAK_BF16_TFLOPS, 4),
                      "flops": flops, "flops_rule": "10 d b hp pairs (five products)",
                      "workspace_bytes": int(nbytes)},
         "layout": layout,
     }
 
 
-def main():
-    args = parse_args()
-    if args.copy_calibration:
-        copy_calibration()
-        return
-    if args.gpus != 1:
-        print(f"bench.py measures one rank's share on ONE GPU; --gpus {args.gpus} is not "
-              "supported (the all-to-all across GPUs is not implemented here)",
-              file=sys.stderr)
-        sys.exit(2)
+def settle_probe_ms(torch, step) -> float:
+    """Wall time of one more untimed step (ms), to size the timed run."""
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    step(False)
+    torch.cuda.synchronize()
+    return (time.perf_counter() - t0) * 1e3
 
+
+def run_workload(args, w, headline: bool):
+    """Times the forward step (and, for bf16, the backward step) of one share.
+    Returns the record (the headline's carries the extra measurements) and the
+    device tensors of the share the attention consumed."""
     import numpy as np
     import torch
 
     from ulysses_head_sharded_amd import binding, synth
-    from ulysses_head_sharded_amd.workloads import WORKLOADS
 
-    binding.load()
-    w = WORKLOADS[args.workload]
     dev = torch.device("cuda:0")
     tdt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
     sl, hp, hkvp = w.s // w.P, w.hp, w.hkvp
@@ -463,6 +532,7 @@ def main():
             else:
                 a[...] = val
     xq, xk, xv = upload(xq_h), upload(xk_h), upload(xv_h)
+    del xq_h, xk_h, xv_h
     yq = torch.empty((w.P, sl, w.b, hp, w.d), dtype=tdt, device=dev)
     yk = torch.empty((w.P, sl, w.b, hkvp, w.d), dtype=tdt, device=dev)
     yv = torch.empty((w.P, sl, w.b, hkvp, w.d), dtype=tdt, device=dev)
@@ -524,6 +594,8 @@ def main():
 
     for _ in range(args.warmup):
         step(False)
+    settle_s, settle_steps, settle_ms = settle(torch, lambda n: [step(False) for _ in range(n)],
+                                               args.settle_seconds, args.settle_max_seconds)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for _ in range(args.steps):
@@ -532,10 +604,11 @@ def main():
     t1 = time.perf_counter()
     ms_step = (t1 - t0) * 1e3 / args.steps
 
-    pack_ms = float(np.mean([a.elapsed_time(b) for a, b in zip(ev["pack0"], ev["pack1"])]))
-    attn_ms = float(np.mean([a.elapsed_time(b) for a, b in zip(ev["pack1"], ev["attn1"])]))
+    pack = stats_ms([a.elapsed_time(b) for a, b in zip(ev["pack0"], ev["pack1"])])
+    attn = stats_ms([a.elapsed_time(b) for a, b in zip(ev["pack1"], ev["attn1"])])
     unpack_ms = (0.0 if fused else
                  float(np.mean([a.elapsed_time(b) for a, b in zip(ev["attn1"], ev["unpack1"])])))
+    pack_ms, attn_ms = pack["mean"], attn["mean"]
 
     flops = w.attn_flops()
     attn_tflops = flops / (attn_ms * 1e-3) / 1e12
@@ -544,7 +617,9 @@ def main():
     unpack_bytes = 2 * w.shard_bytes()
     pack_gbps = pack_bytes / (pack_ms * 1e-3) / 1e9
     if fused:  # the O exchange is inside the attention call
-        layout = {"pack_qkv_us": round(pack_ms * 1e3, 2), "pack_gbps": round(pack_gbps, 1),
+        layout = {"pack_qkv_us": round(pack_ms * 1e3, 2),
+                  "pack_qkv_us_median": round(pack["median"] * 1e3, 2),
+                  "pack_qkv_us_min": round(pack["min"] * 1e3, 2), "pack_gbps": round(pack_gbps, 1),
                   "frac_hbm_peak": round(pack_gbps / PEAK_HBM_GBPS, 4), "bytes": pack_bytes,
                   "o_exchange": "in the attention epilogue (ulys_attn_fwd_push)"}
     else:
@@ -557,24 +632,16 @@ def main():
                   "bytes": pack_bytes + unpack_bytes}
     kernel_src = os.path.join(ROOT, "ulysses_head_sharded_amd", "csrc",
                               "attn_bf16.hip" if w.dtype == "bf16" else "attn_f32.hip")
-
     rec = {
-        "metric": METRIC,
-        "value": round(flops / (ms_step * 1e-3) / 1e12, 3),
-        "unit": "TFLOP/s",
-        "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
         "ms_per_step": round(ms_step, 4),
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": w.dtype,
-        "data": ("synthetic (seeded N(0,1), SplitMix64 + Box-Muller)" if args.inputs == "normal"
-                 else "constant tensors (diagnostic, not the workload)"),
+        "value": round(flops / (ms_step * 1e-3) / 1e12, 3),
+        "settle": {"seconds": round(settle_s, 2), "steps": settle_steps,
+                   "last_ms_per_step": round(settle_ms, 4)},
         "config": {"workload": w.name, "P": w.P, "s": w.s, "b": w.b, "h": w.h, "h_kv": w.h_kv,
                    "d_h": w.d, "causal": w.causal, "share": f"[{w.s},{w.b},{hp},{w.d}]"},
-        "attn": {"ms": round(attn_ms, 4), "tflops": round(attn_tflops, 2),
+        "attn": {"ms": round(attn_ms, 4), "ms_median": round(attn["median"], 4),
+                 "ms_min": round(attn["min"], 4), "tflops": round(attn_tflops, 2),
+                 "tflops_at_median": round(flops / (attn["median"] * 1e-3) / 1e12, 2),
                  "frac_peak": round(attn_tflops / peak, 4), "flops": flops,
                  "workspace_bytes": int(ws_bytes)},
         "layout": layout,
@@ -584,24 +651,81 @@ def main():
     }
     if args.layout_calls > 0:
         rec["layout_hbm"] = bench_layout_hbm(args, w, binding, torch, tdt, code, stream)
-    if fused:  # o itself, the merge's input, is filled by a plain call
-        call(binding.ulys_attn_fwd_ws(yq.data_ptr(), yk.data_ptr(), yv.data_ptr(), o.data_ptr(),
-                                      None, w.s, w.b, w.h, w.h_kv, w.d, w.P, int(w.causal), code,
-                                      ws.data_ptr(), ws_bytes, sh), "attn")
-    if args.merge_steps > 0:
-        rec["merge"] = bench_merge(args, w, binding, torch, np, o, code, stream)
-    if args.push_steps > 0:
-        rec["exchange_push"] = bench_push(args, w, binding, torch, np, xq, tdt, code, stream)
-    if args.push_attn_calls > 0 and w.dtype == "bf16":
-        rec["attn_push"] = bench_attn_push(args, w, binding, torch, yq, yk, yv, o, xo, tdt, code,
-                                           ws, ws_bytes, stream)
+    if headline:
+        if fused:  # o itself, the merge's input, is filled by a plain call
+            call(binding.ulys_attn_fwd_ws(yq.data_ptr(), yk.data_ptr(), yv.data_ptr(),
+                                          o.data_ptr(), None, w.s, w.b, w.h, w.h_kv, w.d, w.P,
+                                          int(w.causal), code, ws.data_ptr(), ws_bytes, sh),
+                 "attn")
+        if args.merge_steps > 0:
+            rec["merge"] = bench_merge(args, w, binding, torch, np, o, code, stream)
+        if args.push_steps > 0:
+            rec["exchange_push"] = bench_push(args, w, binding, torch, np, xq, tdt, code, stream)
+        if args.push_attn_calls > 0 and w.dtype == "bf16":
+            rec["attn_push"] = bench_attn_push(args, w, binding, torch, yq, yk, yv, o, xo, tdt,
+                                               code, ws, ws_bytes, stream)
     if args.bwd_steps > 0 and w.dtype == "bf16":
         rec["backward"] = bench_backward(args, w, binding, torch, np, yq, yk, yv, code, stream)
+    torch.cuda.synchronize()
+    return rec, (yq, yk, yv)
+
+
+def main():
+    args = parse_args()
+    if args.copy_calibration:
+        copy_calibration()
+        return
+    if args.gpus != 1:
+        print(f"bench.py measures one rank's share on ONE GPU; --gpus {args.gpus} is not "
+              "supported (the all-to-all across GPUs is not implemented here)",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    from ulysses_head_sharded_amd import binding
+    from ulysses_head_sharded_amd.workloads import WORKLOADS
+
+    binding.load()
+    w = WORKLOADS[args.workload]
+    others = [WORKLOADS[n] for n in args.also.split(",") if n and n != w.name]
+    head, share = run_workload(args, w, headline=True)
+    rec = {
+        "metric": METRIC,
+        "value": head.pop("value"),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": head.pop("ms_per_step"),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": ("synthetic (seeded N(0,1), SplitMix64 + Box-Muller)" if args.inputs == "normal"
+                 else "constant tensors (diagnostic, not the workload)"),
+    }
+    rec.update(head)
     if not args.no_cpu_baseline:
-        # the oracle gets its own seeded share-shaped inputs (same distribution)
-        q_h = synth.tensor(100 * w.c + 1, (w.s, w.b, hp, w.d), w.dtype)
-        k_h = synth.tensor(100 * w.c + 2, (w.s, w.b, hkvp, w.d), w.dtype)
-        v_h = synth.tensor(100 * w.c + 3, (w.s, w.b, hkvp, w.d), w.dtype)
+        # the oracle on the very share the GPU attended over (the packed send
+        # buffers [P, s/P, b, hp, d] are the share [s, b, hp, d])
+        def host(t):
+            t = t.contiguous().view(w.s, w.b, -1, w.d)
+            if t.dtype == torch.bfloat16:
+                return t.view(torch.int16).cpu().numpy().view(np.uint16)
+            return t.cpu().numpy()
+        q_h, k_h, v_h = (host(t) for t in share)
+    del share
+    torch.cuda.empty_cache()
+    if others:
+        rec["configs"] = {}
+        for o_w in others:
+            sub, sub_share = run_workload(args, o_w, headline=False)
+            del sub_share
+            torch.cuda.empty_cache()
+            rec["configs"][o_w.name] = sub
+    if not args.no_cpu_baseline:
         rec["cpu_baseline"] = cpu_baseline(w, q_h, k_h, v_h, args.cpu_seconds)
     print(json.dumps(rec), flush=True)
 
