@@ -200,6 +200,31 @@ int ulys_attn_fwd_ws(const void* q, const void* k, const void* v, void* o, float
                      int32_t causal, int32_t dtype, void* workspace, int64_t workspace_bytes,
                      void* stream);
 
+/* Size of the fixed device scratch of ulys_attn_fwd_noalloc, in bytes. */
+#define ULYS_NOALLOC_SCRATCH_BYTES (96LL << 20)
+
+/*
+ * ulys_attn_fwd_ws without caller memory, for callers that cannot allocate
+ * device memory (work captured into a HIP graph, tight serving loops,
+ * harnesses that forbid hipMalloc): the same kernels and results, bit for
+ * bit, as ulys_attn_fwd_ws with a workspace of
+ * ulys_attn_fwd_workspace_size() bytes, the workspace being a fixed array of
+ * ULYS_NOALLOC_SCRATCH_BYTES (96 MiB) in the library's device memory.  Each
+ * GPU the call runs on holds its own array from the first call on it until
+ * the process ends; the call allocates nothing.
+ *   Arguments, layouts and errors as ulys_attn_fwd, plus ULYS_ERR_DIM when the
+ *   workspace the call would use exceeds the array (a causal share with too
+ *   few blocks to fill the GPU twice, whose split partial states need more
+ *   than 96 MiB; e.g. s = 51200 with 2 heads of 128), ULYS_ERR_HIP when the
+ *   array's device address cannot be resolved.
+ * Every call on one GPU uses that GPU's one array: calls that overlap in time
+ * on one GPU (two streams, two host threads) race on it and give undefined
+ * results; calls ordered on one stream are safe.
+ */
+int ulys_attn_fwd_noalloc(const void* q, const void* k, const void* v, void* o, float* lse,
+                          int64_t s, int64_t b, int64_t h, int64_t h_kv, int64_t d_h, int32_t P,
+                          int32_t causal, int32_t dtype, void* stream);
+
 /*
  * Workspace bytes ulys_attn_fwd_ws uses for these arguments on the current
  * device: the split's partial states, 256 for the block counter, or 0.  Negative ULYS_ERR_* for arguments
@@ -386,7 +411,7 @@ const char* ulys_status_string(int status);
 /* ABI version of this header: (major << 16) | minor. */
 int ulys_abi_version(void);
 
-#define ULYS_ABI_VERSION ((1 << 16) | 10)
+#define ULYS_ABI_VERSION ((1 << 16) | 11)
 
 #ifdef __cplusplus
 }

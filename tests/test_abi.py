@@ -36,7 +36,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_version(lib):
-    assert B.ulys_abi_version() == (1 << 16) | 10
+    assert B.ulys_abi_version() == (1 << 16) | 11
 
 
 def test_status_strings(lib):
@@ -74,7 +74,7 @@ def test_layout_rejects(lib, fn, args, expect):
 Q, K, V, O, L = (0x7F0000000000 + i * (1 << 32) for i in range(5))
 
 
-@pytest.mark.parametrize("args,expect", [
+ATTN_REJECTS = [
     ((None, K, V, O, L, 64, 1, 8, 8, 128, 4, 1, B.ULYS_BF16), B.ULYS_ERR_NULL),
     ((Q, K, V, None, L, 64, 1, 8, 8, 128, 4, 1, B.ULYS_BF16), B.ULYS_ERR_NULL),
     ((Q, K, V, O, L, 0, 1, 8, 8, 128, 4, 1, B.ULYS_BF16), B.ULYS_ERR_DIM),
@@ -90,9 +90,19 @@ Q, K, V, O, L = (0x7F0000000000 + i * (1 << 32) for i in range(5))
     ((Q, K, V, V, None, 64, 1, 8, 8, 128, 4, 1, B.ULYS_BF16), B.ULYS_ERR_ALIAS),
     ((Q, K, V, O, O + 64, 64, 1, 8, 8, 128, 4, 1, B.ULYS_BF16), B.ULYS_ERR_ALIAS),
     ((Q, K, V, O, K, 64, 1, 8, 8, 128, 4, 1, B.ULYS_BF16), B.ULYS_ERR_ALIAS),
-])
+]
+
+
+@pytest.mark.parametrize("args,expect", ATTN_REJECTS)
 def test_attn_rejects(lib, args, expect):
     assert B.ulys_attn_fwd(*args) == expect
+
+
+@pytest.mark.parametrize("args,expect", ATTN_REJECTS)
+def test_attn_noalloc_rejects(lib, args, expect):
+    """The allocation-free forward validates its arguments as ulys_attn_fwd
+    does, before it resolves its scratch or launches anything."""
+    assert B.ulys_attn_fwd_noalloc(*args) == expect
 
 
 def test_tensor_helper_raises_status(lib):

@@ -24,7 +24,7 @@ EXPORTED = ("ulys_pack_seq2head", "ulys_unpack_head2seq", "ulys_pack_seq2head_kv
             "ulys_unpack_head2seq_kv", "ulys_pack_seq2head_qkv", "ulys_attn_fwd", "ulys_attn_fwd_ws",
             "ulys_attn_fwd_workspace_size", "ulys_attn_bwd", "ulys_attn_bwd_workspace_size",
             "ulys_attn_merge", "ulys_seq2head_push", "ulys_head2seq_push", "ulys_attn_fwd_push",
-            "ulys_attn_bwd_push",
+            "ulys_attn_bwd_push", "ulys_attn_fwd_noalloc",
             "ulys_status_string", "ulys_abi_version")
 
 _lib = None
@@ -62,6 +62,9 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.ulys_attn_fwd_ws.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i32, i32, i32,
                                      vp, i64, vp]
     lib.ulys_attn_fwd_ws.restype = ctypes.c_int
+    lib.ulys_attn_fwd_noalloc.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i32, i32,
+                                          i32, vp]
+    lib.ulys_attn_fwd_noalloc.restype = ctypes.c_int
     lib.ulys_attn_fwd_workspace_size.argtypes = [i64, i64, i64, i64, i64, i32, i32, i32]
     lib.ulys_attn_fwd_workspace_size.restype = ctypes.c_int64
     lib.ulys_attn_bwd.argtypes = [vp] * 9 + [i64] * 5 + [i32] * 3 + [vp, i64, vp]
@@ -121,6 +124,12 @@ def ulys_attn_fwd_ws(q, k, v, o, lse, s, b, h, h_kv, d_h, P, causal, dtype, work
                      workspace_bytes, stream=None) -> int:
     return load().ulys_attn_fwd_ws(q, k, v, o, lse, s, b, h, h_kv, d_h, P, causal, dtype,
                                    workspace, workspace_bytes, stream)
+
+
+def ulys_attn_fwd_noalloc(q, k, v, o, lse, s, b, h, h_kv, d_h, P, causal, dtype,
+                          stream=None) -> int:
+    return load().ulys_attn_fwd_noalloc(q, k, v, o, lse, s, b, h, h_kv, d_h, P, causal, dtype,
+                                        stream)
 
 
 def ulys_attn_fwd_workspace_size(s, b, h, h_kv, d_h, P, causal, dtype) -> int:
