@@ -77,6 +77,23 @@ def test_small_shapes_bit_exact(s, b, h, d, P, elt):
     assert same_bits(z, x)
 
 
+# shapes whose pack takes the LDS-staged tile transpose (runs of at most 256
+# bytes, input rows of at least 8 KiB, at least as many token rows as ranks):
+# 256-byte runs over 32 and 64 ranks, 128-byte runs over 64 ranks; the unpack
+# of the same shapes takes the output-order walk
+LDS_TILE = [(1024, 1, 32, 128, 32, 2), (2048, 2, 64, 64, 64, 4), (4096, 1, 64, 64, 64, 2),
+            (8192, 3, 64, 128, 64, 2)]
+
+
+@pytest.mark.parametrize("s,b,h,d,P,elt", LDS_TILE)
+def test_lds_tile_shapes_bit_exact(s, b, h, d, P, elt):
+    print(f"case lds tile s={s} b={b} h={h} d={d} P={P} elt={elt}", flush=True)
+    x = bits(9500 + s + h + d + b + elt, (s // P, b, h, d), elt)
+    y, z = run_pack_unpack(x, s, b, h, d, P, elt)
+    assert same_bits(y, oracle.pack(x, s, b, h, d, P))
+    assert same_bits(z, x)
+
+
 def test_unpack_alone_matches_oracle():
     s, b, h, d, P, elt = 48, 2, 12, 16, 4, 2
     y_host = bits(4242, (P, s // P, b, h // P, d), elt)

@@ -8,13 +8,18 @@
 //   pack   in [sl*b][P] runs  -> out [P][sl*b] runs
 //   unpack in [P][sl*b] runs  -> out [sl*b][P] runs
 // Every run is >= 256 bytes in the target workloads, so each 16-byte lane
-// access is already fully coalesced on both sides; staging through LDS would
-// add a round trip without removing any HBM transaction.  Threads walk the
-// OUTPUT in order (consecutive lanes -> consecutive 16-byte vectors), one
-// vector per thread with non-temporal loads and stores: on MI355X that
-// streams at the rate of a plain device copy (measured ~5.9 TB/s from HBM at
-// 128 MiB), while keeping several vectors per thread in flight was slower
-// (4 per thread: ~4.9 TB/s).
+// access is already fully coalesced on both sides.  Threads walk the OUTPUT
+// in order (consecutive lanes -> consecutive 16-byte vectors), one vector per
+// thread with non-temporal loads and stores: on MI355X that streams at the
+// rate of a plain device copy (~5.9 TB/s from HBM at 128 MiB), while keeping
+// several vectors per thread in flight was slower (4 per thread: ~4.9 TB/s).
+// An LDS-staged tile transpose (transpose_runs_lds: a workgroup reads a tile
+// of input rows into LDS and writes it out as contiguous output segments) was
+// measured against it from HBM: 13-16% slower for the 128 MiB shards with
+// 1 KiB runs and 22% slower for 256-byte runs over 8 ranks, but 11% faster
+// for the pack of 256-byte runs over 64 ranks, where the output-order walk
+// reads 256 bytes out of every 16 KiB input row; it serves that case (runs
+// of at most 256 bytes, input rows of at least 8 KiB, the pack direction).
 #include "internal.h"
 
 namespace ulys {
@@ -53,6 +58,35 @@ __global__ __launch_bounds__(kThreads) void transpose_runs32(
   }
 }
 
+// LDS-staged variant of the same map: a workgroup moves a tile of TR input
+// rows x TC input columns of runs.  It reads the tile's TR row segments (TC*V
+// contiguous vectors each) into LDS in input order, then writes the TC output
+// row segments (TR*V contiguous vectors each) from LDS in output order.
+//   in [R][Cc] runs -> out [Cc][R] runs, V vectors per run;
+//   R % TR == 0, Cc % TC == 0, TR*TC*V <= kLdsTile, R*Cc*V < 2^31 (host checks).
+constexpr int kLdsTile = 1024;  // vectors: 16 KiB of LDS per workgroup
+__global__ __launch_bounds__(kThreads) void transpose_runs_lds(
+    const u32x4* __restrict__ in, u32x4* __restrict__ out, uint32_t R, uint32_t Cc, uint32_t V,
+    uint32_t TR, uint32_t TC, FastDiv tiles_c, FastDiv seg_in, FastDiv seg_out) {
+  __shared__ u32x4 tile[kLdsTile];
+  const uint32_t tr = fast_div(blockIdx.x, tiles_c);
+  const uint32_t tc = blockIdx.x - tr * tiles_c.div;
+  const uint32_t r0 = tr * TR, c0 = tc * TC;
+  const uint32_t n = TR * TC * V;
+  for (uint32_t e = threadIdx.x; e < n; e += kThreads) {
+    const uint32_t i = fast_div(e, seg_in);  // input row r0 + i
+    const uint32_t w = e - i * seg_in.div;   // vector within its TC runs
+    tile[e] = __builtin_nontemporal_load(&in[((r0 + i) * Cc + c0) * V + w]);
+  }
+  __syncthreads();
+  for (uint32_t e = threadIdx.x; e < n; e += kThreads) {
+    const uint32_t j = fast_div(e, seg_out);  // output row c0 + j
+    const uint32_t w = e - j * seg_out.div;   // vector within its TR runs
+    const uint32_t i = w / V, c = w - i * V;
+    __builtin_nontemporal_store(tile[(i * TC + j) * V + c], &out[((c0 + j) * R + r0) * V + w]);
+  }
+}
+
 // Same map with 64-bit indices, for grids of 2^32 vectors or more.
 template <typename Vec>
 __global__ __launch_bounds__(kThreads) void transpose_runs64(
@@ -66,10 +100,36 @@ __global__ __launch_bounds__(kThreads) void transpose_runs64(
   }
 }
 
+// The tile of transpose_runs_lds for an [A][B] grid of runs of vpr 16-byte
+// vectors, or false where the output-order walk is the faster kernel (see the
+// file comment).  The walk reads one input run out of every B-run input row
+// before it moves to the next row, and comes back B times: with runs of at
+// most 256 bytes and rows of at least 8 KiB that reopens every row B times.
+// The LDS tile serves that case in the pack direction (at least as many rows
+// as columns; the unpack's few rows are read as that many sequential
+// streams), with whole 8 x TC tiles.
+bool lds_tile(uint64_t A, uint64_t B, uint64_t vpr, uint64_t* TR, uint64_t* TC) {
+  if (vpr > 16 || B * vpr * 16 < 8192 || A < B || A * B * vpr >= (1ull << 31)) return false;
+  *TR = 8;
+  *TC = 8;
+  while (*TR * *TC * vpr > (uint64_t)kLdsTile && *TC > 1) *TC >>= 1;
+  return *TR * *TC * vpr <= (uint64_t)kLdsTile && A % *TR == 0 && B % *TC == 0;
+}
+
 template <typename Vec>
 hipError_t launch_vec(const void* in, void* out, uint64_t A, uint64_t B, uint64_t run_bytes,
                       hipStream_t stream) {
   const uint64_t vpr = run_bytes / sizeof(Vec);
+  uint64_t TR = 0, TC = 0;
+  if (sizeof(Vec) == 16 && lds_tile(A, B, vpr, &TR, &TC)) {
+    const uint32_t tiles = (uint32_t)((A / TR) * (B / TC));
+    hipLaunchKernelGGL(transpose_runs_lds, dim3(tiles), dim3(kThreads), 0, stream,
+                       static_cast<const u32x4*>(in), static_cast<u32x4*>(out), (uint32_t)A,
+                       (uint32_t)B, (uint32_t)vpr, (uint32_t)TR, (uint32_t)TC,
+                       make_fastdiv((uint32_t)(B / TC)), make_fastdiv((uint32_t)(TC * vpr)),
+                       make_fastdiv((uint32_t)(TR * vpr)));
+    return hipGetLastError();
+  }
   const uint64_t total = A * B * vpr;
   if (total == 0) return hipSuccess;
   if (total < (1ull << 32) - (uint64_t)kThreads * kUnroll) {
