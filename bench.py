@@ -80,6 +80,10 @@ def parse_args():
                     help="normal: the seeded N(0,1) tensors (the workload); constant: the "
                          "same work on constant tensors, a diagnostic of how much the GPU "
                          "clock depends on the data the matrix cores see (not a result)")
+    ap.add_argument("--layout-sweep", action="store_true",
+                    help="only time the fused Q/K/V pack and the O unpack from HBM over shard "
+                         "sizes of the 32K share's head layout (s from 8192 to 262144) and fit "
+                         "time = fixed + bytes / bandwidth; prints one JSON line and exits")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain device-to-device copy of known size (for scaling "
                          "rocprofv3 FETCH_SIZE/WRITE_SIZE to bytes) and exit")
@@ -100,6 +104,45 @@ def copy_calibration():
         dst.copy_(src)
     torch.cuda.synchronize()
     print(json.dumps({"copy_calibration_bytes_per_dispatch": n}), flush=True)
+
+
+def layout_sweep(args):
+    """The layout kernels' time against their size: the fused Q/K/V pack and
+    the O unpack of the 32K share's head layout (h = 16, P = 8, d = 128, bf16)
+    at s = 8192 .. 262144, each streaming from HBM (rotating buffer sets of at
+    least 2 GiB), and a least-squares fit time = fixed + bytes / bandwidth.
+    A fixed cost that is large against the 32K share's time shows that kernel
+    is bound by its launch and drain rather than by HBM bandwidth."""
+    import numpy as np
+    import torch
+
+    from ulysses_head_sharded_amd import binding
+    from ulysses_head_sharded_amd.workloads import Workload
+
+    binding.load()
+    dev = torch.device("cuda:0")
+    st = torch.cuda.current_stream()
+    sh = st.cuda_stream
+    rows = []
+    for s in (8192, 16384, 32768, 65536, 131072, 262144):
+        w = Workload("sweep", 2, 8, s, 1, 16, 16, 128, "bf16", True, "")
+        args.layout_calls = 64
+        r = bench_layout_hbm(args, w, binding, torch, torch.bfloat16, binding.ULYS_BF16, st)
+        pack_b = 2 * w.shard_bytes() + 2 * (w.shard_bytes(kv=True) + w.kv_blocks_bytes())
+        rows.append({"s": s, "pack_qkv_bytes": pack_b, "pack_qkv_us": r["pack_qkv_us"],
+                     "pack_gbps": r["pack_gbps"], "unpack_o_bytes": 2 * w.shard_bytes(),
+                     "unpack_o_us": r["unpack_o_us"], "unpack_gbps": r["unpack_gbps"]})
+        torch.cuda.empty_cache()
+    fit = {}
+    for kind in ("pack_qkv", "unpack_o"):
+        x = np.array([r[f"{kind}_bytes"] for r in rows], dtype=np.float64)
+        y = np.array([r[f"{kind}_us"] for r in rows], dtype=np.float64)
+        slope, fixed = np.polyfit(x, y, 1)
+        fit[kind] = {"fixed_us": round(float(fixed), 2),
+                     "steady_gbps": round(float(1e-3 / slope), 1),
+                     "steady_frac_hbm_peak": round(float(1e-3 / slope) / PEAK_HBM_GBPS, 4)}
+    print(json.dumps({"layout_sweep": rows, "fit": fit,
+                      "shape": "h=16, P=8, d_h=128, b=1, bf16 (the 32K share's layout)"}), flush=True)
 
 
 def source_digest(path: str) -> str:
@@ -674,6 +717,9 @@ def main():
     args = parse_args()
     if args.copy_calibration:
         copy_calibration()
+        return
+    if args.layout_sweep:
+        layout_sweep(args)
         return
     if args.gpus != 1:
         print(f"bench.py measures one rank's share on ONE GPU; --gpus {args.gpus} is not "
