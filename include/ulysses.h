@@ -209,9 +209,10 @@ int ulys_attn_fwd_ws(const void* q, const void* k, const void* v, void* o, float
  * harnesses that forbid hipMalloc): the same kernels and results, bit for
  * bit, as ulys_attn_fwd_ws with a workspace of
  * ulys_attn_fwd_workspace_size() bytes, the workspace being a fixed array of
- * ULYS_NOALLOC_SCRATCH_BYTES (96 MiB) in the library's device memory.  Each
- * GPU the call runs on holds its own array from the first call on it until
- * the process ends; the call allocates nothing.
+ * ULYS_NOALLOC_SCRATCH_BYTES (96 MiB) in the library's device memory.  The
+ * array is part of the library's device code, so every GPU on which any of
+ * the library's kernels has run holds its own copy until the process ends;
+ * the call allocates nothing.
  *   Arguments, layouts and errors as ulys_attn_fwd, plus ULYS_ERR_DIM when the
  *   workspace the call would use exceeds the array (a causal share with too
  *   few blocks to fill the GPU twice, whose split partial states need more
