@@ -146,6 +146,20 @@ def test_workspace_size_rejects(lib, args, expect):
     assert B.ulys_attn_fwd_workspace_size(*args) == expect
 
 
+def test_bf16_offset_bound(lib):
+    """The bf16 kernels form 32-bit byte offsets up to one 256-row block past a
+    tensor's end: s = 1048312 with 8 local heads of 128 is the largest share of
+    that head layout the ABI admits, and the next multiple of P is refused
+    (fp32 inputs, which the kernels address with 64-bit offsets, are not)."""
+    ok = (1048312, 1, 64, 64, 128, 8, 1, B.ULYS_BF16)
+    assert B.ulys_attn_fwd_workspace_size(*ok) >= 0
+    assert B.ulys_attn_bwd_workspace_size(*ok) > 0
+    over = (1048320, 1, 64, 64, 128, 8, 1, B.ULYS_BF16)
+    assert B.ulys_attn_fwd_workspace_size(*over) == B.ULYS_ERR_DIM
+    assert B.ulys_attn_bwd_workspace_size(*over) == B.ULYS_ERR_DIM
+    assert B.ulys_attn_fwd_workspace_size(1048320, 1, 64, 64, 128, 8, 1, B.ULYS_F32) == 0
+
+
 def test_workspace_size_fp32_is_zero(lib):
     assert B.ulys_attn_fwd_workspace_size(16, 1, 8, 8, 64, 4, 0, B.ULYS_F32) == 0
 

@@ -17,6 +17,11 @@ the HIP path and the CPU oracle receive the identical host arrays it makes.
 
 Seeds per workload c (1-based): Q = 100c+1, K = 100c+2, V = 100c+3, random
 bit patterns for layout tests 100c+9, row samples 100c+7.
+
+For tensors of gigabytes, which the host draws too slowly for a test,
+``device_normal_bf16`` and ``device_bits`` draw on the GPU with torch's
+seeded counter-based (Philox) generator; the oracle then receives the very
+same values copied back to the host.
 """
 from __future__ import annotations
 
@@ -150,3 +155,29 @@ def row_sample(seed: int, s: int, b: int, hp: int, n_random: int = 1024,
             blk[:, 2] = t_arr
             rows.append(blk)
     return np.concatenate(rows, axis=0)
+
+
+def device_normal_bf16(seed: int, shape, device="cuda", chunk: int = 1 << 26):
+    """N(0,1) tensor of ``shape`` drawn on the device (torch's Philox generator
+    seeded with ``seed``, float32 samples rounded to bf16, nearest-even), in
+    chunks of ``chunk`` elements so no float32 copy of the whole tensor exists."""
+    import torch
+
+    n = int(np.prod(shape))
+    out = torch.empty(n, dtype=torch.bfloat16, device=device)
+    g = torch.Generator(device=device)
+    g.manual_seed(seed)
+    for c0 in range(0, n, chunk):
+        c1 = min(n, c0 + chunk)
+        out[c0:c1] = torch.randn(c1 - c0, generator=g, dtype=torch.float32, device=device)
+    return out.view(*shape)
+
+
+def device_bits(seed: int, shape, device="cuda"):
+    """int16 tensor of ``shape`` with uniformly drawn bit patterns, on the device."""
+    import torch
+
+    g = torch.Generator(device=device)
+    g.manual_seed(seed)
+    return torch.randint(-32768, 32768, tuple(shape), generator=g, dtype=torch.int16,
+                         device=device)
