@@ -160,7 +160,8 @@ int ulys_unpack_head2seq(const void* y, void* x, int64_t s, int64_t b, int64_t h
  *         or NULL to skip it.
  * O is accumulated in fp32 and rounded once (nearest-even) to the dtype.
  * Supported: ULYS_BF16 with d_h in {64, 128} (MFMA kernel); ULYS_F32 with
- * d_h in {64, 128} (fp32 kernel).  s may be any positive multiple of P.
+ * d_h in {64, 128} (fp32 kernel, b * h/P at most 65535).  s may be any
+ * positive multiple of P.
  * Errors: as above, plus h_kv !| h, neither of P and h_kv dividing the other,
  * unsupported d_h/dtype, and o or lse overlapping q, k, v or each other.
  */
@@ -256,11 +257,12 @@ int64_t ulys_attn_fwd_workspace_size(int64_t s, int64_t b, int64_t h, int64_t h_
  *   dq         : [s, b, hp, d_h]   dk, dv : [s, b, hkvp, d_h]   (dtype of q)
  *   workspace  : device, 16-byte aligned, at least
  *                ulys_attn_bwd_workspace_size() bytes (per-row statistics;
- *                partial sums when a causal share is split; on shares of
- *                four or more rounds of dQ work, a counter from which the dQ
- *                workgroups take their blocks); contents ignored on entry,
- *                undefined on return.
- * Gradients are accumulated in fp32 and rounded once (nearest-even).  No
+ *                for bf16 also partial sums when a causal share is split and,
+ *                on shares of four or more rounds of dQ work, a counter from
+ *                which the dQ workgroups take their blocks); contents ignored
+ *                on entry, undefined on return.
+ * Gradients are accumulated in fp32 and rounded once (nearest-even) to the
+ * dtype.  No
  * gradient is accumulated with atomics: every output element is summed by
  * one workgroup in a fixed order (split halves are added by a merge kernel in
  * a fixed order), so the result does not depend on scheduling.  The only
@@ -268,7 +270,9 @@ int64_t ulys_attn_fwd_workspace_size(int64_t s, int64_t b, int64_t h, int64_t h_
  * the index of the next query block from it, and that block is then computed
  * by the same code whichever workgroup runs it, so the values are the same
  * bit for bit as with the static block order.
- * Supported: ULYS_BF16 with d_h in {64, 128}.
+ * Supported: ULYS_BF16 with d_h in {64, 128} (MFMA kernels); ULYS_F32 with
+ * d_h in {64, 128} (fp32 kernels: one group of d_h/32 lanes per query row for
+ * dq and per key row for dk and dv, b * h/P at most 65535).
  * Errors: as ulys_attn_fwd, plus ULYS_ERR_NULL for any missing pointer
  * (lse and workspace included), ULYS_ERR_UNSUPPORTED for another dtype or
  * head size, ULYS_ERR_DIM for a workspace smaller than required, and
@@ -368,6 +372,7 @@ int ulys_attn_fwd_push(const void* q, const void* k, const void* v, void* const*
  *             j's shards [s/P, b, h, d_h] (dQ) and [s/P, b, h_kv, d_h] (dK,
  *             dV); only this rank's head columns are written
  *   rank    : this rank, 0 <= rank < P <= ULYS_MAX_RANKS
+ *   dtype   : ULYS_BF16 only (ULYS_ERR_UNSUPPORTED otherwise)
  * Same values, bit for bit, as the separate calls.  Errors: as
  * ulys_attn_bwd and ulys_head2seq_push; ULYS_ERR_UNSUPPORTED when the KV
  * heads would be replicated (h_kv < P: the copies' gradients have to be
@@ -412,7 +417,7 @@ const char* ulys_status_string(int status);
 /* ABI version of this header: (major << 16) | minor. */
 int ulys_abi_version(void);
 
-#define ULYS_ABI_VERSION ((1 << 16) | 11)
+#define ULYS_ABI_VERSION ((1 << 16) | 12)
 
 #ifdef __cplusplus
 }

@@ -36,7 +36,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_version(lib):
-    assert B.ulys_abi_version() == (1 << 16) | 11
+    assert B.ulys_abi_version() == (1 << 16) | 12
 
 
 def test_status_strings(lib):
@@ -187,7 +187,9 @@ def bwd_args(**kw):
     (dict(h=12, h_kv=6), B.ULYS_ERR_DIVISIBILITY),
     (dict(h_kv=3), B.ULYS_ERR_DIVISIBILITY),
     (dict(d=96), B.ULYS_ERR_UNSUPPORTED),
-    (dict(dtype=B.ULYS_F32), B.ULYS_ERR_UNSUPPORTED),
+    (dict(dtype=9), B.ULYS_ERR_UNSUPPORTED),
+    (dict(dtype=B.ULYS_F32, b=16384, h=32, h_kv=32), B.ULYS_ERR_DIM),  # b*h/P past the grid
+    (dict(dtype=B.ULYS_F32, nbytes=256), B.ULYS_ERR_DIM),  # fp32 needs b*hp*s floats
     (dict(nbytes=16), B.ULYS_ERR_DIM),
     (dict(dk=DK + 4), B.ULYS_ERR_ALIGNMENT),
     (dict(dq=Q + 256), B.ULYS_ERR_ALIAS),
@@ -205,7 +207,10 @@ def test_attn_bwd_workspace_size(lib):
     assert B.ulys_attn_bwd_workspace_size(66, 1, 8, 8, 128, 2, 1, B.ULYS_BF16) == 2 * 4 * 68 * 4
     assert B.ulys_attn_bwd_workspace_size(64, 1, 8, 8, 64, 4, 1, B.ULYS_BF16) == 2 * 2 * 64 * 4
     assert B.ulys_attn_bwd_workspace_size(64, 1, 8, 8, 96, 4, 1, B.ULYS_BF16) == B.ULYS_ERR_UNSUPPORTED
-    assert B.ulys_attn_bwd_workspace_size(64, 1, 8, 8, 128, 4, 1, B.ULYS_F32) == B.ULYS_ERR_UNSUPPORTED
+    # fp32: D = rowsum(dout * o) per query row, rounded up to 256 bytes
+    assert B.ulys_attn_bwd_workspace_size(64, 1, 8, 8, 128, 4, 1, B.ULYS_F32) == 512
+    assert B.ulys_attn_bwd_workspace_size(100, 1, 8, 8, 64, 4, 0, B.ULYS_F32) == 1024
+    assert B.ulys_attn_bwd_workspace_size(64, 1, 8, 8, 128, 4, 1, 9) == B.ULYS_ERR_UNSUPPORTED
     assert B.ulys_attn_bwd_workspace_size(0, 1, 8, 8, 128, 4, 1, B.ULYS_BF16) == B.ULYS_ERR_DIM
 
 

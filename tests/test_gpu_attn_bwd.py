@@ -26,9 +26,9 @@ pytestmark = pytest.mark.gpu
 REL = 2e-2
 
 
-def check(name, got, ref):
+def check(name, got, ref, rel=REL):
     err = np.max(np.abs(as_f64(got) - ref)) if ref.size else 0.0
-    bound = REL * max(1.0, float(np.max(np.abs(ref))) if ref.size else 1.0)
+    bound = rel * max(1.0, float(np.max(np.abs(ref))) if ref.size else 1.0)
     print(f"  {name}: max err {err:.3e} (bound {bound:.3e})", flush=True)
     assert err <= bound, (name, err, bound)
 
@@ -40,22 +40,24 @@ def oracle_fwd_inputs(q, k, v, s, b, h, h_kv, d, P, causal):
 
 
 def gpu_bwd(q, k, v, o, lse, dout, s, b, h, h_kv, d, P, causal):
-    """ulys_attn_bwd with guarded outputs and workspace; host arrays in and out."""
+    """ulys_attn_bwd with guarded outputs and workspace; host arrays in and out
+    (bf16 bit patterns or float32, which selects the kernels)."""
     dev()
     hp, hkvp = h // P, h_kv // P
+    f32 = q.dtype == np.float32
+    tdt, code = (torch.float32, binding.ULYS_F32) if f32 else (torch.bfloat16, binding.ULYS_BF16)
     qd, kd, vd, od, gd = to_dev(q), to_dev(k), to_dev(v), to_dev(o), to_dev(dout)
     ld = to_dev(np.ascontiguousarray(lse, dtype=np.float32))
-    dq = Guarded((s, b, hp, d), torch.bfloat16)
-    dk = Guarded((s, b, hkvp, d), torch.bfloat16)
-    dv = Guarded((s, b, hkvp, d), torch.bfloat16)
-    nbytes = binding.ulys_attn_bwd_workspace_size(s, b, h, h_kv, d, P, int(causal),
-                                                  binding.ULYS_BF16)
+    dq = Guarded((s, b, hp, d), tdt)
+    dk = Guarded((s, b, hkvp, d), tdt)
+    dv = Guarded((s, b, hkvp, d), tdt)
+    nbytes = binding.ulys_attn_bwd_workspace_size(s, b, h, h_kv, d, P, int(causal), code)
     assert nbytes > 0, binding.ulys_status_string(int(nbytes))
     ws = Guarded((nbytes,), torch.uint8)
     rc = binding.ulys_attn_bwd(qd.data_ptr(), kd.data_ptr(), vd.data_ptr(), od.data_ptr(),
                                gd.data_ptr(), ld.data_ptr(), dq.tensor.data_ptr(),
                                dk.tensor.data_ptr(), dv.tensor.data_ptr(), s, b, h, h_kv, d, P,
-                               int(causal), binding.ULYS_BF16, ws.tensor.data_ptr(), nbytes,
+                               int(causal), code, ws.tensor.data_ptr(), nbytes,
                                torch.cuda.current_stream().cuda_stream)
     assert rc == 0, binding.ulys_status_string(rc)
     torch.cuda.synchronize()
@@ -98,6 +100,44 @@ def test_bwd_small_parity(s, b, h, h_kv, d, P, causal):
     check("dq", dq, rq)
     check("dk", dk, rk)
     check("dv", dv, rv)
+
+
+# The fp32 kernels on the same shapes up to s = 321.  The oracle's forward o
+# and lse enter as float32; everything on the GPU is fp32, so the bound is the
+# fp32 forward's 1e-4 (of each gradient's scale past 1).
+REL_F32 = 1e-4
+SMALL_F32 = [c for c in SMALL if c[0] <= 321]
+
+
+@pytest.mark.parametrize("s,b,h,h_kv,d,P,causal", SMALL_F32)
+def test_bwd_small_parity_f32(s, b, h, h_kv, d, P, causal):
+    print(f"case bwd f32 s={s} b={b} h={h} h_kv={h_kv} d={d} P={P} causal={causal}", flush=True)
+    q, k, v = share_inputs(7, s, b, h // P, h_kv // P, d, "f32")
+    dout = synth.tensor(704, (s, b, h // P, d), "f32")
+    o, lse = oracle.attn(q, k, v, s, b, h, h_kv, d, P, causal)
+    dq, dk, dv = gpu_bwd(q, k, v, o.astype(np.float32), lse.astype(np.float32), dout, s, b, h,
+                         h_kv, d, P, causal)
+    rq, rk, rv = oracle.attn_bwd(q, k, v, dout, s, b, h, h_kv, d, P, causal)
+    check("dq", dq, rq, REL_F32)
+    check("dk", dk, rk, REL_F32)
+    check("dv", dv, rv, REL_F32)
+
+
+@pytest.mark.parametrize("s,b,h,h_kv,d,P,causal", [
+    (300, 2, 8, 2, 128, 2, True), (257, 1, 4, 4, 64, 1, False), (16, 1, 8, 8, 64, 4, False)])
+def test_bwd_chain_after_gpu_forward_f32(s, b, h, h_kv, d, P, causal):
+    """The fp32 backward fed by the fp32 GPU forward's o and lse (the last
+    case is the tiny workload's share)."""
+    print(f"case chain f32 s={s} b={b} h={h} h_kv={h_kv} d={d} P={P} causal={causal}",
+          flush=True)
+    q, k, v = share_inputs(8, s, b, h // P, h_kv // P, d, "f32")
+    dout = synth.tensor(804, (s, b, h // P, d), "f32")
+    o, lse = gpu_fwd(q, k, v, s, b, h, h_kv, d, P, causal)
+    dq, dk, dv = gpu_bwd(q, k, v, o, lse, dout, s, b, h, h_kv, d, P, causal)
+    rq, rk, rv = oracle.attn_bwd(q, k, v, dout, s, b, h, h_kv, d, P, causal)
+    check("dq", dq, rq, REL_F32)
+    check("dk", dk, rk, REL_F32)
+    check("dv", dv, rv, REL_F32)
 
 
 @pytest.mark.parametrize("s,b,h,h_kv,d,P,causal", [

@@ -18,7 +18,7 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD_DIR = os.path.join(ROOT, "_build")
 LIB_PATH = os.path.join(PKG, "libulysses.so")
 SOURCES = ["abi.cpp", "layout.hip", "attn_bf16.hip", "attn_bwd_bf16.hip", "attn_f32.hip",
-           "merge.hip", "noalloc.hip"]
+           "attn_bwd_f32.hip", "merge.hip", "noalloc.hip"]
 ARCH = "gfx950"
 
 

@@ -112,6 +112,8 @@ int check_attn_shape(int64_t s, int64_t b, int64_t h, int64_t h_kv, int64_t d_h,
   // the kernels index tokens and work items with 32-bit integers
   if (s > 0x7FFFFFFF || b * hp > 0x7FFFFFFF || b * hp * s > (int64_t(1) << 40))
     return ULYS_ERR_DIM;
+  // the fp32 kernels put (batch, head) on the grid's second dimension
+  if (dtype == ULYS_F32 && b * hp > 65535) return ULYS_ERR_DIM;
   // the bf16 kernels address each tensor with 32-bit byte offsets, up to one
   // 256-row workgroup block past the end (read as zero, stores dropped)
   if (dtype == ULYS_BF16 && (*nq + 256 * b * hp * d_h * 2 >= (int64_t(1) << 31) ||
@@ -201,7 +203,6 @@ int64_t ulys_attn_bwd_workspace_size(int64_t s, int64_t b, int64_t h, int64_t h_
   int64_t nq = 0, nkv = 0, nl = 0;
   const int rc = check_attn_shape(s, b, h, h_kv, d_h, P, dtype, &nq, &nkv, &nl);
   if (rc != ULYS_OK) return rc;
-  if (dtype != ULYS_BF16) return ULYS_ERR_UNSUPPORTED;
   ulys::AttnBwdArgs a;
   a.s = s;
   a.b = b;
@@ -209,6 +210,7 @@ int64_t ulys_attn_bwd_workspace_size(int64_t s, int64_t b, int64_t h, int64_t h_
   a.hkvp = kv_per_rank(h_kv, P);
   a.d = d_h;
   a.causal = causal != 0;
+  if (dtype == ULYS_F32) return ulys::attn_bwd_f32_workspace_size(a);
   const int64_t need = ulys::attn_bwd_bf16_workspace_size(a);
   // the kernels address the per-row statistics with 32-bit byte offsets
   if (need >= (int64_t(1) << 31)) return ULYS_ERR_DIM;
@@ -259,7 +261,8 @@ int ulys_attn_bwd(const void* q, const void* k, const void* v, const void* o, co
   a.causal = causal != 0;
   a.workspace = workspace;
   a.workspace_bytes = workspace_bytes;
-  const hipError_t e = ulys::launch_attn_bwd_bf16(a, (hipStream_t)stream);
+  const hipError_t e = (dtype == ULYS_BF16) ? ulys::launch_attn_bwd_bf16(a, (hipStream_t)stream)
+                                            : ulys::launch_attn_bwd_f32(a, (hipStream_t)stream);
   return e == hipSuccess ? ULYS_OK : ULYS_ERR_HIP;
 }
 
@@ -273,6 +276,8 @@ int ulys_attn_bwd_push(const void* q, const void* k, const void* v, const void* 
     return ULYS_ERR_NULL;
   const int64_t need = ulys_attn_bwd_workspace_size(s, b, h, h_kv, d_h, P, causal, dtype);
   if (need < 0) return (int)need;
+  // the pushing epilogues exist in the bf16 kernels only
+  if (dtype != ULYS_BF16) return ULYS_ERR_UNSUPPORTED;
   if (workspace_bytes < need) return ULYS_ERR_DIM;
   int64_t nq = 0, nkv = 0, nl = 0;
   const int rc = check_attn_shape(s, b, h, h_kv, d_h, P, dtype, &nq, &nkv, &nl);

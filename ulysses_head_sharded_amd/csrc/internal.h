@@ -117,5 +117,8 @@ struct AttnBwdArgs {
 
 hipError_t launch_attn_bwd_bf16(const AttnBwdArgs& a, hipStream_t stream);
 int64_t attn_bwd_bf16_workspace_size(const AttnBwdArgs& a);
+// fp32 inputs (no pushing epilogue): the workspace holds D = rowsum(dout * o)
+hipError_t launch_attn_bwd_f32(const AttnBwdArgs& a, hipStream_t stream);
+int64_t attn_bwd_f32_workspace_size(const AttnBwdArgs& a);
 
 }  // namespace ulys
