@@ -26,17 +26,20 @@
 //    fragments in registers, dS^T = P^T (dP^T - D), dq^T += K^T dS^T with
 //    K^T read transposed from LDS;
 //  * dkv: a workgroup of 8 waves owns 256 keys of one KV head (32 per wave,
-//    K^T fragments in registers, V rows in LDS for the whole loop), streaming
+//    K^T and V^T fragments in registers for the whole loop), streaming
 //    64-query tiles of Q, dout and their statistics through LDS for every
 //    query head of the group: S = Q K^T, dP = dout V^T, then dv^T += dout^T P
-//    and dk^T += Q^T dS with dout^T and Q^T read transposed;
+//    and dk^T += Q^T dS with dout^T and Q^T read transposed.  S comes first,
+//    so that its exponentials run beside the dP products, and dV, which needs
+//    only P, beside dS;
 //  * merge (dq, dkv): when a causal share has too few work items to fill the
 //    GPU twice, every item is run as two halves (keys for dq, queries for
 //    dkv) that leave fp32 partial sums in the workspace, and a merge adds the
 //    two halves in a fixed order, scales and rounds.
-// S and dP are computed by both kernels.  Each kernel has a branch-free fast
-// path for tiles with no masked entry and a masked path for diagonal and
-// tail tiles.
+// S and dP are computed by both kernels.  The dq kernel has a branch-free
+// fast path for tiles with no masked entry and a masked path for diagonal and
+// tail tiles; the dkv kernel masks by starting the masked entries' S and dP
+// accumulators at -inf and 0, so every tile then runs the same code.
 //
 // Every tile read both row-wise (16-byte MFMA operand reads of 16
 // consecutive rows) and transposed (ds_read_b64_tr_b16 over 4 consecutive
@@ -73,11 +76,9 @@ struct Geo {
   static constexpr int kDqPart = kWaves * 64 * (D / 2);           // floats of one split unit
   // dkv
   static constexpr int kQTile = kQT * ROW;                        // one Q or dout tile
-  static constexpr int kVBlock = kKB * ROW;                       // the workgroup's V rows
   static constexpr int kKLoads = kQT * CHUNKS / (64 * kWaves);    // loads per lane per tensor
-  static constexpr int kVLoads = kVBlock / (1024 * kWaves);       // loads per lane, V block
   static constexpr int kDkvPart = kWaves * 64 * D;                // floats of one split unit
-  static constexpr int kDkvLds = kVBlock + 4 * kQTile + 2 * kStatBuf;
+  static constexpr int kDkvLds = 4 * kQTile + 2 * kStatBuf;
 };
 
 // Chunk swizzle g(r) of row r (the tile layout above).
@@ -562,17 +563,16 @@ __device__ __forceinline__ KItem decode_k_item(const BwdParams& p, int rank) {
 template <int D, bool CAUSAL, bool PUSH>
 __global__ __launch_bounds__(kThreads, 1) void bwd_dkv_kernel(BwdParams p) {
   constexpr int ROW = Geo<D>::ROW, CHUNKS = Geo<D>::CHUNKS, RPL = Geo<D>::RPL;
-  constexpr int kQTile = Geo<D>::kQTile, kVBlock = Geo<D>::kVBlock;
-  constexpr int kKLoads = Geo<D>::kKLoads, kVLoads = Geo<D>::kVLoads;
+  constexpr int kQTile = Geo<D>::kQTile;
+  constexpr int kKLoads = Geo<D>::kKLoads;
   constexpr int kDkvPart = Geo<D>::kDkvPart;
-  // LDS: Q0 Q1 | dout0 dout1 | V block | stats0 stats1.  The tiles first:
+  // LDS: Q0 Q1 | dout0 dout1 | stats0 stats1.  The tiles first:
   // with the buffer and half indices compile-time constants, every tile read
   // is one lane register plus an offset that fits the instruction's 16 bits.
   __shared__ __attribute__((aligned(16))) uint8_t lds[Geo<D>::kDkvLds];
   uint8_t* qt = lds;
   uint8_t* gt = qt + 2 * kQTile;
-  uint8_t* vblk = gt + 2 * kQTile;
-  uint8_t* stt = vblk + kVBlock;
+  uint8_t* stt = gt + 2 * kQTile;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
   const int l32 = lane & 31, hh = lane >> 5;
@@ -595,24 +595,19 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkv_kernel(BwdParams p) {
   const __amdgpu_buffer_rsrc_t rde = rsrc(p.ndelta, p.stat_bytes);
   const int kv_head_off = (it.be * p.hkvp + it.kvg) * ROW;
 
-  // K^T fragments (B operand of S = Q K^T): key my_key, features 16 dk + 8 hh .. +7
-  bf16x8 kf[D / 16];
+  // K^T and V^T fragments (B operands of S = Q K^T and dP = dout V^T): key
+  // my_key, features 16 dk + 8 hh .. +7
+  bf16x8 kf[D / 16], vf[D / 16];
   {
     const int off = my_key * p.kv_tok_bytes + kv_head_off + hh * 16;
 #pragma unroll
-    for (int dk = 0; dk < D / 16; ++dk)
+    for (int dk = 0; dk < D / 16; ++dk) {
       kf[dk] = as_bf16x8(__builtin_amdgcn_raw_buffer_load_b128(rk, off + dk * 32, 0, 0));
-  }
-  // the workgroup's V rows into LDS (swizzled like the tiles)
-#pragma unroll
-  for (int i = 0; i < kVLoads; ++i) {
-    const int row = (wave * kVLoads + i) * RPL + lane / CHUNKS;
-    load_lds16(rv, vblk + (wave * kVLoads + i) * 1024,
-               (it.kblk * kKB + row) * p.kv_tok_bytes + kv_head_off +
-                   (((lane % CHUNKS) ^ dswz<D>(row)) << 4));
+      vf[dk] = as_bf16x8(__builtin_amdgcn_raw_buffer_load_b128(rv, off + dk * 32, 0, 0));
+    }
   }
 #pragma unroll
-  for (int dk = 0; dk < D / 16; ++dk) asm volatile("" ::"v"(kf[dk]));
+  for (int dk = 0; dk < D / 16; ++dk) asm volatile("" ::"v"(kf[dk]), "v"(vf[dk]));
 
   // steps: (query head of the group, 64-query tile); causal tiles start at
   // the workgroup's first key
@@ -663,7 +658,6 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkv_kernel(BwdParams p) {
   if (st_lo < st_hi) load_step(st_lo, 0);
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
-  const uint8_t* vrow = vblk + wave * 32 * ROW;  // this wave's V rows
   // one step: query tile st in buffer CUR, its two 32-query halves
   auto dkv_step = [&](int st, auto cur_tag) __attribute__((always_inline)) {
     constexpr int cur = decltype(cur_tag)::value;
@@ -680,7 +674,12 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkv_kernel(BwdParams p) {
       const float* sl = reinterpret_cast<const float*>(stt + cur * kStatBuf) + 32 * hq + 4 * hh;
       // S (queries x keys) and dP: rows qr + 8 (r/4) + 4 hh + r%4, column
       // my_key.  The accumulators start from the rows' statistics (broadcast
-      // reads), so they end as q.k - lse sqrt(d_h) and dP - D.
+      // reads), so they end as q.k - lse sqrt(d_h) and dP - D.  Entries
+      // above the diagonal or past the sequence start from -inf and 0
+      // instead, so that P and dS come out as 0 from the same code as every
+      // other entry (statistics of rows past the sequence are not defined,
+      // and the Q, dout and K rows past it read as zero).
+      const bool need_mask = (CAUSAL && qr < kw0 + 31) || (qr + 32 > p.s) || (kw0 + 32 > p.s);
       f32x16 sc, dp;
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
@@ -692,53 +691,54 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkv_kernel(BwdParams p) {
           dp[4 * j + i] = d4[i];
         }
       }
+      if (need_mask) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int qq = qr + 8 * (r >> 2) + 4 * hh + (r & 3);
+          const bool off = qq >= p.s || my_key >= p.s || (CAUSAL && my_key > qq);
+          sc[r] = off ? -INFINITY : sc[r];
+          dp[r] = off ? 0.f : dp[r];
+        }
+      }
+      // S first, so that its exponentials run beside the dP products; then
+      // dV, which needs only P, beside dS = P (dP - D); then dK
 #pragma unroll
       for (int dk = 0; dk < D / 16; ++dk) {
         const bf16x8 qa = *(const bf16x8*)(ql + ta.row_rd(dk));
-        const bf16x8 ga = *(const bf16x8*)(gl + ta.row_rd(dk));
-        const bf16x8 vb = *(const bf16x8*)(vrow + ta.row_rd(dk));
         sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa, kf[dk], sc, 0, 0, 0);
-        dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ga, vb, dp, 0, 0, 0);
       }
-      const bool need_mask = (CAUSAL && qr < kw0 + 31) || (qr + 32 > p.s) || (kw0 + 32 > p.s);
-      if (!need_mask) {
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const float pr = __builtin_amdgcn_exp2f(sc[r] * p.c);
-          sc[r] = pr;
-          dp[r] = pr * dp[r];
-        }
-      } else {
-        // masked entries are set to zero, not multiplied by it: statistics
-        // of query rows past the sequence are not defined
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const float pr = __builtin_amdgcn_exp2f(sc[r] * p.c);
-          const float ds = pr * dp[r];
-          const int qq = qr + 8 * (r >> 2) + 4 * hh + (r & 3);
-          const bool off = qq >= p.s || my_key >= p.s || (CAUSAL && my_key > qq);
-          sc[r] = off ? 0.f : pr;
-          dp[r] = off ? 0.f : ds;
-        }
+      for (int dk = 0; dk < D / 16; ++dk) {
+        const bf16x8 ga = *(const bf16x8*)(gl + ta.row_rd(dk));
+        dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ga, vf[dk], dp, 0, 0, 0);
       }
       bf16x8 pb[2], dsb[2];
 #pragma unroll
-      for (int ks = 0; ks < 2; ++ks)
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          pb[ks][e] = (__bf16)sc[ks * 8 + e];
-          dsb[ks][e] = (__bf16)dp[ks * 8 + e];
-        }
-      // dv^T += dout^T P, dk^T += Q^T dS (tiles read transposed)
+      for (int r = 0; r < 16; ++r) sc[r] = __builtin_amdgcn_exp2f(sc[r] * p.c);
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
-        for (int db = 0; db < D / 32; ++db) {
+        for (int e = 0; e < 8; ++e) pb[ks][e] = (__bf16)sc[ks * 8 + e];
+      // dv^T += dout^T P (dout^T read transposed)
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db)
           dva[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(read_tr<D>(gl, ta, ks, db), pb[ks],
                                                             dva[db], 0, 0, 0);
+#pragma unroll
+      for (int r = 0; r < 16; ++r) dp[r] = sc[r] * dp[r];
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) dsb[ks][e] = (__bf16)dp[ks * 8 + e];
+      // dk^T += Q^T dS (Q^T read transposed)
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db)
           dka[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(read_tr<D>(ql, ta, ks, db), dsb[ks],
                                                             dka[db], 0, 0, 0);
-        }
     }
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
