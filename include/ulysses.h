@@ -20,7 +20,9 @@
  *   - Every tensor pointer is a DEVICE pointer to a contiguous row-major
  *     array (last axis fastest) and must be 16-byte aligned.  The caller owns
  *     every buffer; the library allocates nothing and keeps no state between
- *     calls, so all entry points are thread-safe.
+ *     calls, so the entry points are thread-safe -- except that
+ *     ulys_attn_fwd_noalloc works in one fixed device array per GPU, so its
+ *     calls that overlap in time on one GPU race (see there).
  *   - s, h and h_kv are GLOBAL sizes (whole sequence, all heads); P is the
  *     number of ranks of the sequence-parallel group.  Shapes below use
  *     sl = s/P, hp = h/P, and hkvp = h_kv/P, or hkvp = 1 when h_kv < P and
