@@ -197,12 +197,27 @@ def cpu_baseline(w, q, k, v, budget_s: float):
         t_used += time.perf_counter() - t0
         flops += float(4 * w.d * keys.sum())
         rows_done += t.size
+    # the layout oracle (orc_pack, one thread) on one rank-local shard of the
+    # workload's Q ([s/P, b, h, d]: as many elements as the share; the share's
+    # bits serve as its contents, the pack only moves them)
+    x = np.ascontiguousarray(q).reshape(w.s // w.P, w.b, w.h, w.d)
+    nbytes = x.nbytes
+    reps, t_lay = 0, 0.0
+    while t_lay < min(2.0, budget_s) and reps < 50:
+        t0 = time.perf_counter()
+        oracle.pack(x, w.s, w.b, w.h, w.d, w.P)
+        t_lay += time.perf_counter() - t0
+        reps += 1
     return {
         "value": flops / t_used / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
         "cpu_model": cpu_model(),
         "sample": f"{rows_done} uniformly drawn query rows of the {w.name} share the GPU "
                   f"attends over (fp64 oracle, {t_used:.1f} s wall, algorithmic flops of the "
                   f"sample)",
+        "layout": {"value": 2.0 * nbytes * reps / t_lay / 1e9, "unit": "GB/s", "cores": 1,
+                   "kind": "oracle",
+                   "sample": f"orc_pack of one {nbytes / 2**10:.0f} KiB rank-local Q shard of "
+                             f"{w.name}, {reps} calls in {t_lay:.2f} s (bytes read + written)"},
     }
 
 
