@@ -23,8 +23,9 @@
 //  * dq: a workgroup of 8 waves owns 256 queries (as the forward: up to 8
 //    query heads of one KV group), streaming 64-key K/V tiles through LDS:
 //    S^T = K Q^T and dP^T = V dout^T with the wave's Q^T and dout^T
-//    fragments in registers, dS^T = P^T (dP^T - D), dq^T += K^T dS^T with
-//    K^T read transposed from LDS;
+//    fragments in registers (dP^T accumulated from -D, so it ends as
+//    dP^T - D), dS^T = P^T (dP^T - D), dq^T += K^T dS^T with K^T read
+//    transposed from LDS;
 //  * dkv: a workgroup of 8 waves owns 256 keys of one KV head (32 per wave,
 //    K^T and V^T fragments in registers for the whole loop), streaming
 //    64-query tiles of Q, dout and their statistics through LDS for every
@@ -476,9 +477,13 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dq_kernel(BwdParams p) {
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
         const uint8_t* kh = kl + kb * 32 * ROW;
+        // dP^T starts from -D (this lane's query), so it ends as dP - D
         f32x16 sc, dp;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) sc[r] = dp[r] = 0.f;
+        for (int r = 0; r < 16; ++r) {
+          sc[r] = 0.f;
+          dp[r] = ndlt;
+        }
 #pragma unroll
         for (int dk = 0; dk < D / 16; ++dk) {
           const bf16x8 ka = *(const bf16x8*)(kh + ta.row_rd(dk));
@@ -492,7 +497,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dq_kernel(BwdParams p) {
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
             const float pr = __builtin_amdgcn_exp2f(fmaf(sc[r], p.c, clse));
-            sc[r] = pr * (dp[r] + ndlt);
+            sc[r] = pr * dp[r];
           }
         } else {
           // masked entries are set to zero, not multiplied by it
@@ -500,7 +505,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dq_kernel(BwdParams p) {
           for (int r = 0; r < 16; ++r) {
             const float pr = __builtin_amdgcn_exp2f(fmaf(sc[r], p.c, clse));
             const int key = kh0 + 8 * (r >> 2) + 4 * hh + (r & 3);
-            const float ds = pr * (dp[r] + ndlt);
+            const float ds = pr * dp[r];
             sc[r] = (key >= p.s || (CAUSAL && key > my_q)) ? 0.f : ds;
           }
         }
