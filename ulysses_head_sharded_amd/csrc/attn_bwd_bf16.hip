@@ -18,8 +18,9 @@
 // (each workgroup takes the index of its query block from it; the block is
 // computed by the same code wherever it runs):
 //  * prep: -D and -lse * sqrt(d_h) per query row, into the caller's
-//    workspace (the dkv kernel starts its dP and S accumulators from them,
-//    so that exp2(c S) is P and dP - D comes out of the MFMA);
+//    workspace (both kernels start their dP accumulators from -D, so that
+//    dP - D comes out of the MFMA, and the dkv kernel its S accumulators
+//    from -lse * sqrt(d_h), so that exp2(c S) is P);
 //  * dq: a workgroup of 8 waves owns 256 queries (as the forward: up to 8
 //    query heads of one KV group), streaming 64-key K/V tiles through LDS:
 //    S^T = K Q^T and dP^T = V dout^T with the wave's Q^T and dout^T
