@@ -216,9 +216,14 @@ def cpu_baseline(w, q, k, v, budget_s: float):
                   f"sample)",
         "layout": {"value": 2.0 * nbytes * reps / t_lay / 1e9, "unit": "GB/s", "cores": 1,
                    "kind": "oracle",
-                   "sample": f"orc_pack of one {nbytes / 2**10:.0f} KiB rank-local Q shard of "
+                   "sample": f"orc_pack of one {size_text(nbytes)} rank-local Q shard of "
                              f"{w.name}, {reps} calls in {t_lay:.2f} s (bytes read + written)"},
     }
+
+
+def size_text(nbytes: int) -> str:
+    """A byte count in MiB, or KiB below one MiB."""
+    return f"{nbytes / 2**20:.0f} MiB" if nbytes >= 2**20 else f"{nbytes / 2**10:.0f} KiB"
 
 
 def cpu_model() -> str:
